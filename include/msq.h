@@ -1,0 +1,204 @@
+/*
+ * msq.h -- block-wise mixed-precision weight-only quantized matmul, C ABI.
+ *
+ * What the library computes
+ * -------------------------
+ * A bf16 weight matrix W [N out][K in] is reordered in both directions
+ * (rows by perm_row, columns by perm_col), cut into blocks of 64 rows x 128
+ * columns, and every block is round-to-nearest quantized at its own bitwidth
+ * b in {0,1,2,3,4,8}: asymmetric, one group of 128 along K per row per block,
+ * so each (row, block) has one scale and one integer zero point.  The codes
+ * are packed into one compact buffer, segment by segment in ascending
+ * bitwidth, located through a prefix-summed block-offset table.  Inference
+ * then computes y = x . W^T by dequantizing every block on the fly.
+ *
+ *   - Precision chosen per 64x128 block after reordering rows and columns so
+ *     that sensitive weights cluster into block-aligned regions:
+ *     "ScaleBITS" summary page (atlas.scime.ai), section Approach; the
+ *     abstract on the paper-with-me page calls this hardware-aligned,
+ *     block-wise partitioning.
+ *   - Scalar quantizer is RTN with group size 128: same summary page,
+ *     section Limitations ("RTN-g128" is also the uniform baseline in
+ *     section Key results).  Minimum precision 0 or 1 bit: section
+ *     Surprising findings.
+ *   - Row/column reordering costs a small activation reordering at inference:
+ *     "SFMP" abstract (aiqbench page).  This library gathers x through
+ *     perm_col inside its kernels and scatters y back through perm_row.
+ *   - A precision map guides reconstruction into compact weight buffers that
+ *     the kernel reuses: "TileQuant" abstract (fugumt page).
+ *
+ * Readings where the pages are silent (each is a choice of this library):
+ *   - Block orientation: 64 rows along N (outputs) x 128 columns along K, so a
+ *     block row holds exactly one 128-wide quantization group.
+ *   - Quantizer, all in IEEE fp32 rounded after every operation:
+ *       lo = min(0, min over group of w),  hi = max(0, max over group of w)
+ *       qmax = 2^b - 1,  s = (hi - lo) / qmax
+ *       if s == 0:  z = 0 and every code is 0
+ *       else:       z = clamp(rint(-lo / s), 0, qmax)
+ *                   q = clamp(rint(w / s) + z, 0, qmax)
+ *     rint is round-half-to-even.  The dequantized weight is s * (q - z).
+ *     b == 0 means the block is pruned: no codes, s = 0, z = 0, W-hat = 0.
+ *   - Permutations use the gather convention: reordered row i is original row
+ *     perm_row[i]; reordered column j is original column perm_col[j].
+ *   - y comes back in the ORIGINAL row order, in fp32.
+ *
+ * Packed format, version 1 (MSQ_FORMAT_VERSION)
+ * ---------------------------------------------
+ * Block (r, c) covers reordered rows 64r..64r+63 and reordered columns
+ * 128c..128c+127.  For element (ib, jb) of the block (0 <= ib < 64,
+ * 0 <= jb < 128) define
+ *     rt = ib >> 4,  n = ib & 15,  kt = jb >> 5,  kg = (jb >> 3) & 3,
+ *     e = jb & 7,  lane l = n + 16*kg,  fragment F = 4*rt + kt,
+ *     word d = e >> 1,  half h = e & 1.
+ * For b in {1,2,4,8}: phi = 16 / b fragments share one 1 KiB chunk;
+ * chunk t = F / phi, slot s = F % phi.  The b-bit code sits at bit
+ * 16*h + b*s of the little-endian uint32 at byte 1024*t + 16*l + 4*d of the
+ * block.  A b-bit block therefore occupies 1024*b bytes.
+ * For b == 3 the code q = q_lo + 4*q_hi is split into planes: q_lo (2 bits)
+ * follows the b == 2 rule in chunks 0..1 and q_hi (1 bit) follows the
+ * b == 1 rule in chunk 2; the block occupies 3072 bytes.
+ * Every chunk is one contiguous KiB that a 64-lane wavefront fetches with
+ * one 16-byte load per lane; for each slot, masking the four words of a lane
+ * yields the 8 codes of one 16x32 operand fragment of a gfx950 bf16 matrix
+ * instruction (row 16*rt + n, columns 32*kt + 8*kg .. +7).
+ *
+ * Buffer: block (r, c) starts at byte 1024 * block_offset[r][c] of codes.
+ * Blocks are laid out segment by segment for b = 1, 2, 3, 4, 8; inside a
+ * segment in row-major (r, c) order; block_offset is the exclusive prefix
+ * sum of bits over that order, in KiB.  0-bit blocks own no bytes and have
+ * block_offset == MSQ_NO_BLOCK.  code_bytes = 1024 * sum(bits).
+ * scale is float32 [N/64][K/128][64] and zero is uint8 [N/64][K/128][64],
+ * both indexed by (block row, block column, row inside the block) in
+ * reordered row order.
+ *
+ * Conventions
+ * -----------
+ *   - Pointers are device pointers unless the name ends in _host.
+ *   - The caller allocates and owns every buffer; the library allocates no
+ *     memory, keeps no device state and never synchronizes.  Device calls
+ *     are asynchronous on the given stream.
+ *   - Errors are return codes.  All argument checks run before any launch,
+ *     so outputs are untouched when a call returns an error.  A failed
+ *     launch returns MSQ_ERR_HIP.
+ *   - msq_plan validates bits and permutations on the host; the device
+ *     calls trust a weight descriptor whose bits and permutations passed
+ *     msq_plan.  Non-finite W or |W| >= 2^127 gives unspecified codes.
+ */
+#ifndef MSQ_H_
+#define MSQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSQ_FORMAT_VERSION 1
+#define MSQ_BLOCK_ROWS 64
+#define MSQ_BLOCK_COLS 128
+#define MSQ_NO_BLOCK 0xFFFFFFFFu
+/* Largest M the decode (GEMV) kernel accepts. */
+#define MSQ_GEMV_MAX_M 64
+
+typedef enum {
+  MSQ_OK = 0,
+  MSQ_ERR_INVALID_ARG = 1,      /* null pointer, misaligned pointer, bad enum */
+  MSQ_ERR_SHAPE = 2,            /* N or K not a positive multiple of 64 / 128, M < 0 */
+  MSQ_ERR_BITS = 3,             /* a bits entry outside {0,1,2,3,4,8} */
+  MSQ_ERR_PERM = 4,             /* perm_row or perm_col is not a permutation */
+  MSQ_ERR_BUFFER_TOO_SMALL = 5, /* code_bytes or workspace smaller than needed */
+  MSQ_ERR_HIP = 6,              /* a HIP launch or runtime call failed */
+  MSQ_ERR_UNSUPPORTED = 7       /* e.g. forcing the GEMV kernel with M > 64 */
+} msq_status;
+
+typedef enum {
+  MSQ_KERNEL_AUTO = 0,  /* GEMV for M <= MSQ_GEMV_MAX_M, GEMM otherwise */
+  MSQ_KERNEL_GEMV = 1,  /* decode kernel; M <= MSQ_GEMV_MAX_M */
+  MSQ_KERNEL_GEMM = 2   /* prefill kernel; any M >= 1 */
+} msq_kernel;
+
+/* Buffer sizes for one weight matrix, filled by msq_plan. */
+typedef struct {
+  int64_t code_bytes;          /* 1024 * sum(bits) */
+  int64_t scale_bytes;         /* 4 * N * K / 128 */
+  int64_t zero_bytes;          /* N * K / 128 */
+  int64_t offset_bytes;        /* 4 * (N/64) * (K/128) */
+  int64_t blocks_per_bits[9];  /* histogram of bits; index = bitwidth */
+  double mean_bits;            /* sum(bits) / number of blocks */
+} msq_sizes;
+
+/* Descriptor of one packed weight matrix.  Caller-owned; the library reads
+ * the pointers and never frees them. */
+typedef struct {
+  int64_t N, K;               /* N % 64 == 0, K % 128 == 0, both > 0 */
+  const uint8_t *bits;        /* [N/64][K/128], values in {0,1,2,3,4,8} */
+  const int32_t *perm_row;    /* [N]: reordered row i <- original row perm_row[i] */
+  const int32_t *perm_col;    /* [K]: reordered col j <- original col perm_col[j] */
+  uint32_t *block_offset;     /* [N/64][K/128] in KiB; MSQ_NO_BLOCK for 0-bit */
+  uint8_t *codes;             /* [code_bytes], 256-byte aligned */
+  float *scale;               /* [N/64][K/128][64] */
+  uint8_t *zero;              /* [N/64][K/128][64] */
+  int64_t code_bytes;         /* size of the codes buffer in bytes */
+} msq_weight;
+
+/* Host only; needs no GPU.  Validates N, K, the bit map and both
+ * permutations (host copies) and fills *out with the buffer sizes.
+ * Block-wise precision map and reordering: "ScaleBITS" summary page,
+ * section Approach.  Returns MSQ_ERR_SHAPE, MSQ_ERR_BITS, MSQ_ERR_PERM or
+ * MSQ_ERR_INVALID_ARG (null pointer); *out is untouched on error. */
+msq_status msq_plan(int64_t N, int64_t K, const uint8_t *bits_host,
+                    const int32_t *perm_row_host, const int32_t *perm_col_host,
+                    msq_sizes *out);
+
+/* Quantizes and packs W (bf16 bit patterns, [N][K] row-major, original
+ * order, 16-byte aligned) into w->block_offset, w->codes, w->scale and
+ * w->zero, asynchronously on stream.  RTN-g128 per block at the block's
+ * bitwidth ("ScaleBITS" summary page, sections Approach and Limitations);
+ * compact per-bitwidth buffers ("TileQuant" abstract).  Results are
+ * bit-exact against the quantizer and format stated at the top of this
+ * header.  This offline call is the one exception to "never synchronizes":
+ * before launching it copies bits, perm_row and perm_col back to the host
+ * (ordered on stream, then waited for) and validates them exactly as
+ * msq_plan does, so a bad descriptor is refused instead of read out of
+ * bounds.  Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer),
+ * MSQ_ERR_SHAPE, MSQ_ERR_BITS, MSQ_ERR_PERM, MSQ_ERR_BUFFER_TOO_SMALL
+ * (w->code_bytes below 1024 * sum(bits)), MSQ_ERR_HIP. */
+msq_status msq_quantize_pack(const uint16_t *W_bf16, const msq_weight *w,
+                             hipStream_t stream);
+
+/* Bytes of device workspace msq_gemm / msq_gemm_ex need for this shape
+ * (any kernel choice).  Zero for M == 0. */
+size_t msq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* y = x . W^T with W dequantized block by block from the packed buffers.
+ * x: bf16 bit patterns [M][K] row-major in ORIGINAL column order (16-byte
+ * aligned); y: fp32 [M][N] row-major in ORIGINAL row order, fully
+ * overwritten.  The activation gather through perm_col is the reordering
+ * overhead of the "SFMP" abstract; the row scatter through perm_row restores
+ * the original output order.  M == 0 is a no-op.  workspace must hold
+ * msq_gemm_workspace_bytes(M, N, K) bytes (256-byte aligned); calls that
+ * share a workspace must be ordered on one stream.  Errors:
+ * MSQ_ERR_INVALID_ARG, MSQ_ERR_SHAPE, MSQ_ERR_BUFFER_TOO_SMALL, MSQ_ERR_HIP. */
+msq_status msq_gemm(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
+                    float *y, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/* As msq_gemm, with the kernel chosen by the caller (testing and
+ * benchmarking).  MSQ_ERR_UNSUPPORTED for MSQ_KERNEL_GEMV with M > 64;
+ * MSQ_ERR_INVALID_ARG for an unknown kernel value. */
+msq_status msq_gemm_ex(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
+                       float *y, void *workspace, size_t workspace_bytes,
+                       msq_kernel kernel, hipStream_t stream);
+
+/* Static English text for a status code; never NULL. */
+const char *msq_status_string(msq_status status);
+
+/* MSQ_FORMAT_VERSION of the library that was loaded. */
+int msq_format_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MSQ_H_ */
