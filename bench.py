@@ -1,0 +1,319 @@
+#!/usr/bin/env python
+"""Benchmark of the block-wise mixed-precision quantized matmul on one MI355X.
+
+Workload: the seven linears of a Llama-3-70B-shaped decoder layer
+(q/o 8192x8192, k/v 1024x8192, gate/up 28672x8192, down 8192x28672), random
+N(0, 0.02) bf16 weights with 1% outlier input columns x10, block bitwidths
+drawn i.i.d. from {0:5%, 1:10%, 2:60%, 3:15%, 4:8%, 8:2%} (labelled "about
+2.1 bits"), random row/column permutations, x ~ N(0, 1) bf16.  Seed 0.
+
+A step is one decode pass (M = 1) through all seven packed linears: the
+activation gather, on-the-fly dequantization, matrix-core product and row
+scatter of every linear, captured once per weight copy in a HIP graph and
+replayed.  The packed weights of the layer are cloned R times (R * packed >=
+1 GiB) and the copies are rotated step by step so that the 256 MB Infinity
+Cache cannot serve them.  value = effective weight GB/s = packed weight bytes
+(codes + scales/zero points + bit map/offsets) of the layer / step time.
+
+Also reported, each timed in its own leg of the same run:
+  prefill : M = 2048 through all seven linears, TFLOP/s and fraction of the
+            2.5 PFLOP/s dense bf16 matrix-core peak;
+  pack    : quantize-pack throughput over the seven matrices;
+  roofline: the decode kernel on the largest linear (gate_proj), bytes per
+            launch / average launch time, against 8 TB/s;
+  cpu_baseline: the CPU oracle (numpy) decoding a bounded sample of block
+            rows of every linear, scaled to GB/s.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective weight GB/s & %HBM peak at M=1; TFLOP/s & %MFMA peak at M=2048"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+WORKLOAD = "llama3-70b-layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_m1_traffic.json")
+GEMV_SOURCES = ("block_wise_mixed_amd/csrc/msq_gemv.hip", "block_wise_mixed_amd/csrc/msq_dequant.h")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for p in GEMV_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(expected_sha: str):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3 counter runs,
+    or None when they were taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != expected_sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def decode_bytes(pw, M: int) -> int:
+    """Algorithmic bytes of one decode of one linear: packed weight + x + y."""
+    return pw.packed_bytes + 2 * M * pw.K + 4 * M * pw.N
+
+
+def prefill_flops(pw, M: int) -> int:
+    """2 * M * 64 * 128 per block that is not pruned."""
+    live = int((pw.bits != 0).sum().item())
+    return 2 * M * 64 * 128 * live
+
+
+def cpu_baseline(inputs, target_s: float = 12.0):
+    """The oracle decoding a sample of block rows of every linear (M = 1).
+
+    Per linear: the oracle quantizes and packs the sampled block rows (not
+    timed), then the timed part unpacks their codes, dequantizes in fp64 and
+    multiplies (the oracle's decode).  The sample grows until it takes about
+    target_s seconds in total; the rate is sample packed bytes / time.
+    """
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    def run(rows_per):
+        t_sum = b_sum = 0.0
+        n_rows = 0
+        for mi in inputs:
+            brs = np.arange(min(rows_per, mi.N // 64))
+            q = oracle.quantize(mi.W, mi.bits, mi.perm_row, mi.perm_col, block_rows=brs,
+                                check=False)
+            sub_bits = mi.bits[brs]
+            off, codes = oracle.pack(q["q"], sub_bits)
+            x = mi.x(1)
+            t0 = time.perf_counter()
+            qq = oracle.unpack(codes, sub_bits, off)
+            What = oracle.dequantize(qq, q["s"], q["z"])
+            oracle.matmul(oracle.bf16_to_f32(x), What, mi.perm_col)
+            t_sum += time.perf_counter() - t0
+            live = int((sub_bits != 0).sum())
+            b_sum += codes.size + 320 * live + 5 * sub_bits.size
+            n_rows += brs.size * 64
+        return t_sum, b_sum, n_rows
+
+    t1, _, _ = run(1)  # calibration
+    rows_per = int(max(1, min(64, round(target_s / max(t1, 1e-3)))))
+    total_t, total_b, sample_rows = run(rows_per)
+    return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s",
+            "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"first {rows_per} block rows ({sample_rows} output rows total) of each of "
+                      f"the 7 linears, M=1: unpack + fp64 dequantize + fp64 matmul; "
+                      f"{total_t:.2f} s for {total_b / 1e6:.1f} MB packed"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--prefill-steps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(block rows would shard across GPUs; see the design notes). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_wise_mixed_amd as msq
+    from block_wise_mixed_amd import synth
+
+    msq.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[WORKLOAD]
+
+    # ---- inputs and pack leg -----------------------------------------------------------
+    inputs, packed = [], []
+    pack_ms = 0.0
+    w_bytes = 0
+    for mi_idx, m in enumerate(wl.matrices):
+        mi = synth.matrix_inputs(WORKLOAD, mi_idx)
+        log(f"pack {m.name} {m.N}x{m.K} mean bits {mi.mean_bits:.3f}")
+        Wd = torch.from_numpy(mi.W.view(np.int16)).view(torch.bfloat16).to(dev)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        pw = msq.quantize_pack(Wd, mi.bits, mi.perm_row, mi.perm_col)
+        e1.record()
+        torch.cuda.synchronize()
+        pack_ms += e0.elapsed_time(e1)
+        w_bytes += 2 * m.N * m.K
+        del Wd
+        inputs.append(mi)
+        packed.append(pw)
+    torch.cuda.empty_cache()
+    layer_packed = sum(p.packed_bytes for p in packed)
+    mean_bits = float(sum(int(p.bits.to(torch.int64).sum().item()) for p in packed) /
+                      sum(p.bits.numel() for p in packed))
+    R = max(2, int(np.ceil((1 << 30) / layer_packed)))
+    log(f"layer packed {layer_packed / 1e6:.1f} MB, {R} copies for cache rotation")
+    copies = [packed] + [[p.clone() for p in packed] for _ in range(R - 1)]
+
+    # ---- decode leg (M = 1), one HIP graph per weight copy -----------------------------
+    M = 1
+    xs = [torch.from_numpy(mi.x(M).view(np.int16)).view(torch.bfloat16).to(dev) for mi in inputs]
+    ys = [torch.empty((M, p.N), dtype=torch.float32, device=dev) for p in packed]
+    wss = [torch.empty(max(msq.workspace_bytes(M, p.N, p.K), 256), dtype=torch.uint8, device=dev)
+           for p in packed]
+
+    def decode_step(ws_copy):
+        for i, p in enumerate(ws_copy):
+            msq.gemm(xs[i], p, out=ys[i], workspace=wss[i])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for cp in copies:
+            decode_step(cp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for cp in copies:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            decode_step(cp)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        graphs[s % R].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for s in range(args.steps):
+        graphs[s % R].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    step_decode_bytes = sum(decode_bytes(p, M) for p in packed)
+    value = layer_packed / (ms_per_step * 1e-3) / 1e9
+    hbm_frac = step_decode_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS
+    log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s effective, {hbm_frac:.3f} of HBM")
+
+    # ---- roofline leg: decode kernel on gate_proj, rotating copies --------------------
+    gi = [m.name for m in wl.matrices].index("gate_proj")
+    L = 4 * R
+    g_roof = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_roof):
+        for k in range(L):
+            msq.gemm(xs[gi], copies[k % R][gi], out=ys[gi], workspace=wss[gi])
+    g_roof.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        g_roof.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    launch_us = e0.elapsed_time(e1) * 1e3 / (reps * L)
+    per_launch = decode_bytes(packed[gi], M)
+    achieved = per_launch / (launch_us * 1e-6) / 1e9
+    sha = kernel_source_sha()
+    traffic = measured_traffic(sha)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic,
+                "kernel": "msq decode (k_gemv<1,true> + split-K reduce) on gate_proj 28672x8192, M=1",
+                "bytes_per_launch": per_launch, "avg_launch_us": round(launch_us, 3),
+                "kernel_sha": sha}
+    log(f"roofline: {launch_us:.2f} us/launch, {achieved:.0f} GB/s")
+
+    # ---- prefill leg (M = 2048) --------------------------------------------------------
+    prefill = None
+    if not args.no_prefill:
+        Mp = 2048
+        del graphs, g_roof
+        xp = [torch.from_numpy(mi.x(Mp).view(np.int16)).view(torch.bfloat16).to(dev) for mi in inputs]
+        yp = [torch.empty((Mp, p.N), dtype=torch.float32, device=dev) for p in packed]
+        wsp = [torch.empty(max(msq.workspace_bytes(Mp, p.N, p.K), 256), dtype=torch.uint8,
+                           device=dev) for p in packed]
+        for i, p in enumerate(packed):
+            msq.gemm(xp[i], p, out=yp[i], workspace=wsp[i])
+        torch.cuda.synchronize()
+        e0.record()
+        for s in range(args.prefill_steps):
+            cp = copies[s % R]
+            for i, p in enumerate(cp):
+                msq.gemm(xp[i], p, out=yp[i], workspace=wsp[i])
+        e1.record()
+        torch.cuda.synchronize()
+        ms_p = e0.elapsed_time(e1) / args.prefill_steps
+        flops = sum(prefill_flops(p, Mp) for p in packed)
+        tflops = flops / (ms_p * 1e-3) / 1e12
+        prefill = {"M": Mp, "ms_per_step": round(ms_p, 4), "tflops": round(tflops, 2),
+                   "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                   "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "flops_per_step": flops}
+        log(f"prefill M={Mp}: {ms_p:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        del xp, yp, wsp
+
+    pack = {"ms": round(pack_ms, 3), "weight_bytes": w_bytes,
+            "gbps_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1),
+            "note": "host-side descriptor validation included"}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(inputs)
+        log(f"cpu baseline {cpu['value']} GB/s")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama3-70b-layer decode M=1: q,o 8192x8192; k,v 1024x8192; "
+                               "gate,up 28672x8192; down 8192x28672",
+                   "M": M, "mean_bits": round(mean_bits, 4), "packed_bytes": layer_packed,
+                   "decode_bytes": step_decode_bytes, "weight_copies": R,
+                   "timing": "HIP graph per weight copy, events around the timed replays"},
+        "hbm_frac": round(hbm_frac, 4),
+        "prefill": prefill,
+        "pack": pack,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(t_wall, 4),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,246 @@
+"""Block-wise mixed-precision weight-only quantized matmul for MI355X (gfx950).
+
+Thin ctypes binding over the C ABI of libmsq.so (include/msq.h).  This module
+only marshals arguments: every step of quantize-pack and of y = x . W^T runs
+in the library's HIP kernels.  PyTorch provides device memory and the current
+stream.  There is no fallback: if libmsq.so is missing every call raises.
+
+    pw = quantize_pack(W_bf16_cuda, bits, perm_row, perm_col)   # offline
+    y  = gemm(x_bf16_cuda, pw)                                   # fp32 [M][N]
+
+Method: a bf16 weight is reordered in rows and columns, cut into 64x128
+blocks with a bitwidth from {0,1,2,3,4,8} each, and every block row-group of
+128 is round-to-nearest quantized with its own scale and zero point
+("ScaleBITS" summary page, sections Approach and Limitations).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+__all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspace_bytes",
+           "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M"]
+
+FORMAT_VERSION = 1
+GEMV_MAX_M = 64
+KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmsq.so"
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("MSQ_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+class MsqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        text = _lib.msq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: msq status {status} ({text})")
+
+
+class _Sizes(ctypes.Structure):
+    _fields_ = [("code_bytes", ctypes.c_int64), ("scale_bytes", ctypes.c_int64),
+                ("zero_bytes", ctypes.c_int64), ("offset_bytes", ctypes.c_int64),
+                ("blocks_per_bits", ctypes.c_int64 * 9), ("mean_bits", ctypes.c_double)]
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("bits", ctypes.c_void_p), ("perm_row", ctypes.c_void_p),
+                ("perm_col", ctypes.c_void_p), ("block_offset", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("zero", ctypes.c_void_p), ("code_bytes", ctypes.c_int64)]
+
+
+def load_library():
+    """Load libmsq.so once; raises OSError with the path if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise OSError(f"{path} not found: build it with `python -m block_wise_mixed_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.msq_plan.argtypes = [i64, i64, vp, vp, vp, ctypes.POINTER(_Sizes)]
+    lib.msq_plan.restype = ctypes.c_int
+    lib.msq_quantize_pack.argtypes = [vp, ctypes.POINTER(_Weight), vp]
+    lib.msq_quantize_pack.restype = ctypes.c_int
+    lib.msq_gemm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.msq_gemm_workspace_bytes.restype = sz
+    lib.msq_gemm.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz, vp]
+    lib.msq_gemm.restype = ctypes.c_int
+    lib.msq_gemm_ex.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz, ctypes.c_int, vp]
+    lib.msq_gemm_ex.restype = ctypes.c_int
+    lib.msq_status_string.argtypes = [ctypes.c_int]
+    lib.msq_status_string.restype = ctypes.c_char_p
+    lib.msq_format_version.argtypes = []
+    lib.msq_format_version.restype = ctypes.c_int
+    if lib.msq_format_version() != FORMAT_VERSION:
+        raise OSError(f"{path} implements format {lib.msq_format_version()}, expected {FORMAT_VERSION}")
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MsqError(status, where)
+
+
+def _host(a, dtype) -> np.ndarray:
+    if hasattr(a, "detach"):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=dtype)
+
+
+def plan(N: int, K: int, bits, perm_row, perm_col) -> dict:
+    """Validate a problem on the host (no GPU needed) and return buffer sizes."""
+    lib = load_library()
+    b = _host(bits, np.uint8)
+    pr = _host(perm_row, np.int32)
+    pc = _host(perm_col, np.int32)
+    if N > 0 and K > 0 and N % 64 == 0 and K % 128 == 0 and b.size != (N // 64) * (K // 128):
+        raise ValueError("bits must have (N/64)*(K/128) entries")
+    out = _Sizes()
+    _check(lib.msq_plan(N, K, b.ctypes.data, pr.ctypes.data, pc.ctypes.data, ctypes.byref(out)),
+           "msq_plan")
+    return dict(code_bytes=out.code_bytes, scale_bytes=out.scale_bytes, zero_bytes=out.zero_bytes,
+                offset_bytes=out.offset_bytes, blocks_per_bits=list(out.blocks_per_bits),
+                mean_bits=out.mean_bits)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _as_bf16_cuda(a, device):
+    torch = _torch()
+    if isinstance(a, np.ndarray):
+        if a.dtype != np.uint16:
+            raise TypeError("numpy inputs must be bf16 bit patterns (uint16)")
+        a = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    if a.dtype in (torch.int16, torch.uint16):
+        a = a.view(torch.bfloat16)
+    if a.dtype != torch.bfloat16:
+        raise TypeError(f"expected bf16 data, got {a.dtype}")
+    return a.to(device).contiguous()
+
+
+@dataclass
+class PackedWeight:
+    """Device buffers of one packed weight (format version 1).  Holds the tensors
+    so their memory outlives every call that uses the descriptor."""
+    N: int
+    K: int
+    bits: "object"          # uint8 [N/64][K/128]
+    perm_row: "object"      # int32 [N]
+    perm_col: "object"      # int32 [K]
+    block_offset: "object"  # int32 view of uint32 [N/64][K/128]
+    codes: "object"         # uint8 [code_bytes] (256-byte aligned by the allocator)
+    scale: "object"         # float32 [N/64][K/128][64]
+    zero: "object"          # uint8 [N/64][K/128][64]
+    code_bytes: int
+    mean_bits: float = 0.0
+
+    def descriptor(self) -> _Weight:
+        w = _Weight()
+        w.N, w.K = self.N, self.K
+        w.bits = self.bits.data_ptr()
+        w.perm_row = self.perm_row.data_ptr()
+        w.perm_col = self.perm_col.data_ptr()
+        w.block_offset = self.block_offset.data_ptr()
+        w.codes = self.codes.data_ptr() if self.code_bytes > 0 else None
+        w.scale = self.scale.data_ptr()
+        w.zero = self.zero.data_ptr()
+        w.code_bytes = self.code_bytes
+        return w
+
+    def to_numpy(self) -> dict:
+        return dict(bits=self.bits.cpu().numpy(), perm_row=self.perm_row.cpu().numpy(),
+                    perm_col=self.perm_col.cpu().numpy(),
+                    block_offset=self.block_offset.cpu().numpy().view(np.uint32),
+                    codes=self.codes.cpu().numpy()[: self.code_bytes],
+                    scale=self.scale.cpu().numpy(), zero=self.zero.cpu().numpy())
+
+    def clone(self) -> "PackedWeight":
+        """Independent copy of every buffer (used to defeat caches in benchmarks)."""
+        return PackedWeight(self.N, self.K, self.bits.clone(), self.perm_row.clone(),
+                            self.perm_col.clone(), self.block_offset.clone(), self.codes.clone(),
+                            self.scale.clone(), self.zero.clone(), self.code_bytes, self.mean_bits)
+
+    @property
+    def packed_bytes(self) -> int:
+        """Bytes the decode kernel must read for the weight: codes + scale/zero of live
+        blocks + bit map and offsets + permutations."""
+        nb = int(self.bits.numel())
+        live = int((self.bits != 0).sum().item())
+        return self.code_bytes + 320 * live + 5 * nb + 4 * (self.N + self.K)
+
+
+def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> PackedWeight:
+    """Quantize and pack W (bf16 [N][K], original order) on the GPU."""
+    torch = _torch()
+    lib = load_library()
+    Wd = _as_bf16_cuda(W, device)
+    N, K = int(Wd.shape[0]), int(Wd.shape[1])
+    bh = _host(bits, np.uint8)
+    if N % 64 == 0 and K % 128 == 0 and N > 0 and K > 0:
+        bh = bh.reshape(N // 64, K // 128)
+    ph = _host(perm_row, np.int32)
+    qh = _host(perm_col, np.int32)
+    sizes = plan(N, K, bh, ph, qh)
+    dev = Wd.device
+    code_bytes = int(sizes["code_bytes"])
+    pw = PackedWeight(
+        N, K,
+        bits=torch.from_numpy(bh.copy()).to(dev),
+        perm_row=torch.from_numpy(ph.copy()).to(dev),
+        perm_col=torch.from_numpy(qh.copy()).to(dev),
+        block_offset=torch.empty(bh.shape, dtype=torch.int32, device=dev),
+        codes=torch.empty(max(code_bytes, 256), dtype=torch.uint8, device=dev),
+        scale=torch.empty((N // 64, K // 128, 64), dtype=torch.float32, device=dev),
+        zero=torch.empty((N // 64, K // 128, 64), dtype=torch.uint8, device=dev),
+        code_bytes=code_bytes, mean_bits=float(sizes["mean_bits"]))
+    w = pw.descriptor()
+    _check(lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), _stream_handle(stream)),
+           "msq_quantize_pack")
+    return pw
+
+
+def workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load_library().msq_gemm_workspace_bytes(M, N, K))
+
+
+def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, stream=None):
+    """y = x . W^T (fp32 [M][N], original row order) from packed weights."""
+    torch = _torch()
+    lib = load_library()
+    xd = _as_bf16_cuda(x, pw.bits.device)
+    if xd.dim() != 2 or xd.shape[1] != pw.K:
+        raise ValueError(f"x must be [M][{pw.K}]")
+    M = int(xd.shape[0])
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=xd.device)
+    need = workspace_bytes(M, pw.N, pw.K)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xd.device)
+    w = pw.descriptor()
+    ws_ptr = workspace.data_ptr() if need > 0 else None
+    _check(lib.msq_gemm_ex(xd.data_ptr() if M > 0 else None, M, ctypes.byref(w),
+                           out.data_ptr() if M > 0 else None, ws_ptr, workspace.numel(),
+                           KERNELS[kernel], _stream_handle(stream)), "msq_gemm")
+    return out

@@ -1,0 +1,53 @@
+// Internal declarations of the msq library: launch helpers implemented in the
+// .hip translation units and called by the C-ABI layer (msq_host.cpp).
+// Nothing here is part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msq {
+
+constexpr int kBlockRows = 64;    // rows of W per block (along N)
+constexpr int kBlockCols = 128;   // columns of W per block (along K) = one RTN group
+constexpr uint32_t kNoBlock = 0xFFFFFFFFu;
+
+// Plain-old-data view of a packed weight passed to kernels.
+struct WeightView {
+  int64_t N, K;
+  int NBr, NBc;                // N / 64, K / 128
+  const uint8_t* bits;         // [NBr][NBc]
+  const int32_t* perm_row;     // [N]
+  const int32_t* perm_col;     // [K]
+  const uint32_t* block_offset;// [NBr][NBc] KiB
+  const uint8_t* codes;
+  const float* scale;          // [NBr][NBc][64]
+  const uint8_t* zero;         // [NBr][NBc][64]
+};
+
+// ---- pack (msq_pack.hip)
+hipError_t launch_block_offsets(const uint8_t* bits, int64_t nblocks, uint32_t* offsets,
+                                hipStream_t stream);
+hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* bits,
+                       const int32_t* perm_row, const int32_t* perm_col,
+                       const uint32_t* offsets, uint8_t* codes, float* scale, uint8_t* zero,
+                       hipStream_t stream);
+
+// ---- decode GEMV, M <= 64 (msq_gemv.hip)
+struct GemvPlan {
+  int split;        // K-splits across workgroups
+  int kr;           // block columns per split
+  int mt;           // 16-row tiles of M
+  size_t lds_bytes; // dynamic LDS per workgroup
+  size_t workspace; // bytes of fp32 partials (0 when split == 1)
+};
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
+                       void* workspace, const GemvPlan& plan, hipStream_t stream);
+
+// ---- prefill GEMM, any M (msq_gemm.hip)
+size_t gemm_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
+                       void* workspace, hipStream_t stream);
+
+}  // namespace msq

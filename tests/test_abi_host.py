@@ -1,0 +1,154 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+libmsq.so must load, export every function include/msq.h declares, and refuse
+bad arguments with the documented status codes before touching the GPU.
+msq_plan is host-only and is exercised fully here.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_wise_mixed_amd as msq
+from block_wise_mixed_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, SHAPE, BITS, PERM, SMALL, HIP, UNSUP = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(msq.library_path()):
+        pytest.fail("libmsq.so is not built (run __graft_entry__.build())")
+    return msq.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "msq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w[\w\s\*]*?\b(msq_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"msq_plan", "msq_quantize_pack", "msq_gemm", "msq_gemm_ex",
+            "msq_gemm_workspace_bytes", "msq_status_string", "msq_format_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.msq_status_string(s)
+    assert lib.msq_status_string(99) == b"unknown status"
+    assert lib.msq_format_version() == 1
+
+
+def _plan_raw(lib, N, K, bits, pr, pc):
+    out = msq._Sizes()
+    b = np.ascontiguousarray(bits, np.uint8)
+    p = np.ascontiguousarray(pr, np.int32)
+    q = np.ascontiguousarray(pc, np.int32)
+    st = lib.msq_plan(N, K, b.ctypes.data, p.ctypes.data, q.ctypes.data, ctypes.byref(out))
+    return st, out
+
+
+def test_plan_sizes(lib):
+    c = synth.random_case(256, 512, 0)
+    st, out = _plan_raw(lib, 256, 512, c.bits, c.perm_row, c.perm_col)
+    assert st == OK
+    total = int(c.bits.astype(np.int64).sum())
+    assert out.code_bytes == 1024 * total
+    assert out.scale_bytes == 4 * 256 * 4 and out.zero_bytes == 256 * 4 and out.offset_bytes == 4 * 16
+    hist = np.bincount(c.bits.ravel(), minlength=9)
+    assert list(out.blocks_per_bits) == list(hist)
+    assert out.mean_bits == pytest.approx(total / 16)
+
+
+def test_plan_error_matrix(lib):
+    c = synth.random_case(128, 256, 1)
+    b, p, q = c.bits, c.perm_row, c.perm_col
+    assert _plan_raw(lib, 100, 256, np.zeros(8, np.uint8), np.arange(100), q)[0] == SHAPE
+    assert _plan_raw(lib, 128, 200, b, p, np.arange(200))[0] == SHAPE
+    assert _plan_raw(lib, 0, 256, b, p, q)[0] == SHAPE
+    assert _plan_raw(lib, -64, 256, b, p, q)[0] == SHAPE
+    for bad in (5, 6, 7, 9, 255):
+        bb = b.copy()
+        bb[1, 1] = bad
+        assert _plan_raw(lib, 128, 256, bb, p, q)[0] == BITS
+    pp = p.copy()
+    pp[3] = pp[4]
+    assert _plan_raw(lib, 128, 256, b, pp, q)[0] == PERM
+    qq = q.copy()
+    qq[0] = 256
+    assert _plan_raw(lib, 128, 256, b, p, qq)[0] == PERM
+    qq[0] = -1
+    assert _plan_raw(lib, 128, 256, b, p, qq)[0] == PERM
+    out = msq._Sizes()
+    out.code_bytes = 12345
+    assert lib.msq_plan(128, 256, None, p.ctypes.data, q.ctypes.data, ctypes.byref(out)) == INVALID
+    assert out.code_bytes == 12345  # untouched on error
+    st, _ = _plan_raw(lib, 128, 256, b, p, q)
+    assert st == OK
+
+
+def test_plan_python_wrapper(lib):
+    c = synth.random_case(64, 128, 2)
+    sz = msq.plan(64, 128, c.bits, c.perm_row, c.perm_col)
+    assert sz["code_bytes"] == 1024 * int(c.bits.sum())
+    with pytest.raises(msq.MsqError):
+        msq.plan(64, 128, np.full((1, 1), 7, np.uint8), c.perm_row, c.perm_col)
+
+
+def _fake_weight(N=128, K=256, code_bytes=1 << 20):
+    """Descriptor with aligned, non-null fake addresses: only argument checks may read it."""
+    w = msq._Weight()
+    w.N, w.K = N, K
+    base = 1 << 40
+    w.bits, w.perm_row, w.perm_col = base, base + 4096, base + 8192
+    w.block_offset, w.codes, w.scale, w.zero = base + 12288, base + 16384, base + (1 << 30), base + (1 << 31)
+    w.code_bytes = code_bytes
+    return w
+
+
+def test_gemm_argument_errors_before_any_launch(lib):
+    w = _fake_weight()
+    x, y, ws = 1 << 41, 1 << 42, 1 << 43
+    g = lib.msq_gemm_ex
+    assert g(x, 1, ctypes.byref(w), y, ws, 1 << 30, 7, None) == INVALID        # bad kernel enum
+    assert g(x, 1, None, y, ws, 1 << 30, 0, None) == INVALID                   # null weight
+    assert g(x, -1, ctypes.byref(w), y, ws, 1 << 30, 0, None) == SHAPE         # M < 0
+    assert g(None, 0, ctypes.byref(w), None, None, 0, 0, None) == OK          # M == 0: no-op
+    assert g(None, 4, ctypes.byref(w), y, ws, 1 << 30, 0, None) == INVALID     # null x
+    assert g(x + 2, 4, ctypes.byref(w), y, ws, 1 << 30, 0, None) == INVALID    # misaligned x
+    assert g(x, 65, ctypes.byref(w), y, ws, 1 << 30, 1, None) == UNSUP        # GEMV with M > 64
+    assert g(x, 600, ctypes.byref(w), y, ws, 1, 2, None) == SMALL              # workspace too small
+    assert g(x, 600, ctypes.byref(w), y, ws + 16, 1 << 30, 2, None) == INVALID  # misaligned workspace
+    w2 = _fake_weight(N=100)
+    assert g(x, 1, ctypes.byref(w2), y, ws, 1 << 30, 0, None) == SHAPE
+    w3 = _fake_weight()
+    w3.codes = (1 << 40) + 16400  # not 256-aligned
+    assert g(x, 1, ctypes.byref(w3), y, ws, 1 << 30, 0, None) == INVALID
+    w4 = _fake_weight()
+    w4.scale = None
+    assert lib.msq_gemm(x, 1, ctypes.byref(w4), y, ws, 1 << 30, None) == INVALID
+
+
+def test_quantize_pack_argument_errors_before_any_launch(lib):
+    w = _fake_weight()
+    assert lib.msq_quantize_pack(None, ctypes.byref(w), None) == INVALID
+    assert lib.msq_quantize_pack((1 << 41) + 2, ctypes.byref(w), None) == INVALID
+    assert lib.msq_quantize_pack(1 << 41, None, None) == INVALID
+    w2 = _fake_weight(K=100)
+    assert lib.msq_quantize_pack(1 << 41, ctypes.byref(w2), None) == SHAPE
+
+
+def test_workspace_sizes(lib):
+    assert lib.msq_gemm_workspace_bytes(0, 4096, 4096) == 0
+    assert lib.msq_gemm_workspace_bytes(1, 100, 4096) == 0
+    for M in (1, 16, 64, 65, 2048):
+        ws = lib.msq_gemm_workspace_bytes(M, 4096, 14336)
+        # at least the gathered activations and group sums the prefill kernel stages
+        assert ws >= M * 14336 * 2 + M * 112 * 4

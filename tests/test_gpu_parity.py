@@ -1,0 +1,239 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+* Block offsets, codes, scales (as bit patterns) and zero points: bit-exact.
+* y: max|y - y_ref| / max|y_ref| <= 2e-3 per (matrix, M), the tolerance the
+  method is held to; y_ref is the oracle's fp64 product with the oracle's own
+  dequantized weights.  With max|y_ref| == 0, y must be exactly 0.
+* Integer lattice (s = 1, integer x): y must equal y_ref exactly.
+* Full-size workloads run in the same launch configuration as bench.py
+  (msq_gemm's automatic kernel choice) and are compared on sampled block rows
+  that the oracle computes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from block_wise_mixed_amd import synth
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def msq():
+    import block_wise_mixed_amd as m
+    m.load_library()
+    assert torch.cuda.is_available()
+    return m
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def check_pack(msq, case, block_rows=None):
+    """Pack on the GPU and compare with the oracle (all block rows or the listed ones)."""
+    _log(f"pack {case.name} {case.N}x{case.K}")
+    pw = msq.quantize_pack(case.W, case.bits, case.perm_row, case.perm_col)
+    torch.cuda.synchronize()
+    got = pw.to_numpy()
+    off_ref, cb = oracle.block_offsets(case.bits)
+    assert pw.code_bytes == cb
+    assert np.array_equal(got["block_offset"], off_ref)
+    ref = oracle.quantize(case.W, case.bits, case.perm_row, case.perm_col, block_rows=block_rows,
+                          check=block_rows is None)
+    brs = ref["block_rows"]
+    assert np.array_equal(got["scale"][brs].view(np.uint32), ref["scale"].view(np.uint32))
+    assert np.array_equal(got["zero"][brs], ref["zero"])
+    qb = oracle.msq_oracle.blocks_of(ref["q"])  # [len(brs)][NBc][64][128]
+    bits_sub = case.bits[brs]
+    for b in oracle.SEGMENT_ORDER:
+        ii, cc = np.nonzero(bits_sub == b)
+        if ii.size == 0:
+            continue
+        want = oracle.pack_blocks(qb[ii, cc], b)
+        starts = off_ref[brs[ii], cc].astype(np.int64) * 1024
+        have = got["codes"][starts[:, None] + np.arange(1024 * b)[None, :]]
+        assert np.array_equal(have, want), f"codes differ for {b}-bit blocks"
+    return pw, ref
+
+
+def check_y(msq, pw, case, ref, M, kernel="auto", exact=False, x=None):
+    x = case.x(M) if x is None else x
+    _log(f"gemm {case.name} {case.N}x{case.K} M={M} kernel={kernel}")
+    y = msq.gemm(x, pw, kernel=kernel)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    yref = oracle.reference_gemm(x, ref, case.perm_row, case.perm_col)
+    if yref.shape[1] != case.N:
+        y = y[:, case.perm_row[ref["rows"]]]
+    assert np.isfinite(y).all()
+    if exact:
+        assert np.array_equal(y, yref)
+        return 0.0
+    scale = np.abs(yref).max() if yref.size else 0.0
+    if scale == 0:
+        assert (y == 0).all()
+        return 0.0
+    err = float(np.abs(y - yref).max() / scale)
+    _log(f"   rel err {err:.3e}")
+    assert err <= TOL
+    return err
+
+
+SMALL_DIST = {0: .1, 1: .15, 2: .3, 3: .2, 4: .15, 8: .1}
+
+
+@pytest.mark.parametrize("N,K,seed", [(64, 128, 0), (192, 384, 1), (320, 640, 2), (256, 4096, 3),
+                                      (1024, 256, 4)])
+def test_pack_bit_exact_small(msq, N, K, seed):
+    check_pack(msq, synth.random_case(N, K, seed, dist=SMALL_DIST))
+
+
+@pytest.mark.parametrize("b", [0, 1, 2, 3, 4, 8])
+def test_pack_uniform_bitwidth(msq, b):
+    pw, ref = check_pack(msq, synth.random_case(192, 512, 10 + b, dist={b: 1.0}))
+    if b == 0:
+        assert pw.code_bytes == 0
+
+
+def test_pack_edge_values(msq):
+    """All-zero groups, signed zeros, one-signed groups, tiny (subnormal) and huge values."""
+    c = synth.random_case(128, 512, 20, dist=SMALL_DIST)
+    W = oracle.bf16_to_f32(c.W).copy()
+    Wr = W[np.ix_(c.perm_row, c.perm_col)]
+    Wr[0, :128] = 0.0
+    Wr[1, :128] = -0.0
+    Wr[2, 128:256] = np.abs(Wr[2, 128:256])
+    Wr[3, 256:384] = -np.abs(Wr[3, 256:384])
+    Wr[4, :128] = np.float32(1e-40)  # fp32/bf16 subnormal
+    Wr[5, :128] *= np.float32(1e-38)
+    Wr[6, 128:256] *= np.float32(1e30)
+    Wr[70, 384:] = np.float32(1.5e38)
+    Wr[71, 384:] = np.linspace(-1, 1, 128, dtype=np.float32)
+    W[np.ix_(c.perm_row, c.perm_col)] = Wr
+    c.W = synth.f32_to_bf16_bits(W)
+    check_pack(msq, c)
+
+
+@pytest.mark.parametrize("kernel", ["auto", "gemm"])
+def test_smoke_workload_256x512(msq, kernel):
+    c = synth.matrix_inputs("linear-256x512", 0)
+    pw, ref = check_pack(msq, c)
+    for M in synth.WORKLOADS["linear-256x512"].ms:
+        check_y(msq, pw, c, ref, M, kernel=kernel)
+
+
+@pytest.mark.parametrize("N,K,seed", [(512, 1024, 30), (320, 4096, 31)])
+def test_m_boundary_sweep(msq, N, K, seed):
+    c = synth.random_case(N, K, seed, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    for M in (1, 2, 15, 16, 17, 63, 64, 65, 511, 512, 513):
+        check_y(msq, pw, c, ref, M, kernel="auto")
+        if M <= 64:
+            check_y(msq, pw, c, ref, M, kernel="gemm")
+
+
+@pytest.mark.parametrize("N,K,seed", [(192, 512, 0), (512, 4096, 1)])
+def test_integer_lattice_is_exact(msq, N, K, seed):
+    c, xgen = synth.lattice_case(N, K, seed, dist={0: .1, 1: .2, 2: .2, 3: .2, 4: .2, 8: .1})
+    pw, ref = check_pack(msq, c)
+    assert (ref["s"][np.repeat(c.bits, 64, axis=0) > 0] == 1).all()
+    for M, kernel in ((1, "auto"), (5, "auto"), (64, "auto"), (1, "gemm"), (130, "gemm")):
+        check_y(msq, pw, c, ref, M, kernel=kernel, exact=True, x=xgen(M))
+
+
+def test_all_pruned_gives_zero(msq):
+    c = synth.random_case(128, 256, 40, dist={0: 1.0})
+    pw, ref = check_pack(msq, c)
+    for M, kernel in ((1, "auto"), (3, "auto"), (100, "auto"), (2, "gemm")):
+        y = msq.gemm(c.x(M), pw, kernel=kernel)
+        torch.cuda.synchronize()
+        assert (y.cpu().numpy() == 0).all()
+
+
+def test_empty_batch(msq):
+    c = synth.random_case(128, 256, 41)
+    pw, _ = check_pack(msq, c)
+    y = msq.gemm(np.zeros((0, 256), np.uint16), pw)
+    assert tuple(y.shape) == (0, 128)
+
+
+def test_deterministic(msq):
+    c = synth.random_case(512, 4096, 42, dist=SMALL_DIST)
+    pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
+    pw2 = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
+    torch.cuda.synchronize()
+    assert torch.equal(pw.codes[:pw.code_bytes], pw2.codes[:pw2.code_bytes])
+    for M in (1, 16, 300):
+        x = c.x(M)
+        a = msq.gemm(x, pw)
+        b = msq.gemm(x, pw)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+def test_rejects_wrong_x_shape(msq):
+    c = synth.random_case(64, 128, 43)
+    pw, _ = check_pack(msq, c)
+    with pytest.raises(ValueError):
+        msq.gemm(np.zeros((2, 256), np.uint16), pw)
+    with pytest.raises(msq.MsqError):
+        msq.gemm(c.x(65), pw, kernel="gemv")
+
+
+# ---- full-size workloads, sampled rows --------------------------------------------------
+
+def _sample_block_rows(NBr, seed):
+    g = np.random.default_rng(seed)
+    pick = {0, NBr - 1} | set(int(v) for v in g.choice(NBr, size=min(NBr, 3), replace=False))
+    return np.array(sorted(pick))
+
+
+FULL = [(w, m.name) for w in ("llama3-8b-q_proj", "llama3-8b-mlp", "llama3-8b-down_proj-prefill",
+                              "llama3-70b-layer")
+        for m in synth.WORKLOADS[w].matrices]
+
+
+@pytest.mark.parametrize("workload,matrix", FULL)
+def test_full_size_sampled(msq, workload, matrix):
+    c = synth.matrix_inputs(workload, matrix)
+    brs = _sample_block_rows(c.N // 64, 7)
+    pw, ref = check_pack(msq, c, block_rows=brs)
+    for M in synth.WORKLOADS[workload].ms:
+        check_y(msq, pw, c, ref, M)
+    del pw
+    torch.cuda.empty_cache()
+
+
+def test_graph_replay_matches_eager(msq):
+    """The decode and prefill calls are captured in HIP graphs by bench.py: every replay,
+    with eager work in between, must equal the eager result bit for bit."""
+    c = synth.random_case(1024, 4096, 50, dist=SMALL_DIST)
+    pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
+    for M in (1, 16, 200):
+        x = torch.from_numpy(c.x(M).view(np.int16)).view(torch.bfloat16).cuda()
+        ws = torch.empty(max(msq.workspace_bytes(M, c.N, c.K), 256), dtype=torch.uint8, device="cuda")
+        y_eager = msq.gemm(x, pw)
+        y = torch.empty_like(y_eager)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            msq.gemm(x, pw, out=y, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            msq.gemm(x, pw, out=y, workspace=ws)
+        other = (-x).contiguous()
+        for rep in range(3):
+            y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_eager), f"replay {rep} differs at M={M}"
+            msq.gemm(other, pw, workspace=ws)  # eager work between replays, same workspace
+            torch.cuda.synchronize()
