@@ -108,6 +108,86 @@ __device__ __forceinline__ bf16x8 hi3_operand(const uint4* ch) {
   return unpack_hi3<F>(ch[2]);
 }
 
+// ---- shift-minimizing unpack (used by the M = 1 decode path) --------------------------
+//
+// A field q < 2^w sitting at bit p (p + w <= 7) of a 16-bit half lies inside
+// the bf16 mantissa.  OR-ing exponent e = 134 - p into bits 7..14 makes that
+// half the exact bf16 value 2^(7-p) + q (the mantissa LSB weighs 2^(p-7) of
+// 2^(e-127)), so no shift is needed to bring the field down to bit 0.  One
+// shift per word serves every field that lands in bits 0..6 after it: 1-bit
+// codes in groups of 7 slots, 2-bit codes in groups of 3, 4-bit codes one
+// slot at a time.  For the high plane of 3-bit codes exponent 136 - p gives
+// 2^(9-p) + 4*q_hi.  Each fragment therefore carries a known power-of-two
+// bias per element, removed later with per-32-column activation sums.
+
+// One operand fragment: word i becomes (x_i & mask) | c, four v_and_or_b32
+// with the mask in an SGPR and c in a VGPR (gfx9 VOP3 takes no literal
+// operands, and the compiler does not form this instruction by itself).
+// The compiler's hazard tracking does not look inside inline asm, so the
+// block carries its own wait states.  The trailing s_nop 1 lets a matrix
+// instruction read the results (two wait states after a VALU write).  The
+// leading s_nop 7 covers the opposite order: the compiler may allocate the
+// outputs onto registers that a matrix instruction issued just before still
+// reads as its source, and overwriting them too early corrupts that
+// instruction's operands.  ALU only.
+__device__ __forceinline__ uint4 and_or4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                         uint32_t mask, uint32_t c) {
+  uint4 r;
+  asm("s_nop 7\n\t"
+      "v_and_or_b32 %0, %4, %8, %9\n\t"
+      "v_and_or_b32 %1, %5, %8, %9\n\t"
+      "v_and_or_b32 %2, %6, %8, %9\n\t"
+      "v_and_or_b32 %3, %7, %8, %9\n\t"
+      "s_nop 1"
+      : "=&v"(r.x), "=&v"(r.y), "=&v"(r.z), "=&v"(r.w)
+      : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "s"(mask), "v"(c));
+  return r;
+}
+
+// Slot geometry of fragment F for the shift-minimizing unpack.
+template <int B, int F>
+struct ExpSlot {
+  // chunk, right shift applied to the words, bit position after the shift
+  static constexpr int kw = B == 3 ? 2 : B;  // width of the low (or only) field
+  static constexpr int s = B == 1 ? F : (B == 2 || B == 3 ? F % 8 : F % 4);
+  static constexpr int chunk = B == 1 ? 0 : (B == 2 || B == 3 ? F / 8 : F / 4);
+  static constexpr int group = B == 1 ? s / 7 : (B == 2 || B == 3 ? s / 3 : s);
+  static constexpr int shift = B == 1 ? 7 * group : (B == 2 || B == 3 ? 6 * group : 4 * group);
+  static constexpr int pos = B == 1 ? s - 7 * group : (B == 2 || B == 3 ? 2 * (s - 3 * group) : 0);
+  // high plane of 3-bit blocks: 1-bit field at bit F of chunk 2
+  static constexpr int hgroup = F / 7;
+  static constexpr int hshift = 7 * hgroup;
+  static constexpr int hpos = F - 7 * hgroup;
+};
+
+// Bias of every element of fragment F of a B-bit block under this unpack.
+__host__ __device__ constexpr float exp_bias(int b, int F) {
+  if (b == 8) return 0.0f;
+  int s = b == 1 ? F : (b == 4 ? F % 4 : F % 8);
+  int pos = b == 1 ? s % 7 : (b == 4 ? 0 : 2 * (s % 3));
+  float lo = (float)(1 << (7 - pos));
+  if (b != 3) return lo;
+  return lo + (float)(1 << (9 - (F % 7)));
+}
+
+template <int B, int F>
+__device__ __forceinline__ bf16x8 exp_operand(const uint4* ch) {
+  using G = ExpSlot<B, F>;
+  constexpr uint32_t mask = (((1u << G::kw) - 1u) << G::pos) * 0x00010001u;
+  constexpr uint32_t e = (uint32_t)(134 - G::pos) * 0x00800080u;  // exponent in bits 7..14 of each half
+  const uint4& c = ch[G::chunk];
+  return as_bf16x8(and_or4(c.x >> G::shift, c.y >> G::shift, c.z >> G::shift, c.w >> G::shift, mask, e));
+}
+
+template <int F>
+__device__ __forceinline__ bf16x8 exp_hi3_operand(const uint4* ch) {
+  using G = ExpSlot<3, F>;
+  constexpr uint32_t mask = (1u << G::hpos) * 0x00010001u;
+  constexpr uint32_t e = (uint32_t)(136 - G::hpos) * 0x00800080u;
+  const uint4& c = ch[2];
+  return as_bf16x8(and_or4(c.x >> G::hshift, c.y >> G::hshift, c.z >> G::hshift, c.w >> G::hshift, mask, e));
+}
+
 // Number of 1 KiB chunks of a B-bit block.
 __host__ __device__ constexpr int chunks_of(int b) { return b; }
 

@@ -36,8 +36,10 @@ hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* b
 // ---- decode GEMV, M <= 64 (msq_gemv.hip)
 struct GemvPlan {
   int split;        // K-splits across workgroups
-  int kr;           // block columns per split
+  int kr;           // block columns per split (<= 64)
   int mt;           // 16-row tiles of M
+  int nw;           // wavefronts per workgroup
+  int xs_stride;    // bf16 elements per LDS row of the activation slice
   size_t lds_bytes; // dynamic LDS per workgroup
   size_t workspace; // bytes of fp32 partials (0 when split == 1)
 };

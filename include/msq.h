@@ -135,7 +135,7 @@ typedef struct {
   int64_t N, K;               /* N % 64 == 0, K % 128 == 0, both > 0 */
   const uint8_t *bits;        /* [N/64][K/128], values in {0,1,2,3,4,8} */
   const int32_t *perm_row;    /* [N]: reordered row i <- original row perm_row[i] */
-  const int32_t *perm_col;    /* [K]: reordered col j <- original col perm_col[j] */
+  const int32_t *perm_col;    /* [K]: reordered col j <- original col perm_col[j]; 16-byte aligned */
   uint32_t *block_offset;     /* [N/64][K/128] in KiB; MSQ_NO_BLOCK for 0-bit */
   uint8_t *codes;             /* [code_bytes], 256-byte aligned */
   float *scale;               /* [N/64][K/128][64] */
