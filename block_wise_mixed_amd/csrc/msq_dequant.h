@@ -47,28 +47,42 @@ __device__ __forceinline__ uint32_t shr(uint32_t v) {
   else return v;
 }
 
+// Hide a constant from the optimizer, pinned to a scalar (opq_s) or vector
+// (opq_v) register.  gfx9 VOP3 encodings take no literal operands, so with
+// literal masks the compiler splits (x & mask) | c into two VOP2
+// instructions; with both constants in registers it selects one
+// v_and_or_b32 and still tracks every hazard around the matrix
+// instructions itself.
+__device__ __forceinline__ uint32_t opq_s(uint32_t v) {
+  asm("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t opq_v(uint32_t v) {
+  asm("" : "+v"(v));
+  return v;
+}
+
+// One operand fragment: word i becomes (x_i & mask) | c.
+__device__ __forceinline__ uint4 and_or4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                         uint32_t mask, uint32_t c) {
+  const uint32_t m = opq_s(mask), e = opq_v(c);
+  return uint4{(x0 & m) | e, (x1 & m) | e, (x2 & m) | e, (x3 & m) | e};
+}
+
 // 128 + code for the b-bit field at bits [SH, SH+b) and [16+SH, 16+SH+b) of each word.
 template <int B, int SH>
 __device__ __forceinline__ bf16x8 unpack_magic(const uint4& c) {
   constexpr uint32_t mask = ((1u << B) - 1u) * 0x00010001u;
-  uint4 v;
-  v.x = (shr<SH>(c.x) & mask) | 0x43004300u;
-  v.y = (shr<SH>(c.y) & mask) | 0x43004300u;
-  v.z = (shr<SH>(c.z) & mask) | 0x43004300u;
-  v.w = (shr<SH>(c.w) & mask) | 0x43004300u;
-  return as_bf16x8(v);
+  return as_bf16x8(and_or4(shr<SH>(c.x), shr<SH>(c.y), shr<SH>(c.z), shr<SH>(c.w), mask,
+                           0x43004300u));
 }
 
 // 128 + 4*hi for the 1-bit high plane of a 3-bit block, hi bit at SRC of each half.
 template <int SRC>
 __device__ __forceinline__ bf16x8 unpack_hi3(const uint4& c) {
   constexpr uint32_t mask = 0x00040004u;
-  uint4 v;
-  v.x = (shr<SRC - 2>(c.x) & mask) | 0x43004300u;
-  v.y = (shr<SRC - 2>(c.y) & mask) | 0x43004300u;
-  v.z = (shr<SRC - 2>(c.z) & mask) | 0x43004300u;
-  v.w = (shr<SRC - 2>(c.w) & mask) | 0x43004300u;
-  return as_bf16x8(v);
+  return as_bf16x8(and_or4(shr<SRC - 2>(c.x), shr<SRC - 2>(c.y), shr<SRC - 2>(c.z),
+                           shr<SRC - 2>(c.w), mask, 0x43004300u));
 }
 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
@@ -117,40 +131,24 @@ __device__ __forceinline__ bf16x8 hi3_operand(const uint4* ch) {
 // shift per word serves every field that lands in bits 0..6 after it: 1-bit
 // codes in groups of 7 slots, 2-bit codes in groups of 3, 4-bit codes one
 // slot at a time.  For the high plane of 3-bit codes exponent 136 - p gives
-// 2^(9-p) + 4*q_hi.  Each fragment therefore carries a known power-of-two
-// bias per element, removed later with per-32-column activation sums.
+// 2^(9-p) + 4*q_hi.  8-bit codes are split into their low 7 bits (exponent
+// 134 at bit 0: 128 + q_lo) and their top bit moved to bit 6 (exponent 135:
+// 256 + 128*q_hi), two matrix instructions per fragment like 3-bit codes.
+// Each fragment therefore carries a known bias per element, removed later
+// with per-32-column activation sums.
 
-// One operand fragment: word i becomes (x_i & mask) | c, four v_and_or_b32
-// with the mask in an SGPR and c in a VGPR (gfx9 VOP3 takes no literal
-// operands, and the compiler does not form this instruction by itself).
-// The compiler's hazard tracking does not look inside inline asm, so the
-// block carries its own wait states.  The trailing s_nop 1 lets a matrix
-// instruction read the results (two wait states after a VALU write).  The
-// leading s_nop 7 covers the opposite order: the compiler may allocate the
-// outputs onto registers that a matrix instruction issued just before still
-// reads as its source, and overwriting them too early corrupts that
-// instruction's operands.  ALU only.
-__device__ __forceinline__ uint4 and_or4(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
-                                         uint32_t mask, uint32_t c) {
-  uint4 r;
-  asm("s_nop 7\n\t"
-      "v_and_or_b32 %0, %4, %8, %9\n\t"
-      "v_and_or_b32 %1, %5, %8, %9\n\t"
-      "v_and_or_b32 %2, %6, %8, %9\n\t"
-      "v_and_or_b32 %3, %7, %8, %9\n\t"
-      "s_nop 1"
-      : "=&v"(r.x), "=&v"(r.y), "=&v"(r.z), "=&v"(r.w)
-      : "v"(x0), "v"(x1), "v"(x2), "v"(x3), "s"(mask), "v"(c));
-  return r;
+// Chunk of a B-bit block holding (the low plane of) fragment F.
+template <int B, int F>
+__host__ __device__ constexpr int chunk_of() {
+  return B == 1 ? 0 : (B == 2 || B == 3 ? F / 8 : (B == 4 ? F / 4 : F / 2));
 }
 
-// Slot geometry of fragment F for the shift-minimizing unpack.
+// Slot geometry of fragment F for the shift-minimizing unpack (B in 1..4).
 template <int B, int F>
 struct ExpSlot {
-  // chunk, right shift applied to the words, bit position after the shift
+  // right shift applied to the words, bit position after the shift
   static constexpr int kw = B == 3 ? 2 : B;  // width of the low (or only) field
   static constexpr int s = B == 1 ? F : (B == 2 || B == 3 ? F % 8 : F % 4);
-  static constexpr int chunk = B == 1 ? 0 : (B == 2 || B == 3 ? F / 8 : F / 4);
   static constexpr int group = B == 1 ? s / 7 : (B == 2 || B == 3 ? s / 3 : s);
   static constexpr int shift = B == 1 ? 7 * group : (B == 2 || B == 3 ? 6 * group : 4 * group);
   static constexpr int pos = B == 1 ? s - 7 * group : (B == 2 || B == 3 ? 2 * (s - 3 * group) : 0);
@@ -160,9 +158,10 @@ struct ExpSlot {
   static constexpr int hpos = F - 7 * hgroup;
 };
 
-// Bias of every element of fragment F of a B-bit block under this unpack.
+// Bias of every element of fragment F of a b-bit block under this unpack
+// (both planes together for b = 3 and b = 8).
 __host__ __device__ constexpr float exp_bias(int b, int F) {
-  if (b == 8) return 0.0f;
+  if (b == 8) return 384.0f;
   int s = b == 1 ? F : (b == 4 ? F % 4 : F % 8);
   int pos = b == 1 ? s % 7 : (b == 4 ? 0 : 2 * (s % 3));
   float lo = (float)(1 << (7 - pos));
@@ -170,22 +169,36 @@ __host__ __device__ constexpr float exp_bias(int b, int F) {
   return lo + (float)(1 << (9 - (F % 7)));
 }
 
+// Low (or only) plane of fragment F from its chunk c.
 template <int B, int F>
-__device__ __forceinline__ bf16x8 exp_operand(const uint4* ch) {
-  using G = ExpSlot<B, F>;
-  constexpr uint32_t mask = (((1u << G::kw) - 1u) << G::pos) * 0x00010001u;
-  constexpr uint32_t e = (uint32_t)(134 - G::pos) * 0x00800080u;  // exponent in bits 7..14 of each half
-  const uint4& c = ch[G::chunk];
-  return as_bf16x8(and_or4(c.x >> G::shift, c.y >> G::shift, c.z >> G::shift, c.w >> G::shift, mask, e));
+__device__ __forceinline__ bf16x8 exp_lo(const uint4& c) {
+  if constexpr (B == 8) {
+    constexpr int sh = 8 * (F % 2);
+    return as_bf16x8(and_or4(c.x >> sh, c.y >> sh, c.z >> sh, c.w >> sh, 0x007F007Fu,
+                             134u * 0x00800080u));
+  } else {
+    using G = ExpSlot<B, F>;
+    constexpr uint32_t mask = (((1u << G::kw) - 1u) << G::pos) * 0x00010001u;
+    constexpr uint32_t e = (uint32_t)(134 - G::pos) * 0x00800080u;  // exponent in bits 7..14
+    return as_bf16x8(and_or4(c.x >> G::shift, c.y >> G::shift, c.z >> G::shift, c.w >> G::shift,
+                             mask, e));
+  }
 }
 
-template <int F>
-__device__ __forceinline__ bf16x8 exp_hi3_operand(const uint4* ch) {
-  using G = ExpSlot<3, F>;
-  constexpr uint32_t mask = (1u << G::hpos) * 0x00010001u;
-  constexpr uint32_t e = (uint32_t)(136 - G::hpos) * 0x00800080u;
-  const uint4& c = ch[2];
-  return as_bf16x8(and_or4(c.x >> G::hshift, c.y >> G::hshift, c.z >> G::hshift, c.w >> G::hshift, mask, e));
+// High plane of fragment F (B == 3: from chunk 2; B == 8: from its own chunk).
+template <int B, int F>
+__device__ __forceinline__ bf16x8 exp_hi(const uint4& c) {
+  if constexpr (B == 8) {
+    constexpr int sh = 8 * (F % 2) + 1;
+    return as_bf16x8(and_or4(c.x >> sh, c.y >> sh, c.z >> sh, c.w >> sh, 0x00400040u,
+                             135u * 0x00800080u));
+  } else {
+    using G = ExpSlot<3, F>;
+    constexpr uint32_t mask = (1u << G::hpos) * 0x00010001u;
+    constexpr uint32_t e = (uint32_t)(136 - G::hpos) * 0x00800080u;
+    return as_bf16x8(and_or4(c.x >> G::hshift, c.y >> G::hshift, c.z >> G::hshift,
+                             c.w >> G::hshift, mask, e));
+  }
 }
 
 // Number of 1 KiB chunks of a B-bit block.

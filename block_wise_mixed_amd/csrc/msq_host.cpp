@@ -69,7 +69,7 @@ msq_status weight_ptrs_ok(const msq_weight* w) {
   if (!w->codes && w->code_bytes > 0) return MSQ_ERR_INVALID_ARG;
   if (w->codes && !aligned(w->codes, 256)) return MSQ_ERR_INVALID_ARG;
   if (!aligned(w->perm_row, 4) || !aligned(w->perm_col, 16) || !aligned(w->block_offset, 4) ||
-      !aligned(w->scale, 4))
+      !aligned(w->scale, 16) || !aligned(w->zero, 16))
     return MSQ_ERR_INVALID_ARG;
   return check_shape(w->N, w->K);
 }

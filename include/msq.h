@@ -138,8 +138,8 @@ typedef struct {
   const int32_t *perm_col;    /* [K]: reordered col j <- original col perm_col[j]; 16-byte aligned */
   uint32_t *block_offset;     /* [N/64][K/128] in KiB; MSQ_NO_BLOCK for 0-bit */
   uint8_t *codes;             /* [code_bytes], 256-byte aligned */
-  float *scale;               /* [N/64][K/128][64] */
-  uint8_t *zero;              /* [N/64][K/128][64] */
+  float *scale;               /* [N/64][K/128][64], 16-byte aligned */
+  uint8_t *zero;              /* [N/64][K/128][64], 16-byte aligned */
   int64_t code_bytes;         /* size of the codes buffer in bytes */
 } msq_weight;
 

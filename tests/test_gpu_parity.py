@@ -138,6 +138,30 @@ def test_m_boundary_sweep(msq, N, K, seed):
             check_y(msq, pw, c, ref, M, kernel="gemm")
 
 
+@pytest.fixture(scope="module")
+def shape_cases(msq):
+    """256 x 8192 matrices (64 block columns per block row) with mixed, all 1-bit and all
+    8-bit blocks, packed once for the launch-shape sweep."""
+    out = {}
+    for name, dist, seed in (("mixed", SMALL_DIST, 50), ("1bit", {1: 1.0}, 51), ("8bit", {8: 1.0}, 52)):
+        c = synth.random_case(256, 8192, seed, dist=dist)
+        out[name] = (c,) + check_pack(msq, c)
+    return out
+
+
+@pytest.mark.parametrize("split,waves", [(1, 8), (1, 4), (1, 16), (2, 8), (3, 8), (5, 4), (16, 16),
+                                         (64, 8)])
+@pytest.mark.parametrize("name", ["mixed", "1bit", "8bit"])
+def test_decode_launch_shapes(msq, shape_cases, monkeypatch, name, split, waves):
+    """M = 1 decode in every launch shape the tuning knobs reach: full 64-column ranges
+    (wavefronts then stream more chunks than their ring holds), ragged last ranges, one
+    column per range, 4 to 16 wavefronts per workgroup."""
+    c, pw, ref = shape_cases[name]
+    monkeypatch.setenv("MSQ_GEMV_SPLIT", str(split))
+    monkeypatch.setenv("MSQ_GEMV_WAVES", str(waves))
+    check_y(msq, pw, c, ref, 1)
+
+
 @pytest.mark.parametrize("N,K,seed", [(192, 512, 0), (512, 4096, 1)])
 def test_integer_lattice_is_exact(msq, N, K, seed):
     c, xgen = synth.lattice_case(N, K, seed, dist={0: .1, 1: .2, 2: .2, 3: .2, 4: .2, 8: .1})
