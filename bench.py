@@ -25,6 +25,13 @@ Also reported, each timed in its own leg of the same run:
             rows of every linear, scaled to GB/s.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Two auxiliary modes feed the rocprofv3 counter runs whose results bench.py
+reads back (HBM traffic of the decode kernel):
+  --only-decode NAME --calls C : pack one linear of the layer, run C decode
+                                 calls (M = 1) and exit;
+  --copy-bytes B               : copy B bytes device to device a few times
+                                 (the calibration of the byte counters).
 """
 from __future__ import annotations
 
@@ -120,7 +127,7 @@ def cpu_baseline(inputs, target_s: float = 12.0):
         return t_sum, b_sum, n_rows
 
     t1, _, _ = run(1)  # calibration
-    rows_per = int(max(1, min(64, round(target_s / max(t1, 1e-3)))))
+    rows_per = int(max(1, min(448, round(target_s / max(t1, 1e-3)))))
     total_t, total_b, sample_rows = run(rows_per)
     return {"value": round(total_b / total_t / 1e9, 4), "unit": "GB/s",
             "cores": int(blas_threads), "kind": "oracle",
@@ -137,6 +144,9 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only-decode", default=None, metavar="NAME")
+    ap.add_argument("--calls", type=int, default=20)
+    ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -158,6 +168,31 @@ def main() -> int:
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[WORKLOAD]
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_bytes} bytes 5 times")
+        return 0
+    if args.only_decode is not None:
+        names = [m.name for m in wl.matrices]
+        mi = synth.matrix_inputs(WORKLOAD, names.index(args.only_decode))
+        Wd = torch.from_numpy(mi.W.view(np.int16)).view(torch.bfloat16).to(dev)
+        pw = msq.quantize_pack(Wd, mi.bits, mi.perm_row, mi.perm_col)
+        del Wd
+        x = torch.from_numpy(mi.x(1).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((1, pw.N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(msq.workspace_bytes(1, pw.N, pw.K), 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.calls):
+            msq.gemm(x, pw, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"{args.calls} decode calls on {args.only_decode}: {decode_bytes(pw, 1)} algorithmic "
+            f"bytes per call")
+        return 0
 
     # ---- inputs and pack leg -----------------------------------------------------------
     inputs, packed = [], []
@@ -251,7 +286,8 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "msq decode (k_gemv<1,true> + split-K reduce) on gate_proj 28672x8192, M=1",
+                "kernel": "msq_gemm M=1 on gate_proj 28672x8192: k_prep_m1 + k_gemv_m1 (one call, "
+                          "launch gaps included)",
                 "bytes_per_launch": per_launch, "avg_launch_us": round(launch_us, 3),
                 "kernel_sha": sha}
     log(f"roofline: {launch_us:.2f} us/launch, {achieved:.0f} GB/s")
