@@ -86,63 +86,77 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 
 // ---- GEMM ------------------------------------------------------------------------------
 //
-// Workgroup tile: kBM rows of x_r x kBR block rows (64 outputs each), four
-// wavefronts (wm, wn) = (wave & 1, wave >> 1) of 64 rows x two block rows,
-// one wavefront per SIMD with the whole register file (two blocks of fp32
-// accumulators plus the per-group ones).  Per 128-wide K group c:
-//   - while group c is multiplied, the next group's x_r tile (kBM x 128 bf16)
-//     is loaded into registers, wavefront w loads the codes of the
-//     workgroup's w-th block, and every wavefront loads the scales and zero
-//     points of its two blocks (software pipelining, one group ahead);
-//   - group c: the x_r tile and the codes are in LDS buffer c % 2; per block
-//     the wavefront copies the code chunks to registers; per k-step of 32 it
-//     reads its 4 A fragments from LDS, unpacks 4 B fragments to exact bf16
-//     (128 + q; 3-bit: two planes with bias 256; 8-bit: low 7 bits and top
-//     bit, bias 384), and issues 16 v_mfma_f32_16x16x32_bf16 into the group
-//     accumulators;
+// Workgroup tile: kBM rows of x_r x kBR block rows (64 outputs each); eight
+// wavefronts (wm, wn) = (wave & 1, wave >> 1), each 64 rows x one block row,
+// two wavefronts per SIMD (one workgroup per CU: the LDS holds two stages).
+// Per 128-wide K group c:
+//   - the next group's x_r tile (kBM x 128 bf16), its group sums and the
+//     workgroup's kBR blocks of codes are copied global -> LDS by the
+//     direct-to-LDS loads (global_load_lds_dwordx4) into the other stage,
+//     and each wavefront loads its block's next scales and zero points;
+//   - the wavefront reads its block's code chunks and, per k-step of 32, its
+//     4 A fragments from LDS, unpacks 4 B fragments to exact bf16 (128 + q;
+//     3-bit: two planes with bias 256; 8-bit: low 7 bits and top bit, bias
+//     384), and issues 16 v_mfma_f32_16x16x32_bf16 into group accumulators;
 //   - fold: acc += s_n * acc_g - s_n * (bias + z_n) * sum_x[m][c];
-//   - the prefetched tile and codes go to LDS buffer (c + 1) % 2; one barrier.
-// 0-bit blocks skip the products.  y is scattered to original rows through
-// perm_row.
+//   - wait for its own copies, one barrier.
+// The two stages are distinct LDS objects and the loop is unrolled by two,
+// so the compiler sees that the copies in flight never alias what the
+// products read and adds no wait for them before those reads.  The x_r tile
+// is stored without padding, 16-byte chunk p of row r holding column chunk
+// p ^ (r & 15) (the direct-to-LDS copies write each 1 KiB contiguously; the
+// swizzle keeps the fragment reads free of bank conflicts).  0-bit blocks
+// skip the copies and the products.  y is scattered to original rows
+// through perm_row.
 constexpr int kBM = 128;
 constexpr int kBR = 4;
-constexpr int kWaves = 4;
-constexpr int kWaveBR = kBR / 2;  // block rows per wavefront
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int kAStride = kBlockCols + 8;  // bf16 per LDS row of the A tile: +16 bytes against bank conflicts
-constexpr int kAPieces = kBM * kBlockCols / 8 / kThreads;  // 16-byte pieces per thread per tile
+constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
 
-// Unpacked B operand of fragment F of a B-bit block (low plane for 3- and 8-bit).
-template <int B, int F>
-__device__ __forceinline__ bf16x8 gemm_b_lo(const uint4 (&ch)[8]) {
-  if constexpr (B == 8) return exp_lo<8, F>(ch[F / 2]);
-  else return block_operand<B, F>(ch);
-}
-
-template <int B, int F>
-__device__ __forceinline__ bf16x8 gemm_b_hi(const uint4 (&ch)[8]) {
-  if constexpr (B == 8) return exp_hi<8, F>(ch[F / 2]);
-  else return hi3_operand<F>(ch);
-}
+typedef __attribute__((address_space(3))) void lds_void;
 
 __host__ __device__ constexpr float gemm_bias(int b) {
   return b == 8 ? 384.f : (b == 3 ? 256.f : 128.f);
 }
 
-// acc_g = A . B for one B-bit block: 4 k-steps x 4 row tiles x 4 m tiles.
+// Unpacked B operand of fragment F of a B-bit block (low plane for 3- and 8-bit).
+template <int B, int F>
+__device__ __forceinline__ bf16x8 gemm_b_lo(const uint4* ch) {
+  if constexpr (B == 8) return exp_lo<8, F>(ch[F / 2]);
+  else return block_operand<B, F>(ch);
+}
+
+template <int B, int F>
+__device__ __forceinline__ bf16x8 gemm_b_hi(const uint4* ch) {
+  if constexpr (B == 8) return exp_hi<8, F>(ch[F / 2]);
+  else return hi3_operand<F>(ch);
+}
+
+// One stage of the pipeline in LDS.
+struct Stage {
+  uint4* a;      // x_r tile [kBM][16 chunks], swizzled
+  float* sx;     // group sums [kBM]
+  uint4* codes;  // [kBR][8 chunks][64 lanes]
+};
+
+// acc_g = A . B for this wavefront's B-bit block: 4 k-steps x 4 row tiles x
+// 4 m tiles.  apk[kt] = this lane's byte offset of its A fragment (m tile 0)
+// for k-step kt; m tile mt is 4096 bytes further.
 template <int B>
-__device__ __forceinline__ void group_mfma(const uint16_t* __restrict__ As, int wm,
-                                           const uint4 (&ch)[8], f32x4 (&accg)[4][4]) {
+__device__ __forceinline__ void group_mfma(const Stage& st, int q, const uint32_t (&apk)[4],
+                                           f32x4 (&accg)[4][4]) {
   const int lane = threadIdx.x & 63;
+  uint4 ch[B];
+#pragma unroll
+  for (int t = 0; t < B; ++t) ch[t] = st.codes[(q * 8 + t) * 64 + lane];
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(st.a);
   auto kstep = [&](auto KTc) {
     constexpr int kt = decltype(KTc)::value;
     bf16x8 A[4];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int row = 64 * wm + 16 * mt + (lane & 15);
-      A[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(As + row * kAStride + 32 * kt +
-                                                        8 * (lane >> 4)));
-    }
+    for (int mt = 0; mt < 4; ++mt)
+      A[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(abase + apk[kt] + 4096 * mt));
     auto rstep = [&](auto RTc) {
       constexpr int rt = decltype(RTc)::value;
       constexpr int F = 4 * rt + kt;
@@ -186,214 +200,167 @@ __device__ __forceinline__ void load_meta(const WeightView& w, int r, int c, Blo
   }
 }
 
-// Eight chunks held in named members (not an array): the compiler keeps
-// these in registers even when loads and uses sit in different branches.
-struct Chunks8 {
-  uint4 c0, c1, c2, c3, c4, c5, c6, c7;
-};
-
-// This lane's 16 bytes of chunks 0..7 of a block at base, chunk t read from
-// chunk min(t, last): all eight registers are always written (past the
-// block's b chunks they repeat its last one, which the caches serve).
-__device__ __forceinline__ Chunks8 load_chunks(const uint8_t* base, int last) {
-  Chunks8 k;
-  k.c0 = *reinterpret_cast<const uint4*>(base);
-  k.c1 = *reinterpret_cast<const uint4*>(base + 1024 * min(1, last));
-  k.c2 = *reinterpret_cast<const uint4*>(base + 1024 * min(2, last));
-  k.c3 = *reinterpret_cast<const uint4*>(base + 1024 * min(3, last));
-  k.c4 = *reinterpret_cast<const uint4*>(base + 1024 * min(4, last));
-  k.c5 = *reinterpret_cast<const uint4*>(base + 1024 * min(5, last));
-  k.c6 = *reinterpret_cast<const uint4*>(base + 1024 * min(6, last));
-  k.c7 = *reinterpret_cast<const uint4*>(base + 1024 * min(7, last));
-  return k;
-}
-
-constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
-
-// LDS of k_gemm: two buffers of the x_r tile and its group sums, two buffers
-// of the workgroup's kBR blocks' codes (8 KiB per block), and the bit map and
-// block offsets of the workgroup's block rows for the first kTabG groups.
-struct GemmLds {
-  uint16_t a[2][kBM * kAStride];
-  float sx[2][kBM];
-  uint4 codes[2][kBR][8][64];
-  uint32_t off[kBR][kTabG];
-  uint8_t bits[kBR][kTabG];
-};
-
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1))) void k_gemm(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const float* __restrict__ xsum, int M, WeightView w,
     float* __restrict__ y) {
-  __shared__ GemmLds L;
+  __shared__ __align__(16) uint4 a0[kBM * 16], a1[kBM * 16];
+  __shared__ __align__(16) float sx0[kBM], sx1[kBM];
+  __shared__ __align__(16) uint4 c0s[kBR * 8 * 64], c1s[kBR * 8 * 64];
+  __shared__ uint32_t toff[kBR][kTabG];
+  __shared__ uint8_t tbits[kBR][kTabG];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.x * kBM;
-  const int rb = blockIdx.y * kBR;     // first block row of the workgroup
-  const int r0 = rb + kWaveBR * wn;    // first block row of this wavefront
-  const int rs = rb + wave;            // block row whose codes this wavefront stages
+  const int rb = blockIdx.y * kBR;  // first block row of the workgroup
+  const int r = rb + wn;            // this wavefront's block row
   const int64_t K = w.K;
   const int G = w.NBc;
   const int tabG = min(G, kTabG);
+  const Stage st0{a0, sx0, c0s}, st1{a1, sx1, c1s};
 
   // bitwidth and KiB offset of block (rb + q, c): LDS table, or global past it
   auto block_at = [&](int q, int c, uint32_t& off) __attribute__((always_inline)) -> int {
-    const int r = rb + q;
-    if (r >= w.NBr) {
+    if (rb + q >= w.NBr) {
       off = 0;
       return 0;
     }
     if (c < kTabG) {
-      off = __builtin_amdgcn_readfirstlane(L.off[q][c]);
-      return __builtin_amdgcn_readfirstlane(L.bits[q][c]);
+      off = __builtin_amdgcn_readfirstlane(toff[q][c]);
+      return __builtin_amdgcn_readfirstlane(tbits[q][c]);
     }
-    const int64_t blk = (int64_t)r * w.NBc + c;
+    const int64_t blk = (int64_t)(rb + q) * w.NBc + c;
     off = __builtin_amdgcn_readfirstlane(w.block_offset[blk]);
     return __builtin_amdgcn_readfirstlane(w.bits[blk]);
   };
 
-  // x_r tile loads of group c into registers (zeros past row M)
-  auto load_tile = [&](int c, uint4 (&v)[kAPieces], float& sx) __attribute__((always_inline)) {
+  // Direct-to-LDS copies of group c into stage st: wavefront w copies rows
+  // 16w .. 16w+15 of the x_r tile (rows past M repeat row M - 1; their
+  // products are never stored), wavefronts 0 and 1 the group sums, and the
+  // two wavefronts of block row q alternate its code chunks.
+  auto copy_group = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    const int g = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i) {
-      const int piece = tid + kThreads * i;
-      const int row = piece >> 4, seg = piece & 15;
-      v[i] = uint4{0u, 0u, 0u, 0u};
-      if (m0 + row < M)
-        v[i] = *reinterpret_cast<const uint4*>(xr + (m0 + row) * K + (int64_t)c * kBlockCols + 8 * seg);
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * wave + 4 * i + g;
+      const int64_t mrow = min(m0 + row, (int64_t)M - 1);
+      const uint16_t* src = xr + mrow * K + (int64_t)c * kBlockCols + 8 * (p ^ (row & 15));
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(st.a + (16 * wave + 4 * i) * 16), 16, 0, 0);
     }
-    sx = 0.f;
-    if (tid < kBM && m0 + tid < M) sx = xsum[(m0 + tid) * G + c];
-  };
-  // codes of the staged block of group c; nothing is read for a 0-bit block
-  // (its offset is the MSQ_NO_BLOCK sentinel, and an all-pruned matrix has
-  // no code buffer at all)
-  auto load_staged = [&](int c) __attribute__((always_inline)) -> Chunks8 {
+    if (wave < 2) {
+      const int64_t mrow = min(m0 + 64 * wave + lane, (int64_t)M - 1);
+      __builtin_amdgcn_global_load_lds(xsum + mrow * G + c, (lds_void*)(st.sx + 64 * wave), 4, 0, 0);
+    }
     uint32_t off;
-    const int b = block_at(wave, c, off);
-    Chunks8 k = {};
-    if (b != 0) k = load_chunks(w.codes + (int64_t)off * 1024 + 16 * lane, b - 1);
-    return k;
-  };
-  auto store_stage = [&](int buf, const uint4 (&v)[kAPieces], float sx,
-                         const Chunks8& k) __attribute__((always_inline)) {
+    const int b = block_at(wn, c, off);
+    const uint8_t* cb = w.codes + (int64_t)off * 1024 + 16 * lane;
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i) {
-      const int piece = tid + kThreads * i;
-      const int row = piece >> 4, seg = piece & 15;
-      *reinterpret_cast<uint4*>(&L.a[buf][row * kAStride + 8 * seg]) = v[i];
-    }
-    if (tid < kBM) L.sx[buf][tid] = sx;
-    uint4* dst = L.codes[buf][wave][0] + lane;
-    dst[0] = k.c0;
-    dst[64] = k.c1;
-    dst[128] = k.c2;
-    dst[192] = k.c3;
-    dst[256] = k.c4;
-    dst[320] = k.c5;
-    dst[384] = k.c6;
-    dst[448] = k.c7;
+    for (int t = 0; t < 8; t += 2)
+      if (t + wm < b)
+        __builtin_amdgcn_global_load_lds(cb + 1024 * (t + wm),
+                                         (lds_void*)(st.codes + (wn * 8 + t + wm) * 64), 16, 0, 0);
   };
 
   // the workgroup's bit map and offsets for the first tabG groups
   for (int i = tid; i < kBR * tabG; i += kThreads) {
     const int q = i / tabG, c = i - (i / tabG) * tabG;
-    const int r = rb + q;
-    const int64_t blk = (int64_t)(r < w.NBr ? r : 0) * w.NBc + c;
-    L.bits[q][c] = r < w.NBr ? w.bits[blk] : 0;
-    L.off[q][c] = r < w.NBr ? w.block_offset[blk] : 0u;
+    const int rr = rb + q;
+    const int64_t blk = (int64_t)(rr < w.NBr ? rr : 0) * w.NBc + c;
+    tbits[q][c] = rr < w.NBr ? w.bits[blk] : 0;
+    toff[q][c] = rr < w.NBr ? w.block_offset[blk] : 0u;
   }
   __syncthreads();
 
-  f32x4 acc[kWaveBR][4][4];
+  // this lane's A fragment offsets per k-step (m tile 0), bytes
+  uint32_t apk[4];
+  {
+    const int g = lane >> 4, n = lane & 15;
 #pragma unroll
-  for (int q = 0; q < kWaveBR; ++q)
+    for (int kt = 0; kt < 4; ++kt)
+      apk[kt] = (uint32_t)((64 * wm + n) * 256 + (((4 * kt + g) ^ n) << 4));
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one group from stage st with the block's metadata bm
+  auto compute = [&](const Stage& st, int c, const BlockMeta& bm) __attribute__((always_inline)) {
+    uint32_t unused_off;
+    const int b = block_at(wn, c, unused_off);
+    if (b == 0) return;
+    f32x4 accg[4][4];
+    switch (b) {
+      case 1: group_mfma<1>(st, wn, apk, accg); break;
+      case 2: group_mfma<2>(st, wn, apk, accg); break;
+      case 3: group_mfma<3>(st, wn, apk, accg); break;
+      case 4: group_mfma<4>(st, wn, apk, accg); break;
+      default: group_mfma<8>(st, wn, apk, accg); break;
+    }
+    // group sums of rows 64 wm + 16 mt + 4 (lane >> 4) + i
+    f32x4 sxm[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) acc[q][mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  BlockMeta cur[kWaveBR], nxt[kWaveBR];
-  {
-    uint4 v[kAPieces];
-    float sx;
-    load_tile(0, v, sx);
-    const Chunks8 k = load_staged(0);
-#pragma unroll
-    for (int q = 0; q < kWaveBR; ++q) load_meta(w, r0 + q, 0, cur[q]);
-    store_stage(0, v, sx, k);
-  }
-  __syncthreads();
-
-  for (int c = 0; c < G; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < G;
-    uint4 v[kAPieces];
-    Chunks8 nk;
-    float sx = 0.f;
-    if (more) {
-      load_tile(c + 1, v, sx);
-      nk = load_staged(c + 1);
-#pragma unroll
-      for (int q = 0; q < kWaveBR; ++q) load_meta(w, r0 + q, c + 1, nxt[q]);
-    }
-#pragma unroll
-    for (int q = 0; q < kWaveBR; ++q) {
-      uint32_t unused_off;
-      const int b = block_at(kWaveBR * wn + q, c, unused_off);
-      if (b == 0) continue;
-      // only the first b chunks are meaningful; reading all eight with
-      // static indices keeps the array in registers
-      uint4 ch[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) ch[t] = L.codes[buf][kWaveBR * wn + q][t][lane];
-      f32x4 accg[4][4];
-      switch (b) {
-        case 1: group_mfma<1>(L.a[buf], wm, ch, accg); break;
-        case 2: group_mfma<2>(L.a[buf], wm, ch, accg); break;
-        case 3: group_mfma<3>(L.a[buf], wm, ch, accg); break;
-        case 4: group_mfma<4>(L.a[buf], wm, ch, accg); break;
-        default: group_mfma<8>(L.a[buf], wm, ch, accg); break;
-      }
-      const float bias = gemm_bias(b);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float s = cur[q].s[rt], szz = -s * (bias + (float)cur[q].z[rt]);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sxm = L.sx[buf][64 * wm + 16 * mt + 4 * (lane >> 4) + i];
-            acc[q][mt][rt][i] = fmaf(szz, sxm, fmaf(s, accg[mt][rt][i], acc[q][mt][rt][i]));
-          }
-      }
-    }
-    if (more) {
-      store_stage(buf ^ 1, v, sx, nk);
-#pragma unroll
-      for (int q = 0; q < kWaveBR; ++q) cur[q] = nxt[q];
-    }
-    __syncthreads();
-  }
-
-  // epilogue: y[m][perm_row[n]]
-#pragma unroll
-  for (int q = 0; q < kWaveBR; ++q) {
-    const int r = r0 + q;
-    if (r >= w.NBr) continue;
+      sxm[mt] = *reinterpret_cast<const f32x4*>(st.sx + 64 * wm + 16 * mt + 4 * (lane >> 4));
+    const float bias = gemm_bias(b);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const int64_t row = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
-      int col = w.perm_row[row];
-      col = min(max(col, 0), (int)w.N - 1);
+      const float sc = bm.s[rt], szz = -sc * (bias + (float)bm.z[rt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + 64 * wm + 16 * mt + 4 * (lane >> 4) + i;
-          if (m < M) y[m * w.N + col] = acc[q][mt][rt][i];
-        }
+        for (int i = 0; i < 4; ++i)
+          acc[mt][rt][i] = fmaf(szz, sxm[mt][i], fmaf(sc, accg[mt][rt][i], acc[mt][rt][i]));
     }
+  };
+  // own copies done, then the workgroup barrier (no memory fence: the copies
+  // are the only producer and their completion is what is waited for)
+  auto stage_barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+  };
+
+  BlockMeta cur, nxt;
+  copy_group(st0, 0);
+  load_meta(w, r, 0, cur);
+  stage_barrier();
+
+  for (int c = 0; c < G; c += 2) {
+    // group c from stage 0, group c + 1 arriving in stage 1
+    if (c + 1 < G) {
+      copy_group(st1, c + 1);
+      load_meta(w, r, c + 1, nxt);
+    }
+    compute(st0, c, cur);
+    stage_barrier();
+    if (c + 1 >= G) break;
+    cur = nxt;
+    // group c + 1 from stage 1, group c + 2 arriving in stage 0
+    if (c + 2 < G) {
+      copy_group(st0, c + 2);
+      load_meta(w, r, c + 2, nxt);
+    }
+    compute(st1, c + 1, cur);
+    stage_barrier();
+    cur = nxt;
+  }
+
+  // epilogue: y[m][perm_row[n]]
+  if (r >= w.NBr) return;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t row = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
+    int col = w.perm_row[row];
+    col = min(max(col, 0), (int)w.N - 1);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 64 * wm + 16 * mt + 4 * (lane >> 4) + i;
+        if (m < M) y[m * w.N + col] = acc[mt][rt][i];
+      }
   }
 }
 
