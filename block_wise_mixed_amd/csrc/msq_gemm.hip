@@ -36,18 +36,30 @@ __device__ __forceinline__ float bf16f(uint16_t u) { return __uint_as_float((uin
 // 16-byte loads (when it fits), then every thread gathers chunks of 8
 // reordered columns x_r[m][8q .. 8q+7] = x[m][perm_col[8q ..]] from LDS and
 // stores them contiguously; 16 consecutive chunks are one 128-column group,
-// summed with shuffles.
+// summed with shuffles.  Each group sum S is stored as three bf16 terms
+// S = t0 + t1 + t2 (t0 = bf16(S), t1 = bf16(S - t0), t2 = bf16(S - t0 - t1),
+// exact to fp32 precision) in planes sxs[p][m][0 .. Gp), Gp = G rounded up
+// to a multiple of 32, zero past G: the A operand of the correction product
+// at the end of k_gemm.
 constexpr int kGatherThreads = 256;
 constexpr size_t kGatherMaxLds = 64 * 1024;
 
+__device__ __forceinline__ uint16_t bf16_rn(float v) {
+  f32x2v f = {v, 0.f};
+  bf16x2v h = __builtin_convertvector(f, bf16x2v);
+  return (uint16_t)__builtin_bit_cast(uint32_t, h);
+}
+
+__host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31) & ~(int64_t)31; }
+
 __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __restrict__ x,
-                                                             int64_t K,
+                                                             int64_t K, int64_t M,
                                                              const int32_t* __restrict__ perm_col,
                                                              uint16_t* __restrict__ xr,
-                                                             float* __restrict__ xsum, int staged) {
+                                                             uint16_t* __restrict__ sxs, int staged) {
   const int64_t m = blockIdx.x;
   const int64_t chunks = K / 8;
-  const int G = (int)(K / kBlockCols);
+  const int64_t Gp = padded_groups(K / kBlockCols);
   const uint16_t* xrow = x + m * K;
   uint16_t* srow = reinterpret_cast<uint16_t*>(smem);
   if (staged) {
@@ -58,7 +70,8 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
   }
   const uint16_t* from = staged ? srow : xrow;
   const int kk = (int)K - 1;
-  for (int64_t q0 = 0; q0 < chunks; q0 += kGatherThreads) {
+  const int64_t plane = M * Gp;
+  for (int64_t q0 = 0; q0 < Gp * 16; q0 += kGatherThreads) {
     const int64_t q = q0 + threadIdx.x;
     float part = 0.f;
     if (q < chunks) {
@@ -80,7 +93,16 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
     // a group is 16 consecutive chunks, i.e. 16 consecutive threads
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) part += __shfl_xor(part, d, 64);
-    if (q < chunks && (q & 15) == 0) xsum[m * G + q / 16] = part;
+    if (q < Gp * 16 && (q & 15) == 0) {
+      const uint16_t t0 = bf16_rn(part);
+      const float r1 = part - bf16f(t0);
+      const uint16_t t1 = bf16_rn(r1);
+      const uint16_t t2 = bf16_rn(r1 - bf16f(t1));
+      uint16_t* dst = sxs + m * Gp + q / 16;
+      dst[0] = t0;
+      dst[plane] = t1;
+      dst[2 * plane] = t2;
+    }
   }
 }
 
@@ -90,16 +112,23 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 // wavefronts (wm, wn) = (wave & 1, wave >> 1), each 64 rows x one block row,
 // two wavefronts per SIMD (one workgroup per CU: the LDS holds two stages).
 // Per 128-wide K group c:
-//   - the next group's x_r tile (kBM x 128 bf16), its group sums and the
-//     workgroup's kBR blocks of codes are copied global -> LDS by the
-//     direct-to-LDS loads (global_load_lds_dwordx4) into the other stage,
-//     and each wavefront loads its block's next scales and zero points;
-//   - the wavefront reads its block's code chunks and, per k-step of 32, its
-//     4 A fragments from LDS, unpacks 4 B fragments to exact bf16 (128 + q;
-//     3-bit: two planes with bias 256; 8-bit: low 7 bits and top bit, bias
-//     384), and issues 16 v_mfma_f32_16x16x32_bf16 into group accumulators;
-//   - fold: acc += s_n * acc_g - s_n * (bias + z_n) * sum_x[m][c];
+//   - the next group's x_r tile (kBM x 128 bf16) and the workgroup's kBR
+//     blocks of codes are copied global -> LDS by the direct-to-LDS loads
+//     (global_load_lds_dwordx4) into the other stage, and each wavefront
+//     loads its block's next scales;
+//   - the wavefront reads its 16 A fragments (4 k-steps x 4 m tiles) from
+//     LDS and, row tile by row tile, the code chunks that tile needs,
+//     unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: two planes
+//     with bias 256; 8-bit: low 7 bits and top bit, bias 384), issues 16
+//     v_mfma_f32_16x16x32_bf16 (32 for two planes) into a group accumulator
+//     and folds it, acc += s_n * acc_g, while the next row tile's products
+//     run;
 //   - wait for its own copies, one barrier.
+// acc_g carries the unpack bias and the zero point: acc_g = sum_k (bias +
+// q_k) x_k = sum_k (q_k - z) x_k + (bias + z) S_c with S_c the group's sum
+// of x_r.  The term sum_c s_c (bias + z_c) S_c of every output is removed at
+// the end by one more matrix product over the groups (see below), so the
+// fold is a single FMA per output and group.
 // The two stages are distinct LDS objects and the loop is unrolled by two,
 // so the compiler sees that the copies in flight never alias what the
 // products read and adds no wait for them before those reads.  The x_r tile
@@ -120,96 +149,135 @@ __host__ __device__ constexpr float gemm_bias(int b) {
   return b == 8 ? 384.f : (b == 3 ? 256.f : 128.f);
 }
 
-// Unpacked B operand of fragment F of a B-bit block (low plane for 3- and 8-bit).
-template <int B, int F>
-__device__ __forceinline__ bf16x8 gemm_b_lo(const uint4* ch) {
-  if constexpr (B == 8) return exp_lo<8, F>(ch[F / 2]);
-  else return block_operand<B, F>(ch);
-}
-
-template <int B, int F>
-__device__ __forceinline__ bf16x8 gemm_b_hi(const uint4* ch) {
-  if constexpr (B == 8) return exp_hi<8, F>(ch[F / 2]);
-  else return hi3_operand<F>(ch);
-}
-
 // One stage of the pipeline in LDS.
 struct Stage {
   uint4* a;      // x_r tile [kBM][16 chunks], swizzled
-  float* sx;     // group sums [kBM]
   uint4* codes;  // [kBR][8 chunks][64 lanes]
 };
 
-// acc_g = A . B for this wavefront's B-bit block: 4 k-steps x 4 row tiles x
-// 4 m tiles.  apk[kt] = this lane's byte offset of its A fragment (m tile 0)
-// for k-step kt; m tile mt is 4096 bytes further.
-template <int B>
-__device__ __forceinline__ void group_mfma(const Stage& st, int q, const uint32_t (&apk)[4],
-                                           f32x4 (&accg)[4][4]) {
-  const int lane = threadIdx.x & 63;
-  uint4 ch[B];
-#pragma unroll
-  for (int t = 0; t < B; ++t) ch[t] = st.codes[(q * 8 + t) * 64 + lane];
-  const unsigned char* abase = reinterpret_cast<const unsigned char*>(st.a);
-  auto kstep = [&](auto KTc) {
-    constexpr int kt = decltype(KTc)::value;
-    bf16x8 A[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      A[mt] = as_bf16x8(*reinterpret_cast<const uint4*>(abase + apk[kt] + 4096 * mt));
-    auto rstep = [&](auto RTc) {
-      constexpr int rt = decltype(RTc)::value;
-      constexpr int F = 4 * rt + kt;
-      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-      const bf16x8 bop = gemm_b_lo<B, F>(ch);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        accg[mt][rt] = mfma_bf16(A[mt], bop, kt == 0 ? zero : accg[mt][rt]);
-      if constexpr (B == 3 || B == 8) {
-        const bf16x8 hop = gemm_b_hi<B, F>(ch);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) accg[mt][rt] = mfma_bf16(A[mt], hop, accg[mt][rt]);
-      }
-    };
-    rstep(std::integral_constant<int, 0>{});
-    rstep(std::integral_constant<int, 1>{});
-    rstep(std::integral_constant<int, 2>{});
-    rstep(std::integral_constant<int, 3>{});
-  };
-  kstep(std::integral_constant<int, 0>{});
-  kstep(std::integral_constant<int, 1>{});
-  kstep(std::integral_constant<int, 2>{});
-  kstep(std::integral_constant<int, 3>{});
+// Chunk of a B-bit block holding (the low plane of) fragment F.
+template <int B, int F>
+__host__ __device__ constexpr int lo_chunk() {
+  return B == 1 ? 0 : (B == 2 || B == 3 ? F / 8 : (B == 4 ? F / 4 : F / 2));
 }
 
-// Scale and zero point of rows 16*rt + (lane & 15) of a block, as loaded (the
-// conversions happen at the fold, so that issuing these loads never waits).
-struct BlockMeta {
-  float s[4];
-  uint32_t z[4];
-};
+// Unpacked B operand of fragment F from its chunk c (low plane for 3 and 8 bits).
+template <int B, int F>
+__device__ __forceinline__ bf16x8 b_lo(const uint4& c) {
+  if constexpr (B == 1) return unpack_magic<1, F>(c);
+  else if constexpr (B == 2 || B == 3) return unpack_magic<2, 2 * (F % 8)>(c);
+  else if constexpr (B == 4) return unpack_magic<4, 4 * (F % 4)>(c);
+  else return exp_lo<8, F>(c);
+}
 
-__device__ __forceinline__ void load_meta(const WeightView& w, int r, int c, BlockMeta& bm) {
+// High plane: 3 bits from chunk 2 (c), 8 bits from the fragment's own chunk.
+template <int B, int F>
+__device__ __forceinline__ bf16x8 b_hi(const uint4& c) {
+  if constexpr (B == 8) return exp_hi<8, F>(c);
+  else return unpack_hi3<F>(c);
+}
+
+// One group of this wavefront's B-bit block (block row q of the workgroup,
+// scales sc of rows 16 rt + (lane & 15)), row tile by row tile: the 16 A
+// fragments (4 k-steps x 4 m tiles) are read from LDS once; per row tile rt
+// the code chunks it needs are read, its 4 B fragments unpacked, 16 (two
+// planes: 32) matrix instructions accumulate acc_g, and the fold
+// acc += s_n * acc_g is issued while the next row tile's products run (one
+// basic block, so the scheduler interleaves them).  apk[kt] = this lane's
+// byte offset of its A fragment (m tile 0) for k-step kt; m tile mt is 4096
+// bytes further.
+template <int B>
+__device__ __forceinline__ void group_mfma(const Stage& st, int q, const uint32_t (&apk)[4],
+                                           const float (&sc)[4], f32x4 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const uint4* cb = st.codes + q * 8 * 64 + lane;
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(st.a);
+  bf16x8 A[4][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      A[kt][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(abase + apk[kt] + 4096 * mt));
+  auto rstep = [&](auto RTc) __attribute__((always_inline)) {
+    constexpr int rt = decltype(RTc)::value;
+    constexpr int k0 = lo_chunk<B, 4 * rt>(), k1 = lo_chunk<B, 4 * rt + 3>();
+    const uint4 c0 = cb[64 * k0];
+    const uint4 c1 = k1 == k0 ? c0 : cb[64 * k1];
+    uint4 c2 = c0;
+    if constexpr (B == 3) c2 = cb[64 * 2];
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 g[4];
+    auto kstep = [&](auto KTc) __attribute__((always_inline)) {
+      constexpr int kt = decltype(KTc)::value;
+      constexpr int F = 4 * rt + kt;
+      const uint4& c = lo_chunk<B, F>() == k0 ? c0 : c1;
+      const bf16x8 bop = b_lo<B, F>(c);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], bop, kt == 0 ? zero : g[mt]);
+      if constexpr (B == 3 || B == 8) {
+        const bf16x8 hop = b_hi<B, F>(B == 3 ? c2 : c);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], hop, g[mt]);
+      }
+    };
+    kstep(std::integral_constant<int, 0>{});
+    kstep(std::integral_constant<int, 1>{});
+    kstep(std::integral_constant<int, 2>{});
+    kstep(std::integral_constant<int, 3>{});
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mt][rt][i] = fmaf(sc[rt], g[mt][i], acc[mt][rt][i]);
+  };
+  rstep(std::integral_constant<int, 0>{});
+  rstep(std::integral_constant<int, 1>{});
+  rstep(std::integral_constant<int, 2>{});
+  rstep(std::integral_constant<int, 3>{});
+}
+
+// Scales of rows 16 rt + (lane & 15) of block (r, c).
+__device__ __forceinline__ void load_scales(const WeightView& w, int r, int c, float (&s)[4]) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = r < w.NBr ? (int64_t)r * w.NBc + c : 0;  // in range for absent rows
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int n = 16 * rt + (lane & 15);
-    bm.s[rt] = w.scale[blk * kBlockRows + n];
-    bm.z[rt] = w.zero[blk * kBlockRows + n];
-  }
+  for (int rt = 0; rt < 4; ++rt) s[rt] = w.scale[blk * kBlockRows + 16 * rt + (lane & 15)];
+}
+
+// Correction product.  With T[n][c] = -s[n][c] (bias_c + z[n][c]) (0 for
+// 0-bit blocks) the outputs need acc[m][n] += sum_c S[m][c] T[n][c], a
+// product over the Gp (padded) groups.  Both operands are split into three
+// bf16 terms (S = S0 + S1 + S2 from the gather kernel, T = T0 + T1 + T2
+// here) and the six products Si Tj with i + j <= 2 are accumulated by the
+// matrix instructions, 32 groups per instruction: the dropped terms are
+// below 2^-24 of |S T| each, i.e. the correction is as accurate as an fp32
+// sum.  Per batch of 32 groups the workgroup writes T for its kBR block
+// rows into LDS in B-operand order, [q][term][row tile][lane][8 groups] as
+// bf16 (12 KiB per block row), then every wavefront multiplies.  The
+// scales, zero points and S terms of the next batch are loaded while the
+// current one is built and multiplied.
+constexpr int kTermBytes = 4 * 64 * 16;  // one term of one block row: 4 row tiles x 1 KiB
+constexpr int kTUnits = kBR * 32 * 16 / kThreads;  // 4 rows per unit, units per thread
+
+// Workgroup barrier that waits for the wavefront's LDS operations only (loads
+// from global memory stay in flight); the empty asm statements keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
-    const uint16_t* __restrict__ xr, const float* __restrict__ xsum, int M, WeightView w,
+    const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
     float* __restrict__ y) {
   __shared__ __align__(16) uint4 a0[kBM * 16], a1[kBM * 16];
-  __shared__ __align__(16) float sx0[kBM], sx1[kBM];
   __shared__ __align__(16) uint4 c0s[kBR * 8 * 64], c1s[kBR * 8 * 64];
   __shared__ uint32_t toff[kBR][kTabG];
   __shared__ uint8_t tbits[kBR][kTabG];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // wavefront (wm, wn): rows 64 wm .. 64 wm + 63 of the tile, block row rb + wn
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.x * kBM;
   const int rb = blockIdx.y * kBR;  // first block row of the workgroup
@@ -217,7 +285,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t K = w.K;
   const int G = w.NBc;
   const int tabG = min(G, kTabG);
-  const Stage st0{a0, sx0, c0s}, st1{a1, sx1, c1s};
+  const Stage st0{a0, c0s}, st1{a1, c1s};
 
   // bitwidth and KiB offset of block (rb + q, c): LDS table, or global past it
   auto block_at = [&](int q, int c, uint32_t& off) __attribute__((always_inline)) -> int {
@@ -236,8 +304,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   // Direct-to-LDS copies of group c into stage st: wavefront w copies rows
   // 16w .. 16w+15 of the x_r tile (rows past M repeat row M - 1; their
-  // products are never stored), wavefronts 0 and 1 the group sums, and the
-  // two wavefronts of block row q alternate its code chunks.
+  // products are never stored), and wavefronts 2q, 2q + 1 alternate the code
+  // chunks of block q.
   auto copy_group = [&](const Stage& st, int c) __attribute__((always_inline)) {
     const int g = lane >> 4, p = lane & 15;
 #pragma unroll
@@ -247,18 +315,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const uint16_t* src = xr + mrow * K + (int64_t)c * kBlockCols + 8 * (p ^ (row & 15));
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(st.a + (16 * wave + 4 * i) * 16), 16, 0, 0);
     }
-    if (wave < 2) {
-      const int64_t mrow = min(m0 + 64 * wave + lane, (int64_t)M - 1);
-      __builtin_amdgcn_global_load_lds(xsum + mrow * G + c, (lds_void*)(st.sx + 64 * wave), 4, 0, 0);
-    }
+    const int q = wave >> 1, half = wave & 1;
     uint32_t off;
-    const int b = block_at(wn, c, off);
+    const int b = block_at(q, c, off);
     const uint8_t* cb = w.codes + (int64_t)off * 1024 + 16 * lane;
 #pragma unroll
     for (int t = 0; t < 8; t += 2)
-      if (t + wm < b)
-        __builtin_amdgcn_global_load_lds(cb + 1024 * (t + wm),
-                                         (lds_void*)(st.codes + (wn * 8 + t + wm) * 64), 16, 0, 0);
+      if (t + half < b)
+        __builtin_amdgcn_global_load_lds(cb + 1024 * (t + half),
+                                         (lds_void*)(st.codes + (q * 8 + t + half) * 64), 16, 0, 0);
   };
 
   // the workgroup's bit map and offsets for the first tabG groups
@@ -280,71 +345,145 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       apk[kt] = (uint32_t)((64 * wm + n) * 256 + (((4 * kt + g) ^ n) << 4));
   }
 
+  // acc[mt][rt]: rows 64 wm + 16 mt + 4 (lane >> 4) + i, output row 16 rt + (lane & 15)
   f32x4 acc[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one group from stage st with the block's metadata bm
-  auto compute = [&](const Stage& st, int c, const BlockMeta& bm) __attribute__((always_inline)) {
+  // one group from stage st with the block's scales sc
+  auto compute = [&](const Stage& st, int c, const float (&sc)[4]) __attribute__((always_inline)) {
     uint32_t unused_off;
     const int b = block_at(wn, c, unused_off);
-    if (b == 0) return;
-    f32x4 accg[4][4];
     switch (b) {
-      case 1: group_mfma<1>(st, wn, apk, accg); break;
-      case 2: group_mfma<2>(st, wn, apk, accg); break;
-      case 3: group_mfma<3>(st, wn, apk, accg); break;
-      case 4: group_mfma<4>(st, wn, apk, accg); break;
-      default: group_mfma<8>(st, wn, apk, accg); break;
-    }
-    // group sums of rows 64 wm + 16 mt + 4 (lane >> 4) + i
-    f32x4 sxm[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-      sxm[mt] = *reinterpret_cast<const f32x4*>(st.sx + 64 * wm + 16 * mt + 4 * (lane >> 4));
-    const float bias = gemm_bias(b);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      const float sc = bm.s[rt], szz = -sc * (bias + (float)bm.z[rt]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[mt][rt][i] = fmaf(szz, sxm[mt][i], fmaf(sc, accg[mt][rt][i], acc[mt][rt][i]));
+      case 0: break;
+      case 1: group_mfma<1>(st, wn, apk, sc, acc); break;
+      case 2: group_mfma<2>(st, wn, apk, sc, acc); break;
+      case 3: group_mfma<3>(st, wn, apk, sc, acc); break;
+      case 4: group_mfma<4>(st, wn, apk, sc, acc); break;
+      default: group_mfma<8>(st, wn, apk, sc, acc); break;
     }
   };
   // own copies done, then the workgroup barrier (no memory fence: the copies
   // are the only producer and their completion is what is waited for)
   auto stage_barrier = [&]() __attribute__((always_inline)) {
+    asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
-  BlockMeta cur, nxt;
+  float cur[4], nxt[4];
   copy_group(st0, 0);
-  load_meta(w, r, 0, cur);
+  load_scales(w, r, 0, cur);
   stage_barrier();
 
   for (int c = 0; c < G; c += 2) {
     // group c from stage 0, group c + 1 arriving in stage 1
     if (c + 1 < G) {
       copy_group(st1, c + 1);
-      load_meta(w, r, c + 1, nxt);
+      load_scales(w, r, c + 1, nxt);
     }
     compute(st0, c, cur);
     stage_barrier();
     if (c + 1 >= G) break;
-    cur = nxt;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
     // group c + 1 from stage 1, group c + 2 arriving in stage 0
     if (c + 2 < G) {
       copy_group(st0, c + 2);
-      load_meta(w, r, c + 2, nxt);
+      load_scales(w, r, c + 2, nxt);
     }
     compute(st1, c + 1, cur);
     stage_barrier();
-    cur = nxt;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
+  }
+
+  // ---- correction product (the stages are free now; T of block rows 0, 1
+  // goes to a0, of block rows 2, 3 to a1)
+  const int64_t Gp = padded_groups(G);
+  auto tq = [&](int q) __attribute__((always_inline)) -> unsigned char* {
+    return reinterpret_cast<unsigned char*>(q < 2 ? a0 : a1) + (q & 1) * 3 * kTermBytes;
+  };
+  static_assert(6 * kTermBytes <= (int)sizeof(a0), "two block rows of T terms per stage buffer");
+  const int64_t plane = (int64_t)M * Gp;
+  // unit u = (q, gl, 4 rows n4 .. n4 + 3) for u = tid + kThreads * k
+  float4 ls[kTUnits];
+  uint32_t lz[kTUnits];
+  int lb[kTUnits];
+  auto load_t = [&](int64_t j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < kTUnits; ++k) {
+      const int u = tid + kThreads * k;
+      const int q = u >> 9, gl = (u >> 4) & 31, n4 = 4 * (u & 15);
+      const int64_t c = j0 + gl;
+      const int rr = rb + q;
+      const bool live = rr < w.NBr && c < G;
+      const int64_t blk = live ? (int64_t)rr * w.NBc + c : 0;
+      lb[k] = !live ? 0 : (c < kTabG ? (int)tbits[q][c] : (int)w.bits[blk]);
+      ls[k] = *reinterpret_cast<const float4*>(w.scale + blk * kBlockRows + n4);
+      lz[k] = *reinterpret_cast<const uint32_t*>(w.zero + blk * kBlockRows + n4);
+    }
+  };
+  bf16x8 Sa[3][4];
+  auto load_s = [&](int64_t j0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int64_t mrow = min(m0 + 64 * wm + 16 * mt + (lane & 15), (int64_t)M - 1);
+      const uint16_t* src = sxs + mrow * Gp + j0 + 8 * (lane >> 4);
+#pragma unroll
+      for (int t = 0; t < 3; ++t)
+        Sa[t][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(src + t * plane));
+    }
+  };
+  load_t(0);
+  for (int64_t j0 = 0; j0 < Gp; j0 += 32) {
+    load_s(j0);
+    lds_barrier();  // previous readers of the stage buffers are done
+#pragma unroll
+    for (int k = 0; k < kTUnits; ++k) {
+      const int u = tid + kThreads * k;
+      const int q = u >> 9, gl = (u >> 4) & 31, n4 = 4 * (u & 15);
+      const float bias = gemm_bias(lb[k]);
+      const float sv[4] = {ls[k].x, ls[k].y, ls[k].z, ls[k].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int n = n4 + e;
+        const float T = lb[k] == 0 ? 0.f : -sv[e] * (bias + (float)((lz[k] >> (8 * e)) & 0xFFu));
+        const uint16_t t0 = bf16_rn(T);
+        const float r1 = T - bf16f(t0);
+        const uint16_t t1 = bf16_rn(r1);
+        const uint16_t t2 = bf16_rn(r1 - bf16f(t1));
+        // B operand order: row tile n >> 4, lane 16 (gl >> 3) + (n & 15), element gl & 7
+        const int at = ((n >> 4) * 64 + (gl >> 3) * 16 + (n & 15)) * 16 + (gl & 7) * 2;
+        *reinterpret_cast<uint16_t*>(tq(q) + at) = t0;
+        *reinterpret_cast<uint16_t*>(tq(q) + kTermBytes + at) = t1;
+        *reinterpret_cast<uint16_t*>(tq(q) + 2 * kTermBytes + at) = t2;
+      }
+    }
+    if (j0 + 32 < Gp) load_t(j0 + 32);
+    lds_barrier();
+    bf16x8 Tb[3][4];
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        Tb[t][rt] = as_bf16x8(
+            *reinterpret_cast<const uint4*>(tq(wn) + t * kTermBytes + (rt * 64 + lane) * 16));
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        f32x4 v = acc[mt][rt];
+        v = mfma_bf16(Sa[2][mt], Tb[0][rt], v);
+        v = mfma_bf16(Sa[1][mt], Tb[1][rt], v);
+        v = mfma_bf16(Sa[0][mt], Tb[2][rt], v);
+        v = mfma_bf16(Sa[1][mt], Tb[0][rt], v);
+        v = mfma_bf16(Sa[0][mt], Tb[1][rt], v);
+        acc[mt][rt] = mfma_bf16(Sa[0][mt], Tb[0][rt], v);
+      }
   }
 
   // epilogue: y[m][perm_row[n]]
@@ -369,7 +508,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 size_t gemm_workspace_bytes(int64_t M, int64_t K) {
   const size_t xr = (size_t)M * K * 2;
   const size_t xr_al = (xr + 255) & ~(size_t)255;
-  return xr_al + (size_t)M * (K / kBlockCols) * 4;
+  return xr_al + 3 * (size_t)M * (size_t)padded_groups(K / kBlockCols) * 2;
 }
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
@@ -377,15 +516,15 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
   const int64_t K = w.K;
   uint16_t* xr = reinterpret_cast<uint16_t*>(workspace);
   const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
-  float* xsum = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) + xr_bytes);
+  uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + xr_bytes);
   const size_t row_bytes = (size_t)K * 2;
   const int staged = row_bytes <= kGatherMaxLds;
   hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M), dim3(kGatherThreads), staged ? row_bytes : 0,
-                     stream, x, K, w.perm_col, xr, xsum, staged);
+                     stream, x, K, M, w.perm_col, xr, sxs, staged);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + kBR - 1) / kBR));
-  hipLaunchKernelGGL(k_gemm, grid, dim3(kThreads), 0, stream, xr, xsum, (int)M, w, y);
+  hipLaunchKernelGGL(k_gemm, grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y);
   return hipGetLastError();
 }
 
