@@ -22,8 +22,9 @@
 //         y[row] += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
 //  4. The wavefronts reduce through LDS in a fixed order.  One K split writes
 //     y directly (scattered to original rows through perm_row); several
-//     splits write fp32 partials that k_gemv_reduce sums in split order, so
-//     results are bitwise reproducible.
+//     splits write fp32 partials that are summed in split order (M == 1: by
+//     the last workgroup of the block row to finish; M > 1: by
+//     k_gemv_reduce), so results are bitwise reproducible.
 //
 // M == 1 has its own kernels (k_prep_m1 + k_gemv_m1): the activation gather
 // runs once per call instead of once per workgroup, the unpack avoids most
@@ -34,6 +35,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <utility>
 
@@ -119,10 +121,11 @@ struct WaveRuns {
 };
 
 // Cut the range's packed order (runs of bitwidths 1, 2, 3, 4, 8) into NW
-// pieces of equal packed size; bl = bitwidth of column `lane` (0 beyond the
-// range).  A block belongs to the piece that holds its first chunk.
+// pieces of equal weight, block k of bitwidth kSegBits[k] weighing wt[k];
+// bl = bitwidth of column `lane` (0 beyond the range).  A block belongs to the
+// piece that holds its first unit of weight.
 template <int NW>
-__device__ __forceinline__ WaveRuns wave_runs(int bl, int wave) {
+__device__ __forceinline__ WaveRuns wave_runs(int bl, int wave, const int (&wt)[5]) {
   uint64_t mask[5];
   int cnt[5], start[5];
   int tot = 0;
@@ -131,13 +134,13 @@ __device__ __forceinline__ WaveRuns wave_runs(int bl, int wave) {
     mask[k] = __ballot(bl == kSegBits[k]);
     cnt[k] = __popcll(mask[k]);
     start[k] = tot;
-    tot += cnt[k] * kSegBits[k];
+    tot += cnt[k] * wt[k];
   }
   const int lo = (wave * tot + NW - 1) / NW, hi = ((wave + 1) * tot + NW - 1) / NW;
   WaveRuns wr;
 #pragma unroll
   for (int k = 0; k < 5; ++k) {
-    const int b = kSegBits[k];
+    const int b = wt[k];
     const int a0 = lo - start[k], a1 = hi - start[k];
     int j0 = a0 <= 0 ? 0 : (a0 + b - 1) / b;
     int j1 = a1 <= 0 ? 0 : (a1 + b - 1) / b;
@@ -150,6 +153,14 @@ __device__ __forceinline__ WaveRuns wave_runs(int bl, int wave) {
   }
   return wr;
 }
+
+// Piece weights: packed size (KiB per block) for the general path; for
+// M == 1, where a block's unpack and matrix instructions take about as long
+// as its loads, the measured per-block cost of a wavefront in units of
+// about 0.1 us (1- and 2-bit blocks alike, 3- and 4-bit alike, 8-bit twice
+// those) so that the wavefronts of a workgroup finish together.
+constexpr int kWeightBytes[5] = {1, 2, 3, 4, 8};
+constexpr int kWeightCostM1[5] = {4, 4, 9, 9, 17};
 
 // ======================================================================================
 // General M (2 .. 64)
@@ -323,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x
   const int64_t rowbase = (int64_t)r * w.NBc + c0;
   const int bl = lane < ncl ? (int)w.bits[rowbase + lane] : 0;
   const uint32_t ol = lane < ncl ? w.block_offset[rowbase + lane] : 0u;
-  const WaveRuns wr = wave_runs<NW>(bl, wave);
+  const WaveRuns wr = wave_runs<NW>(bl, wave, kWeightBytes);
 
   // 2. activation slice
   Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, xs, xsum, xs_stride, kmax, M, 0u, 0u,
@@ -411,8 +422,11 @@ __global__ __launch_bounds__(256) void k_prep_m1(const uint16_t* __restrict__ x,
                                                  const int32_t* __restrict__ perm_col,
                                                  uint16_t* __restrict__ xg,
                                                  float* __restrict__ xsum,
-                                                 float* __restrict__ corr) {
+                                                 float* __restrict__ corr,
+                                                 uint32_t* __restrict__ counters, int ncounters) {
   const int lane = threadIdx.x & 63;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid < ncounters) counters[gid] = 0u;
   const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (c >= K / kBlockCols) return;
   const int64_t j = c * kBlockCols + 2 * lane;
@@ -565,8 +579,8 @@ __host__ __device__ constexpr size_t m1_zero_offset(int kmax) {
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
     const uint16_t* __restrict__ xg, const float* __restrict__ xsum_g,
-    const float* __restrict__ corr_g, WeightView w, int split, int kmax, float* __restrict__ out,
-    int direct) {
+    const float* __restrict__ corr_g, WeightView w, int split, int kmax, float* __restrict__ part,
+    float* __restrict__ y, uint32_t* __restrict__ counters) {
   constexpr int kThreads = NW * 64;
   constexpr int kUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // x slice loads per thread
   constexpr int kCorr4 = kMaxCols * kCorrStride / 4;                 // float4s of the corr slice
@@ -600,7 +614,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   // otherwise sink each load into the conditional LDS store that uses it)
   asm volatile("" ::: "memory");
 
-  const WaveRuns wr = wave_runs<NW>(lane < ncl ? blr : 0, wave);
+  const WaveRuns wr = wave_runs<NW>(lane < ncl ? blr : 0, wave, kWeightCostM1);
   uint32_t off[5];
 #pragma unroll
   for (int k = 0; k < 5; ++k)
@@ -637,17 +651,32 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   float* red = reinterpret_cast<float*>(smem);
   if (wave > 0) red[(wave - 1) * 64 + lane] = y1;
   __syncthreads();
-  if (wave == 0) {
-    float v = y1;
+  if (wave != 0) return;
+  float v = y1;
 #pragma unroll
-    for (int k = 0; k < NW - 1; ++k) v += red[k * 64 + lane];
-    const int64_t row = (int64_t)r * kBlockRows + lane;
-    if (direct) {
-      out[orig_row(w.perm_row, row, w.N)] = v;
-    } else {
-      out[(int64_t)sp * w.N + row] = v;
-    }
+  for (int k = 0; k < NW - 1; ++k) v += red[k * 64 + lane];
+  const int64_t row = (int64_t)r * kBlockRows + lane;
+  if (split == 1) {
+    y[orig_row(w.perm_row, row, w.N)] = v;
+    return;
   }
+  // Several splits: the partials are stored and read back with device-scope
+  // (relaxed atomic) accesses, which go to the level shared by all XCDs, and
+  // the stores are complete before the row's counter (cleared by k_prep_m1)
+  // is incremented; the last workgroup of the row to arrive adds the
+  // partials in split order, so y is reproducible.  No cache-wide write-back
+  // or invalidation is needed.
+  __hip_atomic_store(&part[(int64_t)sp * w.N + row], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  unsigned prev = 0;
+  if (lane == 0)
+    prev = __hip_atomic_fetch_add(&counters[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  if (prev != (unsigned)(split - 1)) return;
+  float tot = 0.f;
+  for (int k = 0; k < split; ++k)
+    tot += __hip_atomic_load(&part[(int64_t)k * w.N + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  y[orig_row(w.perm_row, row, w.N)] = tot;
 }
 
 // ======================================================================================
@@ -678,13 +707,15 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
   y[m * N + orig_row(perm_row, n, N)] = v;
 }
 
-// Workspace layout of one call: [partials | xg | xsum | corr], each part
-// 256-byte aligned; the last three only for M == 1.
+// Workspace layout of one call: [partials | xg | xsum | corr | counters],
+// each part 256-byte aligned; the partials only with several splits, the
+// last four only for M == 1.
 struct GemvWorkspace {
   float* part;
   uint16_t* xg;
   float* xsum;
   float* corr;
+  uint32_t* counters;
 };
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -693,9 +724,10 @@ size_t part_bytes(const GemvPlan& p, int64_t M, int64_t N) {
   return p.split > 1 ? align256((size_t)p.split * M * N * 4) : 0;
 }
 
-size_t m1_prep_bytes(int64_t K) {
-  const size_t nbc = (size_t)(K / kBlockCols);
-  return align256((size_t)K * 2) + align256(nbc * 4) + align256(nbc * kCorrStride * 4);
+size_t m1_prep_bytes(int64_t N, int64_t K) {
+  const size_t nbc = (size_t)(K / kBlockCols), nbr = (size_t)(N / kBlockRows);
+  return align256((size_t)K * 2) + align256(nbc * 4) + align256(nbc * kCorrStride * 4) +
+         align256(nbr * 4);
 }
 
 GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K) {
@@ -710,16 +742,18 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
     g.xsum = reinterpret_cast<float*>(b);
     b += align256(nbc * 4);
     g.corr = reinterpret_cast<float*>(b);
+    b += align256(nbc * kCorrStride * 4);
+    g.counters = reinterpret_cast<uint32_t*>(b);
   }
   return g;
 }
 
 template <int NW>
-hipError_t launch_m1(const GemvWorkspace& g, const WeightView& w, float* dst, const GemvPlan& p,
-                     int direct, hipStream_t stream) {
+hipError_t launch_m1(const GemvWorkspace& g, const WeightView& w, float* y, const GemvPlan& p,
+                     hipStream_t stream) {
   const unsigned grid = (unsigned)(w.NBr * p.split);
   hipLaunchKernelGGL((k_gemv_m1<NW>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, g.xg, g.xsum,
-                     g.corr, w, p.split, p.kr, dst, direct);
+                     g.corr, w, p.split, p.kr, g.part, y, g.counters);
   return hipGetLastError();
 }
 
@@ -741,10 +775,9 @@ int env_int(const char* name, int dflt) {
 
 // Launch shape.  The block columns of a block row are split into `split`
 // ranges of at most 64 columns.  M == 1: at most 512 workgroups of 8
-// wavefronts (two per CU) and at most 16 splits (each split adds a partial
-// plane to the reduce).  M > 1: about 512 workgroups.  MSQ_GEMV_SPLIT and
-// MSQ_GEMV_WAVES override the split count and, for M == 1, the wavefronts per
-// workgroup (tuning only).
+// wavefronts (two per CU) and at most 8 splits.  M > 1: about 512
+// workgroups.  MSQ_GEMV_SPLIT and MSQ_GEMV_WAVES override the split count
+// and, for M == 1, the wavefronts per workgroup (tuning only).
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   GemvPlan p{};
   const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);
@@ -766,7 +799,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   if (split <= 0) {
     if (M == 1) {
       split = 512 / NBr;
-      if (split > 16) split = 16;
+      if (split > 8) split = 8;
     } else {
       split = (512 + NBr - 1) / NBr;
     }
@@ -788,7 +821,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   }
   const size_t red_bytes = (size_t)(p.nw - 1) * (size_t)M * kBlockRows * 4;
   p.lds_bytes = x_bytes > red_bytes ? x_bytes : red_bytes;
-  p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(K) : 0);
+  p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : 0);
   return p;
 }
 
@@ -799,14 +832,17 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
   float* dst = direct ? y : g.part;
   hipError_t e;
   if (M == 1) {
+    // the split counters are cleared here, only needed with several splits
     const int64_t nbc = w.K / kBlockCols;
-    hipLaunchKernelGGL(k_prep_m1, dim3((unsigned)((nbc + 3) / 4)), dim3(256), 0, stream, x, w.K,
-                       w.perm_col, g.xg, g.xsum, g.corr);
+    const int ncounters = p.split > 1 ? (int)w.NBr : 0;
+    const int64_t grid = std::max<int64_t>((nbc + 3) / 4, (ncounters + 255) / 256);
+    hipLaunchKernelGGL(k_prep_m1, dim3((unsigned)grid), dim3(256), 0, stream, x, w.K, w.perm_col,
+                       g.xg, g.xsum, g.corr, g.counters, ncounters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (p.nw == 4) e = launch_m1<4>(g, w, dst, p, direct, stream);
-    else if (p.nw == 16) e = launch_m1<16>(g, w, dst, p, direct, stream);
-    else e = launch_m1<8>(g, w, dst, p, direct, stream);
+    if (p.nw == 4) return launch_m1<4>(g, w, y, p, stream);
+    if (p.nw == 16) return launch_m1<16>(g, w, y, p, stream);
+    return launch_m1<8>(g, w, y, p, stream);
   } else if (p.nw == 8) {
     e = launch_cfg<8, 1>(x, (int)M, w, dst, p, direct, stream);
   } else {
