@@ -85,6 +85,27 @@ __device__ __forceinline__ bf16x8 unpack_hi3(const uint4& c) {
                            shr<SRC - 2>(c.w), mask, 0x43004300u));
 }
 
+// One 3-bit fragment F in a single operand: 128 + q with q = q_lo + 4 q_hi,
+// q_lo the 2-bit field of slot F % 8 of the low plane chunk lo, q_hi bit F
+// of the high plane chunk hi moved to bit 2 (both and-ors merge into one
+// word per pair of codes; the codes stay below 8, so they fit the mantissa).
+__device__ __forceinline__ uint4 and_or4v(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3,
+                                          uint32_t mask, const uint4& t) {
+  const uint32_t m = opq_s(mask);
+  return uint4{(x0 & m) | t.x, (x1 & m) | t.y, (x2 & m) | t.z, (x3 & m) | t.w};
+}
+
+template <int F>
+__device__ __forceinline__ bf16x8 unpack3_magic(const uint4& lo, const uint4& hi) {
+  constexpr int SH = 2 * (F % 8);
+  uint4 t = and_or4(shr<SH>(lo.x), shr<SH>(lo.y), shr<SH>(lo.z), shr<SH>(lo.w), 0x00030003u,
+                    0x43004300u);
+  // opaque, so that each half stays one v_and_or_b32 (not and, and, or3)
+  t = uint4{opq_v(t.x), opq_v(t.y), opq_v(t.z), opq_v(t.w)};
+  return as_bf16x8(and_or4v(shr<F - 2>(hi.x), shr<F - 2>(hi.y), shr<F - 2>(hi.z), shr<F - 2>(hi.w),
+                            0x00040004u, t));
+}
+
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   f32x2v f = {lo, hi};
   bf16x2v h = __builtin_convertvector(f, bf16x2v);

@@ -118,9 +118,10 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 //     loads its block's next scales;
 //   - the wavefront reads its 16 A fragments (4 k-steps x 4 m tiles) from
 //     LDS and, row tile by row tile, the code chunks that tile needs,
-//     unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: two planes
-//     with bias 256; 8-bit: low 7 bits and top bit, bias 384), issues 16
-//     v_mfma_f32_16x16x32_bf16 (32 for two planes) into a group accumulator
+//     unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: both planes
+//     merged into one operand; 8-bit: low 7 bits and top bit, two operands,
+//     bias 384), issues 16 v_mfma_f32_16x16x32_bf16 (32 for 8 bits) into a
+//     group accumulator
 //     and folds it, acc += s_n * acc_g, while the next row tile's products
 //     run;
 //   - wait for its own copies, one barrier.
@@ -145,9 +146,7 @@ constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LD
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-__host__ __device__ constexpr float gemm_bias(int b) {
-  return b == 8 ? 384.f : (b == 3 ? 256.f : 128.f);
-}
+__host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 128.f; }
 
 // One stage of the pipeline in LDS.
 struct Stage {
@@ -161,27 +160,22 @@ __host__ __device__ constexpr int lo_chunk() {
   return B == 1 ? 0 : (B == 2 || B == 3 ? F / 8 : (B == 4 ? F / 4 : F / 2));
 }
 
-// Unpacked B operand of fragment F from its chunk c (low plane for 3 and 8 bits).
+// Unpacked B operand of fragment F from its chunk c (3 bits: low plane chunk
+// c and high plane chunk c2, one operand; 8 bits: the low 7 bits).
 template <int B, int F>
-__device__ __forceinline__ bf16x8 b_lo(const uint4& c) {
+__device__ __forceinline__ bf16x8 b_lo(const uint4& c, const uint4& c2) {
   if constexpr (B == 1) return unpack_magic<1, F>(c);
-  else if constexpr (B == 2 || B == 3) return unpack_magic<2, 2 * (F % 8)>(c);
+  else if constexpr (B == 2) return unpack_magic<2, 2 * (F % 8)>(c);
+  else if constexpr (B == 3) return unpack3_magic<F>(c, c2);
   else if constexpr (B == 4) return unpack_magic<4, 4 * (F % 4)>(c);
   else return exp_lo<8, F>(c);
-}
-
-// High plane: 3 bits from chunk 2 (c), 8 bits from the fragment's own chunk.
-template <int B, int F>
-__device__ __forceinline__ bf16x8 b_hi(const uint4& c) {
-  if constexpr (B == 8) return exp_hi<8, F>(c);
-  else return unpack_hi3<F>(c);
 }
 
 // One group of this wavefront's B-bit block (block row q of the workgroup,
 // scales sc of rows 16 rt + (lane & 15)), row tile by row tile: the 16 A
 // fragments (4 k-steps x 4 m tiles) are read from LDS once; per row tile rt
-// the code chunks it needs are read, its 4 B fragments unpacked, 16 (two
-// planes: 32) matrix instructions accumulate acc_g, and the fold
+// the code chunks it needs are read, its 4 B fragments unpacked, 16 (8 bits:
+// two planes, 32) matrix instructions accumulate acc_g, and the fold
 // acc += s_n * acc_g is issued while the next row tile's products run (one
 // basic block, so the scheduler interleaves them).  apk[kt] = this lane's
 // byte offset of its A fragment (m tile 0) for k-step kt; m tile mt is 4096
@@ -211,11 +205,11 @@ __device__ __forceinline__ void group_mfma(const Stage& st, int q, const uint32_
       constexpr int kt = decltype(KTc)::value;
       constexpr int F = 4 * rt + kt;
       const uint4& c = lo_chunk<B, F>() == k0 ? c0 : c1;
-      const bf16x8 bop = b_lo<B, F>(c);
+      const bf16x8 bop = b_lo<B, F>(c, c2);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], bop, kt == 0 ? zero : g[mt]);
-      if constexpr (B == 3 || B == 8) {
-        const bf16x8 hop = b_hi<B, F>(B == 3 ? c2 : c);
+      if constexpr (B == 8) {
+        const bf16x8 hop = exp_hi<8, F>(c);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], hop, g[mt]);
       }
