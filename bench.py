@@ -26,12 +26,13 @@ Also reported, each timed in its own leg of the same run:
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 
-Two auxiliary modes feed the rocprofv3 counter runs whose results bench.py
-reads back (HBM traffic of the decode kernel):
-  --only-decode NAME --calls C : pack one linear of the layer, run C decode
-                                 calls (M = 1) and exit;
-  --copy-bytes B               : copy B bytes device to device a few times
-                                 (the calibration of the byte counters).
+Auxiliary modes for rocprofv3 counter runs (bench.py reads back the HBM
+traffic of the decode kernel):
+  --only-decode NAME --calls C  : pack one linear of the layer, run C decode
+                                  calls (M = 1) and exit;
+  --only-prefill NAME --calls C : the same with prefill calls (M = 2048);
+  --copy-bytes B                : copy B bytes device to device a few times
+                                  (the calibration of the byte counters).
 """
 from __future__ import annotations
 
@@ -47,6 +48,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "effective weight GB/s & %HBM peak at M=1; TFLOP/s & %MFMA peak at M=2048"
+PREFILL_M = 2048
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "llama3-70b-layer"
@@ -145,6 +147,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-decode", default=None, metavar="NAME")
+    ap.add_argument("--only-prefill", default=None, metavar="NAME")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args()
@@ -176,6 +179,22 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.copy_bytes} bytes 5 times")
+        return 0
+    if args.only_prefill is not None:
+        names = [m.name for m in wl.matrices]
+        mi = synth.matrix_inputs(WORKLOAD, names.index(args.only_prefill))
+        Wd = torch.from_numpy(mi.W.view(np.int16)).view(torch.bfloat16).to(dev)
+        pw = msq.quantize_pack(Wd, mi.bits, mi.perm_row, mi.perm_col)
+        del Wd
+        M = PREFILL_M
+        x = torch.from_numpy(mi.x(M).view(np.int16)).view(torch.bfloat16).to(dev)
+        y = torch.empty((M, pw.N), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(msq.workspace_bytes(M, pw.N, pw.K), 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.calls):
+            msq.gemm(x, pw, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"{args.calls} prefill calls (M = {M}) on {args.only_prefill}")
         return 0
     if args.only_decode is not None:
         names = [m.name for m in wl.matrices]
@@ -295,7 +314,7 @@ def main() -> int:
     # ---- prefill leg (M = 2048) --------------------------------------------------------
     prefill = None
     if not args.no_prefill:
-        Mp = 2048
+        Mp = PREFILL_M
         del graphs, g_roof
         xp = [torch.from_numpy(mi.x(Mp).view(np.int16)).view(torch.bfloat16).to(dev) for mi in inputs]
         yp = [torch.empty((Mp, p.N), dtype=torch.float32, device=dev) for p in packed]
