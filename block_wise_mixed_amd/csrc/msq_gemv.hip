@@ -524,9 +524,9 @@ constexpr int ring_depth() {
 // blocks in flight during each consume.  (An exit from the middle of the
 // unrolled body leaves structurized control-flow paths on which the
 // compiler cannot bound the outstanding loads, and it then waits for all.)
-template <int B>
+template <int B, typename AfterIssue>
 __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
-                                         float& y1) {
+                                         float& y1, AfterIssue&& after_issue) {
   constexpr int D = ring_depth<B>();
   constexpr int64_t kStride = 1024 * B;
   BlockRegs<B> rs[D];
@@ -546,6 +546,7 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
     issue_block<B>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
     asm volatile("" ::: "memory");
   }
+  after_issue();  // the first run: the workgroup's start-up, while these loads fly
   int i0 = 0;  // run index of the block in set 0
   do {
 #pragma unroll
@@ -620,6 +621,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int k = 0; k < 5; ++k)
     off[k] = wr.n[k] > 0 ? __builtin_amdgcn_readlane(ol, __builtin_ctzll(wr.cols[k])) : 0u;
 
+  Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
+         (uint32_t)corr_off, (uint32_t)xsum_off, 0u, 0u};
+  cx.a_lane = (uint32_t)(16 * (lane >> 4));
+  cx.zero_off = zero_off;
+
+  // Start-up: the slices go to LDS now; the workgroup barrier (waiting for
+  // this wavefront's LDS stores only) runs after the wavefront has issued
+  // the loads of its first run's first blocks, so their latency overlaps it.
 #pragma unroll
   for (int u = 0; u < kUnits; ++u) {
     const int idx = t + u * kThreads;
@@ -632,19 +641,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   }
   if (t < ncl) reinterpret_cast<float*>(smem + xsum_off)[t] = sv;
   if (t < 64) reinterpret_cast<uint32_t*>(smem + zero_off)[t] = 0u;
+  asm volatile("" ::: "memory");
+  auto startup = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  auto none = []() __attribute__((always_inline)) {};
 
-  Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
-         (uint32_t)corr_off, (uint32_t)xsum_off, 0u, 0u};
-  cx.a_lane = (uint32_t)(16 * (lane >> 4));
-  cx.zero_off = zero_off;
-  __syncthreads();
-
+  // runs of bitwidths 1, 2, 3, 4, 8 in order; the first non-empty one hosts the start-up
   float y1 = 0.f;
-  if (wr.n[0] > 0) run_ring<1>(cx, run_base(cx, off[0]), wr.cols[0], wr.n[0], y1);
-  if (wr.n[1] > 0) run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1);
-  if (wr.n[2] > 0) run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1);
-  if (wr.n[3] > 0) run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1);
-  if (wr.n[4] > 0) run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1);
+  const int kfirst = wr.n[0] > 0 ? 0 : wr.n[1] > 0 ? 1 : wr.n[2] > 0 ? 2 : wr.n[3] > 0 ? 3 : wr.n[4] > 0 ? 4 : 5;
+  switch (kfirst) {
+    case 0: run_ring<1>(cx, run_base(cx, off[0]), wr.cols[0], wr.n[0], y1, startup); break;
+    case 1: run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1, startup); break;
+    case 2: run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, startup); break;
+    case 3: run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1, startup); break;
+    case 4: run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1, startup); break;
+    default: startup(); break;
+  }
+  if (kfirst < 1 && wr.n[1] > 0) run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1, none);
+  if (kfirst < 2 && wr.n[2] > 0) run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, none);
+  if (kfirst < 3 && wr.n[3] > 0) run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1, none);
+  if (kfirst < 4 && wr.n[4] > 0) run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1, none);
 
   // reduce the wavefronts in a fixed order and write out
   __syncthreads();
