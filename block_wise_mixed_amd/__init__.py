@@ -23,6 +23,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspace_bytes",
+           "gemm_group", "group_workspace_bytes", "GROUP_MAX",
            "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M"]
 
 FORMAT_VERSION = 1
@@ -79,6 +80,12 @@ def load_library():
     lib.msq_gemm.restype = ctypes.c_int
     lib.msq_gemm_ex.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz, ctypes.c_int, vp]
     lib.msq_gemm_ex.restype = ctypes.c_int
+    lib.msq_gemm_group_workspace_bytes.argtypes = [i64, ctypes.POINTER(ctypes.POINTER(_Weight)),
+                                                   ctypes.c_int]
+    lib.msq_gemm_group_workspace_bytes.restype = sz
+    lib.msq_gemm_group.argtypes = [ctypes.POINTER(vp), i64, ctypes.POINTER(ctypes.POINTER(_Weight)),
+                                   ctypes.POINTER(vp), ctypes.c_int, vp, sz, vp]
+    lib.msq_gemm_group.restype = ctypes.c_int
     lib.msq_status_string.argtypes = [ctypes.c_int]
     lib.msq_status_string.restype = ctypes.c_char_p
     lib.msq_format_version.argtypes = []
@@ -223,6 +230,49 @@ def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> Pa
 
 def workspace_bytes(M: int, N: int, K: int) -> int:
     return int(load_library().msq_gemm_workspace_bytes(M, N, K))
+
+
+GROUP_MAX = 8
+
+
+def _descriptor_array(pws):
+    descs = [pw.descriptor() for pw in pws]
+    arr = (ctypes.POINTER(_Weight) * len(descs))(*[ctypes.pointer(d) for d in descs])
+    return descs, arr
+
+
+def group_workspace_bytes(M: int, pws) -> int:
+    descs, arr = _descriptor_array(pws)
+    return int(load_library().msq_gemm_group_workspace_bytes(M, arr, len(descs)))
+
+
+def gemm_group(xs, pws, outs=None, workspace=None, stream=None):
+    """[x_i . W_i^T] for up to GROUP_MAX packed weights in one call (M == 1: one prep
+    and one decode launch for all of them).  xs: one activation per weight (the same
+    tensor may repeat); returns the list of fp32 [M][N_i] outputs."""
+    torch = _torch()
+    lib = load_library()
+    pws = list(pws)
+    if not 1 <= len(pws) <= GROUP_MAX or len(xs) != len(pws):
+        raise ValueError(f"1 to {GROUP_MAX} weights, one activation each")
+    xds = [_as_bf16_cuda(x, pw.bits.device) for x, pw in zip(xs, pws)]
+    M = int(xds[0].shape[0])
+    for xd, pw in zip(xds, pws):
+        if xd.dim() != 2 or xd.shape[1] != pw.K or int(xd.shape[0]) != M:
+            raise ValueError(f"each x must be [M][K] of its weight, one M for all")
+    if outs is None:
+        outs = [torch.empty((M, pw.N), dtype=torch.float32, device=xds[0].device) for pw in pws]
+    descs, arr = _descriptor_array(pws)
+    need = int(lib.msq_gemm_group_workspace_bytes(M, arr, len(descs)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xds[0].device)
+    xa = (ctypes.c_void_p * len(xds))(*[xd.data_ptr() for xd in xds])
+    ya = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    if M > 0:
+        _check(lib.msq_gemm_group(xa, M, arr, ya, len(descs),
+                                  workspace.data_ptr() if need > 0 else None, workspace.numel(),
+                                  _stream_handle(stream)), "msq_gemm_group")
+    return outs
 
 
 def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, stream=None):

@@ -418,16 +418,16 @@ constexpr int kBitsM1[5] = {1, 2, 3, 4, 8};
 constexpr int kCorrStride = 20;  // corr entries per block column: 5 bitwidths x 4 row tiles
 
 // One wavefront per block column; lane l handles columns 2l, 2l + 1.
-__global__ __launch_bounds__(256) void k_prep_m1(const uint16_t* __restrict__ x, int64_t K,
-                                                 const int32_t* __restrict__ perm_col,
-                                                 uint16_t* __restrict__ xg,
-                                                 float* __restrict__ xsum,
-                                                 float* __restrict__ corr,
-                                                 uint32_t* __restrict__ counters, int ncounters) {
+// Workgroup `blk` of the prep of one matrix.
+__device__ __forceinline__ void prep_m1(const uint16_t* __restrict__ x, int64_t K,
+                                        const int32_t* __restrict__ perm_col,
+                                        uint16_t* __restrict__ xg, float* __restrict__ xsum,
+                                        float* __restrict__ corr, uint32_t* __restrict__ counters,
+                                        int ncounters, int blk) {
   const int lane = threadIdx.x & 63;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gid = (int64_t)blk * 256 + threadIdx.x;
   if (gid < ncounters) counters[gid] = 0u;
-  const int64_t c = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t c = (int64_t)blk * 4 + (threadIdx.x >> 6);
   if (c >= K / kBlockCols) return;
   const int64_t j = c * kBlockCols + 2 * lane;
   const int2 p = *reinterpret_cast<const int2*>(perm_col + j);
@@ -446,6 +446,15 @@ __global__ __launch_bounds__(256) void k_prep_m1(const uint16_t* __restrict__ x,
                                    exp_bias(b, 4 * rt + 2) * s2 + exp_bias(b, 4 * rt + 3) * s3;
   }
   if (lane == 0) xsum[c] = (s0 + s1) + (s2 + s3);
+}
+
+__global__ __launch_bounds__(256) void k_prep_m1(const uint16_t* __restrict__ x, int64_t K,
+                                                 const int32_t* __restrict__ perm_col,
+                                                 uint16_t* __restrict__ xg,
+                                                 float* __restrict__ xsum,
+                                                 float* __restrict__ corr,
+                                                 uint32_t* __restrict__ counters, int ncounters) {
+  prep_m1(x, K, perm_col, xg, xsum, corr, counters, ncounters, blockIdx.x);
 }
 
 // Route element 0 of v0..v3, lanes 0..15 (rows 16*rt + l of row tile rt;
@@ -577,11 +586,15 @@ __host__ __device__ constexpr size_t m1_zero_offset(int kmax) {
   return ((size_t)kmax * 340 + 15) & ~(size_t)15;
 }
 
+// Workgroup `blk` (block row blk / split, K range blk % split) of the M == 1
+// decode of one matrix.
 template <int NW>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
-    const uint16_t* __restrict__ xg, const float* __restrict__ xsum_g,
-    const float* __restrict__ corr_g, WeightView w, int split, int kmax, float* __restrict__ part,
-    float* __restrict__ y, uint32_t* __restrict__ counters) {
+__device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
+                                        const float* __restrict__ xsum_g,
+                                        const float* __restrict__ corr_g, const WeightView& w,
+                                        int split, int kmax, float* __restrict__ part,
+                                        float* __restrict__ y, uint32_t* __restrict__ counters,
+                                        int blk) {
   constexpr int kThreads = NW * 64;
   constexpr int kUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // x slice loads per thread
   constexpr int kCorr4 = kMaxCols * kCorrStride / 4;                 // float4s of the corr slice
@@ -589,7 +602,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blockIdx.x / split, sp = blockIdx.x - (blockIdx.x / split) * split;
+  const int r = blk / split, sp = blk - (blk / split) * split;
   const int c0 = sp * kmax;
   const int ncl = min(w.NBc, c0 + kmax) - c0;
   const int64_t rowbase = (int64_t)r * w.NBc + c0;
@@ -696,6 +709,74 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
   for (int k = 0; k < split; ++k)
     tot += __hip_atomic_load(&part[(int64_t)k * w.N + row], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   y[orig_row(w.perm_row, row, w.N)] = tot;
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
+    const uint16_t* __restrict__ xg, const float* __restrict__ xsum_g,
+    const float* __restrict__ corr_g, WeightView w, int split, int kmax, float* __restrict__ part,
+    float* __restrict__ y, uint32_t* __restrict__ counters) {
+  gemv_m1<NW>(xg, xsum_g, corr_g, w, split, kmax, part, y, counters, blockIdx.x);
+}
+
+// ---- grouped M == 1 calls: up to kGroupMax matrices per launch ---------------------------
+// One prep launch and one decode launch cover all matrices of the group (for
+// example the q, k, v projections of a layer, which read the same x); the
+// workgroups of the matrices run side by side, so small matrices no longer
+// leave the GPU idle for a launch of their own.  Job j owns the workgroups
+// [prep_begin, prep_begin of j + 1) of the prep launch and
+// [wg_begin, wg_begin of j + 1) of the decode launch.
+constexpr int kGroupMax = 8;
+
+struct M1Job {
+  WeightView w;
+  const uint16_t* x;
+  uint16_t* xg;
+  float* xsum;
+  float* corr;
+  float* part;
+  float* y;
+  uint32_t* counters;
+  int split, kr, ncounters;
+  int prep_begin, wg_begin;
+};
+
+struct M1Group {
+  M1Job job[kGroupMax];
+  int count;
+};
+
+// The job owning workgroup `b` (first index of the range), selected with
+// static indices only so that the kernel arguments are never copied.
+__device__ __forceinline__ int group_job(const M1Group& g, int b, bool prep) {
+  int j = 0;
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.count && b >= (prep ? g.job[k].prep_begin : g.job[k].wg_begin)) j = k;
+  return j;
+}
+
+// Copy of job j (wavefront-uniform) selected field by field with static indices.
+__device__ __forceinline__ M1Job pick_job(const M1Group& g, int j) {
+  M1Job q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k == j) q = g.job[k];
+  return q;
+}
+
+__global__ __launch_bounds__(256) void k_prep_m1_group(M1Group g) {
+  const M1Job q = pick_job(g, group_job(g, blockIdx.x, true));
+  prep_m1(q.x, q.w.K, q.w.perm_col, q.xg, q.xsum, q.corr, q.counters, q.ncounters,
+          blockIdx.x - q.prep_begin);
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1_group(
+    M1Group g) {
+  const M1Job q = pick_job(g, group_job(g, blockIdx.x, false));
+  gemv_m1<NW>(q.xg, q.xsum, q.corr, q.w, q.split, q.kr, q.part, q.y, q.counters,
+              blockIdx.x - q.wg_begin);
 }
 
 // ======================================================================================
@@ -842,6 +923,57 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   p.lds_bytes = x_bytes > red_bytes ? x_bytes : red_bytes;
   p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : 0);
   return p;
+}
+
+size_t gemv_group_workspace_m1(const WeightView* w, int count) {
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) total += align256(plan_gemv(1, w[i].N, w[i].K).workspace);
+  return total;
+}
+
+hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
+                                int count, void* workspace, hipStream_t stream) {
+  if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+  M1Group g{};
+  g.count = count;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  int prep_total = 0, wg_total = 0, nw = 0;
+  size_t lds = 0;
+  for (int i = 0; i < count; ++i) {
+    const GemvPlan p = plan_gemv(1, w[i].N, w[i].K);
+    if (nw == 0) nw = p.nw;
+    if (p.nw != nw) return hipErrorInvalidValue;
+    const GemvWorkspace gw = carve(ws, p, 1, w[i].N, w[i].K);
+    ws += align256(p.workspace);
+    M1Job& q = g.job[i];
+    q.w = w[i];
+    q.x = x[i];
+    q.xg = gw.xg;
+    q.xsum = gw.xsum;
+    q.corr = gw.corr;
+    q.part = gw.part;
+    q.y = y[i];
+    q.counters = gw.counters;
+    q.split = p.split;
+    q.kr = p.kr;
+    q.ncounters = p.split > 1 ? (int)w[i].NBr : 0;
+    q.prep_begin = prep_total;
+    q.wg_begin = wg_total;
+    const int64_t nbc = w[i].K / kBlockCols;
+    prep_total += (int)std::max<int64_t>((nbc + 3) / 4, (q.ncounters + 255) / 256);
+    wg_total += (int)(w[i].NBr * p.split);
+    lds = std::max(lds, p.lds_bytes);
+  }
+  hipLaunchKernelGGL(k_prep_m1_group, dim3((unsigned)prep_total), dim3(256), 0, stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (nw == 4)
+    hipLaunchKernelGGL((k_gemv_m1_group<4>), dim3((unsigned)wg_total), dim3(256), lds, stream, g);
+  else if (nw == 16)
+    hipLaunchKernelGGL((k_gemv_m1_group<16>), dim3((unsigned)wg_total), dim3(1024), lds, stream, g);
+  else
+    hipLaunchKernelGGL((k_gemv_m1_group<8>), dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,

@@ -179,6 +179,51 @@ msq_status msq_gemm(const uint16_t* x_bf16, int64_t M, const msq_weight* w, floa
   return msq_gemm_ex(x_bf16, M, w, y, workspace, workspace_bytes, MSQ_KERNEL_AUTO, stream);
 }
 
+size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight* const* w, int count) {
+  if (!w || count < 1 || count > MSQ_GROUP_MAX || M <= 0) return 0;
+  msq::WeightView v[MSQ_GROUP_MAX];
+  size_t most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!w[i] || check_shape(w[i]->N, w[i]->K) != MSQ_OK) return 0;
+    v[i] = view_of(w[i]);
+    const size_t one = msq_gemm_workspace_bytes(M, w[i]->N, w[i]->K);
+    most = one > most ? one : most;
+  }
+  // M == 1: every matrix keeps its own workspace during the one launch
+  return M == 1 ? msq::gemv_group_workspace_m1(v, count) : most;
+}
+
+msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
+                          float* const* y, int count, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  static_assert(MSQ_GROUP_MAX == msq::kGemvGroupMax, "group size of the header and the kernels");
+  if (!x_bf16 || !w || !y || count < 1 || count > MSQ_GROUP_MAX) return MSQ_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    const msq_status st = weight_ptrs_ok(w[i]);
+    if (st != MSQ_OK) return st;
+    if (!x_bf16[i] || !y[i] || !aligned(x_bf16[i], 16) || !aligned(y[i], 4))
+      return MSQ_ERR_INVALID_ARG;
+  }
+  if (M < 0) return MSQ_ERR_SHAPE;
+  if (M == 0) return MSQ_OK;
+  if (M != 1) {
+    // one matrix after the other, sharing the workspace (ordered on stream)
+    for (int i = 0; i < count; ++i) {
+      const msq_status st = msq_gemm(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, stream);
+      if (st != MSQ_OK) return st;
+    }
+    return MSQ_OK;
+  }
+  const size_t need = msq_gemm_group_workspace_bytes(M, w, count);
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
+  msq::WeightView v[MSQ_GROUP_MAX];
+  for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
+  return msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream) == hipSuccess
+             ? MSQ_OK
+             : MSQ_ERR_HIP;
+}
+
 const char* msq_status_string(msq_status s) {
   switch (s) {
     case MSQ_OK: return "success";

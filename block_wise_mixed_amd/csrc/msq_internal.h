@@ -47,6 +47,13 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 
+// Grouped M == 1 decode of count (1 .. 8) matrices in one prep and one decode
+// launch; the workspace holds each matrix's single-call workspace in turn.
+constexpr int kGemvGroupMax = 8;
+size_t gemv_group_workspace_m1(const WeightView* w, int count);
+hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
+                                int count, void* workspace, hipStream_t stream);
+
 // ---- prefill GEMM, any M (msq_gemm.hip)
 size_t gemm_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,

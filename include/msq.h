@@ -192,6 +192,31 @@ msq_status msq_gemm_ex(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
                        float *y, void *workspace, size_t workspace_bytes,
                        msq_kernel kernel, hipStream_t stream);
 
+/* Most matrices one msq_gemm_group call takes. */
+#define MSQ_GROUP_MAX 8
+
+/* Bytes of device workspace msq_gemm_group needs for these count matrices
+ * at M rows (M == 1: the sum of the single-call workspaces, since all
+ * matrices are in flight together; otherwise their maximum).  Zero for
+ * M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad shape. */
+size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int count);
+
+/* y[i] = x[i] . W_i^T for count matrices (1 .. MSQ_GROUP_MAX), each exactly
+ * as msq_gemm computes it.  For the decode step of a layer, whose q, k, v
+ * projections (and gate, up) read the same activation: at M == 1 one
+ * activation-prep launch and one decode launch cover all matrices, their
+ * workgroups running side by side ("TileQuant" abstract: local accumulation
+ * to reduce memory traffic; the grouping itself is this library's).  Other
+ * M: the matrices are computed one after the other as by msq_gemm.  x,
+ * w and y are host arrays of count device pointers / descriptors; x[i] may
+ * repeat the same activation.  workspace must hold
+ * msq_gemm_group_workspace_bytes(M, w, count) bytes (256-byte aligned).
+ * Errors as msq_gemm; MSQ_ERR_INVALID_ARG also for a null array or count
+ * outside 1 .. MSQ_GROUP_MAX. */
+msq_status msq_gemm_group(const uint16_t *const *x_bf16, int64_t M,
+                          const msq_weight *const *w, float *const *y, int count,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code; never NULL. */
 const char *msq_status_string(msq_status status);
 

@@ -152,3 +152,43 @@ def test_workspace_sizes(lib):
         ws = lib.msq_gemm_workspace_bytes(M, 4096, 14336)
         # at least the gathered activations and group sums the prefill kernel stages
         assert ws >= M * 14336 * 2 + M * 112 * 4
+
+
+def _group_arrays(ws_list):
+    arr = (ctypes.POINTER(msq._Weight) * len(ws_list))(*[ctypes.pointer(w) for w in ws_list])
+    return arr
+
+
+def test_group_argument_errors_before_any_launch(lib):
+    ws_list = [_fake_weight(), _fake_weight(N=256, K=512)]
+    arr = _group_arrays(ws_list)
+    xs = (ctypes.c_void_p * 2)(1 << 41, 1 << 41)
+    ys = (ctypes.c_void_p * 2)(1 << 42, (1 << 42) + 4096)
+    ws = 1 << 43
+    g = lib.msq_gemm_group
+    assert g(xs, 1, arr, ys, 0, ws, 1 << 30, None) == INVALID      # count 0
+    assert g(xs, 1, arr, ys, 9, ws, 1 << 30, None) == INVALID      # count > MSQ_GROUP_MAX
+    assert g(None, 1, arr, ys, 2, ws, 1 << 30, None) == INVALID    # null array
+    assert g(xs, -1, arr, ys, 2, ws, 1 << 30, None) == SHAPE       # M < 0
+    assert g(xs, 0, arr, ys, 2, None, 0, None) == OK              # M == 0: no-op
+    assert g(xs, 1, arr, ys, 2, ws, 1, None) == SMALL              # workspace too small
+    assert g(xs, 1, arr, ys, 2, ws + 16, 1 << 30, None) == INVALID  # misaligned workspace
+    bad_x = (ctypes.c_void_p * 2)(1 << 41, (1 << 41) + 2)
+    assert g(bad_x, 1, arr, ys, 2, ws, 1 << 30, None) == INVALID   # misaligned second x
+    arr_bad = _group_arrays([_fake_weight(), _fake_weight(K=100)])
+    assert g(xs, 1, arr_bad, ys, 2, ws, 1 << 30, None) == SHAPE    # bad second shape
+
+
+def test_group_workspace_sizes(lib):
+    ws_list = [_fake_weight(N=4096, K=4096), _fake_weight(N=1024, K=4096), _fake_weight(N=8192, K=14336)]
+    arr = _group_arrays(ws_list)
+    singles = [lib.msq_gemm_workspace_bytes(1, w.N, w.K) for w in ws_list]
+    # M == 1: every matrix keeps its own workspace, each rounded up to 256 bytes
+    assert lib.msq_gemm_group_workspace_bytes(1, arr, 3) >= sum(singles)
+    assert lib.msq_gemm_group_workspace_bytes(1, arr, 3) <= sum(singles) + 3 * 256
+    # larger M: the matrices run one after the other, so the largest one suffices
+    big = [lib.msq_gemm_workspace_bytes(2048, w.N, w.K) for w in ws_list]
+    assert lib.msq_gemm_group_workspace_bytes(2048, arr, 3) == max(big)
+    assert lib.msq_gemm_group_workspace_bytes(0, arr, 3) == 0
+    assert lib.msq_gemm_group_workspace_bytes(1, arr, 0) == 0
+    assert lib.msq_gemm_group_workspace_bytes(1, arr, 9) == 0

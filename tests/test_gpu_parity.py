@@ -264,3 +264,50 @@ def test_graph_replay_matches_eager(msq):
             assert torch.equal(y, y_eager), f"replay {rep} differs at M={M}"
             msq.gemm(other, pw, workspace=ws)  # eager work between replays, same workspace
             torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def group_cases(msq):
+    """Four matrices of different shapes and bit mixes for the grouped call; the
+    first three share K (one activation, as q, k, v of a layer do)."""
+    out = []
+    for N, K, seed, dist in ((512, 4096, 60, SMALL_DIST), (128, 4096, 61, {2: .7, 3: .3}),
+                             (256, 4096, 62, {8: .5, 1: .5}), (192, 1024, 63, SMALL_DIST)):
+        c = synth.random_case(N, K, seed, dist=dist)
+        out.append((c,) + check_pack(msq, c))
+    return out
+
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_group_matches_single_calls(msq, group_cases, monkeypatch, M):
+    """Each output of the grouped call equals the single call bit for bit (the same
+    kernels, launch plan and summation order) and the oracle within tolerance; at
+    M == 1 with several K splits (the shapes here force them) as well."""
+    monkeypatch.setenv("MSQ_GEMV_SPLIT", "3")
+    pws = [pw for _, pw, _ in group_cases]
+    x_shared = group_cases[0][0].x(M)
+    xs = [x_shared, x_shared, x_shared, group_cases[3][0].x(M)]
+    _log(f"group of {len(pws)} M={M}")
+    for rep in range(2):  # twice: the split counters start from zero every call
+        outs = msq.gemm_group(xs, pws)
+        torch.cuda.synchronize()
+        for (c, pw, ref), x, y in zip(group_cases, xs, outs):
+            single = msq.gemm(x, pw)
+            torch.cuda.synchronize()
+            assert torch.equal(y, single), c.name
+            check_y(msq, pw, c, ref, M, x=x)
+
+
+def test_group_sizes(msq, group_cases):
+    """One matrix, and the largest group: the same matrix eight times."""
+    c, pw, ref = group_cases[1]
+    x = c.x(1)
+    (y1,) = msq.gemm_group([x], [pw])
+    ys = msq.gemm_group([x] * msq.GROUP_MAX, [pw] * msq.GROUP_MAX)
+    single = msq.gemm(x, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, single)
+    for y in ys:
+        assert torch.equal(y, single)
+    with pytest.raises(ValueError):
+        msq.gemm_group([x] * (msq.GROUP_MAX + 1), [pw] * (msq.GROUP_MAX + 1))
