@@ -9,8 +9,11 @@ drawn i.i.d. from {0:5%, 1:10%, 2:60%, 3:15%, 4:8%, 8:2%} (labelled "about
 
 A step is one decode pass (M = 1) through all seven packed linears: the
 activation gather, on-the-fly dequantization, matrix-core product and row
-scatter of every linear, captured once per weight copy in a HIP graph and
-replayed.  The packed weights of the layer are cloned R times (R * packed >=
+scatter of every linear, issued as a decoder layer issues them (q, k, v on
+one activation in one grouped call, o, gate and up on one activation in one
+grouped call, down), captured once per weight copy in a HIP graph and
+replayed.  The same step as seven separate calls, each on its own
+activation, is reported beside it (decode_separate_calls).  The packed weights of the layer are cloned R times (R * packed >=
 1 GiB) and the copies are rotated step by step so that the 256 MB Infinity
 Cache cannot serve them.  value = effective weight GB/s = packed weight bytes
 (codes + scales/zero points + bit map/offsets) of the layer / step time.
@@ -52,6 +55,8 @@ PREFILL_M = 2048
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 WORKLOAD = "llama3-70b-layer"
+# grouped calls of one decoder layer's decode step (linears that read the same activation)
+LAYER_GROUPS = (("q_proj", "k_proj", "v_proj"), ("o_proj",), ("gate_proj", "up_proj"), ("down_proj",))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_m1_traffic.json")
 GEMV_SOURCES = ("block_wise_mixed_amd/csrc/msq_gemv.hip", "block_wise_mixed_amd/csrc/msq_dequant.h")
 
@@ -247,40 +252,68 @@ def main() -> int:
     wss = [torch.empty(max(msq.workspace_bytes(M, p.N, p.K), 256), dtype=torch.uint8, device=dev)
            for p in packed]
 
-    def decode_step(ws_copy):
+    # The layer's linears in the order and grouping a decoder layer calls them:
+    # q, k, v read one activation (one grouped call), then o, then gate, up read
+    # one activation (one grouped call), then down.
+    names = [m.name for m in wl.matrices]
+    layer_groups = [[names.index(n) for n in grp] for grp in LAYER_GROUPS]
+    gws = [torch.empty(max(msq.group_workspace_bytes(M, [packed[i] for i in grp]), 256),
+                       dtype=torch.uint8, device=dev) for grp in layer_groups]
+
+    def decode_step_grouped(ws_copy):
+        for grp, gw in zip(layer_groups, gws):
+            x = xs[grp[0]]  # the group's shared activation
+            if len(grp) == 1:
+                msq.gemm(x, ws_copy[grp[0]], out=ys[grp[0]], workspace=wss[grp[0]])
+            else:
+                msq.gemm_group([x] * len(grp), [ws_copy[i] for i in grp],
+                               outs=[ys[i] for i in grp], workspace=gw)
+
+    def decode_step_single(ws_copy):
         for i, p in enumerate(ws_copy):
             msq.gemm(xs[i], p, out=ys[i], workspace=wss[i])
 
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
+    def time_steps(step_fn):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for cp in copies:
+                step_fn(cp)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
         for cp in copies:
-            decode_step(cp)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graphs = []
-    for cp in copies:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            decode_step(cp)
-        graphs.append(g)
-    torch.cuda.synchronize()
-    for s in range(args.warmup):
-        graphs[s % R].replay()
-    torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step_fn(cp)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for s in range(args.warmup):
+            graphs[s % R].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for s in range(args.steps):
+            graphs[s % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = e0.elapsed_time(e1) / args.steps
+        del graphs
+        return ms, wall
+
+    ms_single, _ = time_steps(decode_step_single)
+    log(f"decode step, seven separate calls: {ms_single * 1e3:.1f} us")
+    ms_per_step, t_wall = time_steps(decode_step_grouped)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    e0.record()
-    for s in range(args.steps):
-        graphs[s % R].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_per_step = e0.elapsed_time(e1) / args.steps
     step_decode_bytes = sum(decode_bytes(p, M) for p in packed)
     value = layer_packed / (ms_per_step * 1e-3) / 1e9
     hbm_frac = step_decode_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS
     log(f"decode step {ms_per_step * 1e3:.1f} us, {value:.1f} GB/s effective, {hbm_frac:.3f} of HBM")
+    decode_single = {"ms_per_step": round(ms_single, 5),
+                     "value": round(layer_packed / (ms_single * 1e-3) / 1e9, 2),
+                     "note": "the seven linears as seven msq_gemm calls, each with its own activation"}
 
     # ---- roofline leg: decode kernel on gate_proj, rotating copies --------------------
     gi = [m.name for m in wl.matrices].index("gate_proj")
@@ -315,7 +348,7 @@ def main() -> int:
     prefill = None
     if not args.no_prefill:
         Mp = PREFILL_M
-        del graphs, g_roof
+        del g_roof
         xp = [torch.from_numpy(mi.x(Mp).view(np.int16)).view(torch.bfloat16).to(dev) for mi in inputs]
         yp = [torch.empty((Mp, p.N), dtype=torch.float32, device=dev) for p in packed]
         wsp = [torch.empty(max(msq.workspace_bytes(Mp, p.N, p.K), 256), dtype=torch.uint8,
@@ -360,6 +393,7 @@ def main() -> int:
                    "decode_bytes": step_decode_bytes, "weight_copies": R,
                    "timing": "HIP graph per weight copy, events around the timed replays"},
         "hbm_frac": round(hbm_frac, 4),
+        "decode_separate_calls": decode_single,
         "prefill": prefill,
         "pack": pack,
         "roofline": roofline,
