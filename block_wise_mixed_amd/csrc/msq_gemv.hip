@@ -878,9 +878,11 @@ int env_int(const char* name, int dflt) {
 // wavefronts (two per CU) and at most 8 splits.  M > 1: about 512
 // workgroups.  MSQ_GEMV_SPLIT and MSQ_GEMV_WAVES override the split count
 // and, for M == 1, the wavefronts per workgroup (tuning only).
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   GemvPlan p{};
   const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);
+  // the split heuristic counts the block rows of every matrix in the launch
+  const int rows = group_rows > 0 ? (int)(group_rows / kBlockRows) : NBr;
   p.mt = (int)((M + 15) / 16);
   p.nw = M > 16 ? 4 : 8;
   if (M == 1) {
@@ -898,7 +900,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   int split = env_int("MSQ_GEMV_SPLIT", 0);
   if (split <= 0) {
     if (M == 1) {
-      split = 512 / NBr;
+      split = 512 / rows;
       if (split > 8) split = 8;
     } else {
       split = (512 + NBr - 1) / NBr;
@@ -925,9 +927,17 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K) {
   return p;
 }
 
+// Rows of all matrices of a group: the launch the split heuristic fills.
+int64_t group_rows(const WeightView* w, int count) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += w[i].N;
+  return rows;
+}
+
 size_t gemv_group_workspace_m1(const WeightView* w, int count) {
   size_t total = 0;
-  for (int i = 0; i < count; ++i) total += align256(plan_gemv(1, w[i].N, w[i].K).workspace);
+  const int64_t rows = group_rows(w, count);
+  for (int i = 0; i < count; ++i) total += align256(plan_gemv(1, w[i].N, w[i].K, rows).workspace);
   return total;
 }
 
@@ -939,8 +949,9 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   int prep_total = 0, wg_total = 0, nw = 0;
   size_t lds = 0;
+  const int64_t rows = group_rows(w, count);
   for (int i = 0; i < count; ++i) {
-    const GemvPlan p = plan_gemv(1, w[i].N, w[i].K);
+    const GemvPlan p = plan_gemv(1, w[i].N, w[i].K, rows);
     if (nw == 0) nw = p.nw;
     if (p.nw != nw) return hipErrorInvalidValue;
     const GemvWorkspace gw = carve(ws, p, 1, w[i].N, w[i].K);

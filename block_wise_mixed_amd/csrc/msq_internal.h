@@ -43,7 +43,10 @@ struct GemvPlan {
   size_t lds_bytes; // dynamic LDS per workgroup
   size_t workspace; // bytes of fp32 partials (0 when split == 1)
 };
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K);
+// group_rows > 0: the plan of one matrix of a grouped launch whose matrices
+// have group_rows output rows in total (the K split then fills the GPU with
+// the whole group's workgroups).
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows = 0);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 

@@ -183,9 +183,12 @@ def test_group_workspace_sizes(lib):
     ws_list = [_fake_weight(N=4096, K=4096), _fake_weight(N=1024, K=4096), _fake_weight(N=8192, K=14336)]
     arr = _group_arrays(ws_list)
     singles = [lib.msq_gemm_workspace_bytes(1, w.N, w.K) for w in ws_list]
-    # M == 1: every matrix keeps its own workspace, each rounded up to 256 bytes
-    assert lib.msq_gemm_group_workspace_bytes(1, arr, 3) >= sum(singles)
-    assert lib.msq_gemm_group_workspace_bytes(1, arr, 3) <= sum(singles) + 3 * 256
+    # M == 1: every matrix keeps its own activation prep (reordered x, group sums,
+    # corrections) and partials; the group's K splits are no more than a single
+    # call's (the split count is planned for the whole launch)
+    prep = sum(2 * w.K + 84 * (w.K // 128) for w in ws_list)
+    g1 = lib.msq_gemm_group_workspace_bytes(1, arr, 3)
+    assert prep <= g1 <= sum(singles) + 3 * 256
     # larger M: the matrices run one after the other, so the largest one suffices
     big = [lib.msq_gemm_workspace_bytes(2048, w.N, w.K) for w in ws_list]
     assert lib.msq_gemm_group_workspace_bytes(2048, arr, 3) == max(big)
