@@ -311,3 +311,34 @@ def test_group_sizes(msq, group_cases):
         assert torch.equal(y, single)
     with pytest.raises(ValueError):
         msq.gemm_group([x] * (msq.GROUP_MAX + 1), [pw] * (msq.GROUP_MAX + 1))
+
+
+def test_group_graph_replay_matches_eager(msq, group_cases):
+    """bench.py captures grouped decode calls in HIP graphs: every replay, with eager
+    work in between on the same workspace, must equal the eager result bit for bit."""
+    pws = [pw for _, pw, _ in group_cases]
+    x_shared = torch.from_numpy(group_cases[0][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
+    x_last = torch.from_numpy(group_cases[3][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
+    xs = [x_shared, x_shared, x_shared, x_last]
+    ws = torch.empty(max(msq.group_workspace_bytes(1, pws), 256), dtype=torch.uint8, device="cuda")
+    eager = [y.clone() for y in msq.gemm_group(xs, pws)]
+    outs = [torch.empty_like(y) for y in eager]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        msq.gemm_group(xs, pws, outs=outs, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        msq.gemm_group(xs, pws, outs=outs, workspace=ws)
+    others = [(-x).contiguous() for x in xs]
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, eager):
+            assert torch.equal(o, e), f"replay {rep} differs"
+        msq.gemm_group(others, pws, workspace=ws)  # eager work between replays
+        torch.cuda.synchronize()
