@@ -19,8 +19,10 @@ Cache cannot serve them.  value = effective weight GB/s = packed weight bytes
 (codes + scales/zero points + bit map/offsets) of the layer / step time.
 
 Also reported, each timed in its own leg of the same run:
-  prefill : M = 2048 through all seven linears, TFLOP/s and fraction of the
-            2.5 PFLOP/s dense bf16 matrix-core peak;
+  prefill : M = 2048 through all seven linears, grouped as the decode step is
+            (q/k/v and gate/up each one gather and one GEMM launch), TFLOP/s
+            and fraction of the 2.5 PFLOP/s dense bf16 matrix-core peak; the
+            same as seven separate calls beside it;
   pack    : quantize-pack throughput over the seven matrices;
   roofline: the decode kernel on the largest linear (gate_proj), bytes per
             launch / average launch time, against 8 TB/s;
@@ -353,24 +355,42 @@ def main() -> int:
         yp = [torch.empty((Mp, p.N), dtype=torch.float32, device=dev) for p in packed]
         wsp = [torch.empty(max(msq.workspace_bytes(Mp, p.N, p.K), 256), dtype=torch.uint8,
                            device=dev) for p in packed]
-        for i, p in enumerate(packed):
-            msq.gemm(xp[i], p, out=yp[i], workspace=wsp[i])
-        torch.cuda.synchronize()
-        e0.record()
-        for s in range(args.prefill_steps):
-            cp = copies[s % R]
+        gwsp = [torch.empty(max(msq.group_workspace_bytes(Mp, [packed[i] for i in grp]), 256),
+                            dtype=torch.uint8, device=dev) for grp in layer_groups]
+
+        def prefill_grouped(cp):
+            # q, k, v (and gate, up) in one gather and one GEMM launch each
+            for grp, gw in zip(layer_groups, gwsp):
+                x = xp[grp[0]]
+                msq.gemm_group([x] * len(grp), [cp[i] for i in grp],
+                               outs=[yp[i] for i in grp], workspace=gw)
+
+        def prefill_single(cp):
             for i, p in enumerate(cp):
                 msq.gemm(xp[i], p, out=yp[i], workspace=wsp[i])
-        e1.record()
-        torch.cuda.synchronize()
-        ms_p = e0.elapsed_time(e1) / args.prefill_steps
+
+        def time_prefill(step_fn):
+            step_fn(packed)
+            torch.cuda.synchronize()
+            e0.record()
+            for s in range(args.prefill_steps):
+                step_fn(copies[s % R])
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / args.prefill_steps
+
+        ms_single = time_prefill(prefill_single)
+        ms_p = time_prefill(prefill_grouped)
         flops = sum(prefill_flops(p, Mp) for p in packed)
         tflops = flops / (ms_p * 1e-3) / 1e12
         prefill = {"M": Mp, "ms_per_step": round(ms_p, 4), "tflops": round(tflops, 2),
                    "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                   "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "flops_per_step": flops}
-        log(f"prefill M={Mp}: {ms_p:.3f} ms/step, {tflops:.1f} TFLOP/s")
-        del xp, yp, wsp
+                   "peak_tflops": MFMA_BF16_PEAK_TFLOPS, "flops_per_step": flops,
+                   "grouping": "q/k/v and gate/up grouped as in the decode step",
+                   "ms_per_step_separate_calls": round(ms_single, 4)}
+        log(f"prefill M={Mp}: {ms_p:.3f} ms/step grouped, {tflops:.1f} TFLOP/s "
+            f"({ms_single:.3f} ms/step as separate calls)")
+        del xp, yp, wsp, gwsp
 
     pack = {"ms": round(pack_ms, 3), "weight_bytes": w_bytes,
             "gbps_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1),

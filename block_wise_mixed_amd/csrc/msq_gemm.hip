@@ -17,6 +17,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <utility>
 
 #include "msq_dequant.h"
@@ -52,12 +53,11 @@ __device__ __forceinline__ uint16_t bf16_rn(float v) {
 
 __host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31) & ~(int64_t)31; }
 
-__global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __restrict__ x,
-                                                             int64_t K, int64_t M,
-                                                             const int32_t* __restrict__ perm_col,
-                                                             uint16_t* __restrict__ xr,
-                                                             uint16_t* __restrict__ sxs, int staged) {
-  const int64_t m = blockIdx.x;
+// Row m of one matrix's gather.
+__device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64_t K, int64_t M,
+                                           const int32_t* __restrict__ perm_col,
+                                           uint16_t* __restrict__ xr, uint16_t* __restrict__ sxs,
+                                           int staged, int64_t m) {
   const int64_t chunks = K / 8;
   const int64_t Gp = padded_groups(K / kBlockCols);
   const uint16_t* xrow = x + m * K;
@@ -104,6 +104,14 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
       dst[2 * plane] = t2;
     }
   }
+}
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __restrict__ x,
+                                                             int64_t K, int64_t M,
+                                                             const int32_t* __restrict__ perm_col,
+                                                             uint16_t* __restrict__ xr,
+                                                             uint16_t* __restrict__ sxs, int staged) {
+  gather_row(x, K, M, perm_col, xr, sxs, staged, blockIdx.x);
 }
 
 // ---- GEMM ------------------------------------------------------------------------------
@@ -262,9 +270,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
-    const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
-    float* __restrict__ y) {
+// Tile (mtile, ntile) of one matrix: rows kBM mtile .., block rows kBR ntile ..
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
+                                          const uint16_t* __restrict__ sxs, int M,
+                                          const WeightView& w, float* __restrict__ y, int mtile,
+                                          int ntile) {
   __shared__ __align__(16) uint4 a0[kBM * 16], a1[kBM * 16];
   __shared__ __align__(16) uint4 c0s[kBR * 8 * 64], c1s[kBR * 8 * 64];
   __shared__ uint32_t toff[kBR][kTabG];
@@ -273,8 +283,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // wavefront (wm, wn): rows 64 wm .. 64 wm + 63 of the tile, block row rb + wn
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.x * kBM;
-  const int rb = blockIdx.y * kBR;  // first block row of the workgroup
+  const int64_t m0 = (int64_t)mtile * kBM;
+  const int rb = ntile * kBR;  // first block row of the workgroup
   const int r = rb + wn;            // this wavefront's block row
   const int64_t K = w.K;
   const int G = w.NBc;
@@ -497,12 +507,114 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 }
 
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
+    const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
+    float* __restrict__ y) {
+  gemm_tile(xr, sxs, M, w, y, blockIdx.x, blockIdx.y);
+}
+
+// ---- grouped calls: up to kGroupMax matrices at the same M -------------------------------
+// One gather launch and one GEMM launch cover all matrices of the group (for
+// example q, k, v of a layer); the tiles of job j follow those of job j - 1,
+// so the tiles of small matrices fill the CUs that a large one leaves idle in
+// its last round.
+constexpr int kGroupMax = 8;
+
+struct GemmJob {
+  WeightView w;
+  const uint16_t* x;
+  uint16_t* xr;
+  uint16_t* sxs;
+  float* y;
+  int staged;      // gather: x row staged in LDS
+  int mtiles;      // tiles along M
+  int tile_begin;  // first tile of the job in the GEMM launch
+};
+
+struct GemmGroup {
+  GemmJob job[kGroupMax];
+  int count;
+  int M;
+};
+
+// Copy of the job owning tile (or gather row) b, selected with static indices.
+__device__ __forceinline__ GemmJob pick_gemm_job(const GemmGroup& g, int b, bool gather) {
+  GemmJob q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.count && b >= (gather ? k * g.M : g.job[k].tile_begin)) q = g.job[k];
+  return q;
+}
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) {
+  const GemmJob q = pick_gemm_job(g, blockIdx.x, true);
+  gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, q.staged, blockIdx.x % g.M);
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
+    GemmGroup g) {
+  const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
+  const int t = blockIdx.x - q.tile_begin;
+  gemm_tile(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles);
+}
+
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t M, int64_t K) {
   const size_t xr = (size_t)M * K * 2;
   const size_t xr_al = (xr + 255) & ~(size_t)255;
   return xr_al + 3 * (size_t)M * (size_t)padded_groups(K / kBlockCols) * 2;
+}
+
+size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count) {
+  size_t total = 0;
+  for (int i = 0; i < count; ++i) total += (gemm_workspace_bytes(M, w[i].K) + 255) & ~(size_t)255;
+  return total;
+}
+
+hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightView* w,
+                             float* const* y, int count, void* workspace, hipStream_t stream) {
+  if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+  GemmGroup g{};
+  g.count = count;
+  g.M = (int)M;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  size_t lds = 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i)
+    tiles += (M + kBM - 1) / kBM * ((w[i].NBr + kBR - 1) / kBR);
+  if (tiles > 0x7FFFFFFF || M * count > 0x7FFFFFFF) {
+    // beyond one launch's grid: each matrix on its own, in its own workspace
+    for (int i = 0; i < count; ++i) {
+      const hipError_t e = launch_gemm(x[i], M, w[i], y[i], ws, stream);
+      if (e != hipSuccess) return e;
+      ws += (gemm_workspace_bytes(M, w[i].K) + 255) & ~(size_t)255;
+    }
+    return hipSuccess;
+  }
+  tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    GemmJob& q = g.job[i];
+    const int64_t K = w[i].K;
+    q.w = w[i];
+    q.x = x[i];
+    q.xr = reinterpret_cast<uint16_t*>(ws);
+    const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
+    q.sxs = reinterpret_cast<uint16_t*>(ws + xr_bytes);
+    ws += (gemm_workspace_bytes(M, K) + 255) & ~(size_t)255;
+    q.y = y[i];
+    q.staged = (size_t)K * 2 <= kGatherMaxLds;
+    if (q.staged) lds = std::max(lds, (size_t)K * 2);
+    q.mtiles = (int)((M + kBM - 1) / kBM);
+    q.tile_begin = (int)tiles;
+    tiles += (int64_t)q.mtiles * ((w[i].NBr + kBR - 1) / kBR);
+  }
+  hipLaunchKernelGGL(k_gather_x_group, dim3((unsigned)(M * count)), dim3(kGatherThreads), lds,
+                     stream, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemm_group, dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,

@@ -189,8 +189,11 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight* const* w, int
     const size_t one = msq_gemm_workspace_bytes(M, w[i]->N, w[i]->K);
     most = one > most ? one : most;
   }
-  // M == 1: every matrix keeps its own workspace during the one launch
-  return M == 1 ? msq::gemv_group_workspace_m1(v, count) : most;
+  // M == 1 and M > 64: every matrix keeps its own workspace during the one
+  // launch; 2 .. 64: the matrices run one after the other
+  if (M == 1) return msq::gemv_group_workspace_m1(v, count);
+  if (M > MSQ_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count);
+  return most;
 }
 
 msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
@@ -206,7 +209,8 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
   }
   if (M < 0) return MSQ_ERR_SHAPE;
   if (M == 0) return MSQ_OK;
-  if (M != 1) {
+  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
+  if (M != 1 && M <= MSQ_GEMV_MAX_M) {
     // one matrix after the other, sharing the workspace (ordered on stream)
     for (int i = 0; i < count; ++i) {
       const msq_status st = msq_gemm(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, stream);
@@ -219,9 +223,9 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
   if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
   msq::WeightView v[MSQ_GROUP_MAX];
   for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
-  return msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream) == hipSuccess
-             ? MSQ_OK
-             : MSQ_ERR_HIP;
+  const hipError_t e = M == 1 ? msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream)
+                              : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
+  return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
 const char* msq_status_string(msq_status s) {

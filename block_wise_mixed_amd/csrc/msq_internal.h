@@ -61,5 +61,10 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
 size_t gemm_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, hipStream_t stream);
+// Grouped prefill of count (1 .. 8) matrices at one M: one gather and one GEMM
+// launch; the workspace holds each matrix's single-call workspace in turn.
+size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count);
+hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightView* w,
+                             float* const* y, int count, void* workspace, hipStream_t stream);
 
 }  // namespace msq

@@ -196,9 +196,10 @@ msq_status msq_gemm_ex(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
 #define MSQ_GROUP_MAX 8
 
 /* Bytes of device workspace msq_gemm_group needs for these count matrices
- * at M rows (M == 1: the sum of the single-call workspaces, since all
- * matrices are in flight together; otherwise their maximum).  Zero for
- * M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad shape. */
+ * at M rows (M == 1 and M > 64: about the sum of the single-call
+ * workspaces, since all matrices are in flight together; 2 .. 64 their
+ * maximum).  Zero for M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad
+ * shape. */
 size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int count);
 
 /* y[i] = x[i] . W_i^T for count matrices (1 .. MSQ_GROUP_MAX), each exactly
@@ -206,8 +207,11 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int
  * projections (and gate, up) read the same activation: at M == 1 one
  * activation-prep launch and one decode launch cover all matrices, their
  * workgroups running side by side ("TileQuant" abstract: local accumulation
- * to reduce memory traffic; the grouping itself is this library's).  Other
- * M: the matrices are computed one after the other as by msq_gemm.  x,
+ * to reduce memory traffic; the grouping itself is this library's).  At
+ * M > 64 (prefill) one activation-gather launch and one GEMM launch cover
+ * all matrices, the tiles of the smaller ones filling the compute units the
+ * larger ones leave idle.  M in 2 .. 64: the matrices are computed one after
+ * the other as by msq_gemm.  x,
  * w and y are host arrays of count device pointers / descriptors; x[i] may
  * repeat the same activation.  workspace must hold
  * msq_gemm_group_workspace_bytes(M, w, count) bytes (256-byte aligned).

@@ -189,9 +189,14 @@ def test_group_workspace_sizes(lib):
     prep = sum(2 * w.K + 84 * (w.K // 128) for w in ws_list)
     g1 = lib.msq_gemm_group_workspace_bytes(1, arr, 3)
     assert prep <= g1 <= sum(singles) + 3 * 256
-    # larger M: the matrices run one after the other, so the largest one suffices
+    # M in 2 .. 64: the matrices run one after the other, so the largest one suffices
+    mid = [lib.msq_gemm_workspace_bytes(16, w.N, w.K) for w in ws_list]
+    assert lib.msq_gemm_group_workspace_bytes(16, arr, 3) == max(mid)
+    # prefill: one launch for all, each matrix with its own gathered activation
     big = [lib.msq_gemm_workspace_bytes(2048, w.N, w.K) for w in ws_list]
-    assert lib.msq_gemm_group_workspace_bytes(2048, arr, 3) == max(big)
+    g = lib.msq_gemm_group_workspace_bytes(2048, arr, 3)
+    assert sum(big) <= g <= sum(big) + 3 * 256
+    assert g >= sum(2048 * w.K * 2 for w in ws_list)
     assert lib.msq_gemm_group_workspace_bytes(0, arr, 3) == 0
     assert lib.msq_gemm_group_workspace_bytes(1, arr, 0) == 0
     assert lib.msq_gemm_group_workspace_bytes(1, arr, 9) == 0

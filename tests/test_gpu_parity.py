@@ -278,11 +278,12 @@ def group_cases(msq):
     return out
 
 
-@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("M", [1, 3, 200])
 def test_group_matches_single_calls(msq, group_cases, monkeypatch, M):
     """Each output of the grouped call equals the single call bit for bit (the same
     kernels, launch plan and summation order) and the oracle within tolerance; at
-    M == 1 with several K splits (the shapes here force them) as well."""
+    M == 1 with several K splits (the shapes here force them) as well, and at a
+    prefill M of two row tiles, the second ragged, with four matrices in one launch."""
     monkeypatch.setenv("MSQ_GEMV_SPLIT", "3")
     pws = [pw for _, pw, _ in group_cases]
     x_shared = group_cases[0][0].x(M)
@@ -298,10 +299,11 @@ def test_group_matches_single_calls(msq, group_cases, monkeypatch, M):
             check_y(msq, pw, c, ref, M, x=x)
 
 
-def test_group_sizes(msq, group_cases):
+@pytest.mark.parametrize("M", [1, 130])
+def test_group_sizes(msq, group_cases, M):
     """One matrix, and the largest group: the same matrix eight times."""
     c, pw, ref = group_cases[1]
-    x = c.x(1)
+    x = c.x(M)
     (y1,) = msq.gemm_group([x], [pw])
     ys = msq.gemm_group([x] * msq.GROUP_MAX, [pw] * msq.GROUP_MAX)
     single = msq.gemm(x, pw)
