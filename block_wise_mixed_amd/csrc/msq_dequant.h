@@ -25,6 +25,8 @@
 namespace msq {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+// LDS pointer type of the direct global-to-LDS copy builtin
+typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 typedef float f32x2v __attribute__((ext_vector_type(2)));

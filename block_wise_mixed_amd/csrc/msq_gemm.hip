@@ -152,7 +152,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 __host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 128.f; }
 

@@ -79,6 +79,8 @@ struct Ctx {
   uint32_t xsum_off;     // M == 1: LDS byte offset of xsum [kmax]
   uint32_t a_lane;       // M == 1: LDS byte offset of this lane's A operand in column 0
   uint32_t zero_off;     // M == 1: LDS byte offset of the zero area (A operand of dead lanes)
+  uint32_t s_off;        // M == 1: LDS byte offset of the range's scales [ncl][64] f32
+  uint32_t z_off;        // M == 1: LDS byte offset of the range's zero points [ncl][64] u8
 };
 
 // This lane's pointer into the first chunk of a run whose first block is at off_kib.
@@ -100,7 +102,9 @@ struct BlockRegs {
 // tell two issues of the same block apart (the register rings repeat a
 // run's last block past its end): merging such loads would tie the ring's
 // register sets together and add waits.
-template <int B>
+// With kScaleZero false (M == 1) only the codes are loaded: the workgroup
+// stages the scales and zero points of its range in LDS at start-up.
+template <int B, bool kScaleZero = true>
 __device__ __forceinline__ void issue_block(const Ctx& cx, const uint8_t* base, int cl,
                                             BlockRegs<B>& br) {
   const int lane = threadIdx.x & 63;
@@ -109,8 +113,10 @@ __device__ __forceinline__ void issue_block(const Ctx& cx, const uint8_t* base, 
   const int64_t blk = cx.rowbase + cl;
 #pragma unroll
   for (int t = 0; t < B; ++t) br.ch[t] = *reinterpret_cast<const uint4*>(base + 1024 * t);
-  br.s = cx.scale[blk * kBlockRows + lane];
-  br.z = cx.zero[blk * kBlockRows + lane];
+  if constexpr (kScaleZero) {
+    br.s = cx.scale[blk * kBlockRows + lane];
+    br.z = cx.zero[blk * kBlockRows + lane];
+  }
 }
 
 // The wavefront's share of the range's blocks: per bitwidth k, the columns
@@ -511,7 +517,9 @@ __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockReg
   const float corr = *reinterpret_cast<const float*>(
       smem + cx.corr_off + __umul24((uint32_t)cl, 4u * kCorrStride) + 16 * kidx + 4 * (lane >> 4));
   const float xsum = *reinterpret_cast<const float*>(smem + cx.xsum_off + 4 * (uint32_t)cl);
-  y1 += br.s * ((v - corr) - (float)br.z * xsum);
+  const float sc = *reinterpret_cast<const float*>(smem + cx.s_off + ((uint32_t)cl << 8) + 4 * lane);
+  const uint32_t z = smem[cx.z_off + ((uint32_t)cl << 6) + lane];
+  y1 += sc * ((v - corr) - (float)z * xsum);
 }
 
 // Blocks per register ring of a B-bit run: (depth - 1) * B KiB of codes stay
@@ -552,10 +560,11 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
     }
     int bi = __builtin_amdgcn_readfirstlane(j < n ? j : n - 1);
     asm("" : "+s"(bi));
-    issue_block<B>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+    issue_block<B, false>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
     asm volatile("" ::: "memory");
   }
-  after_issue();  // the first run: the workgroup's start-up, while these loads fly
+  // the first run: the workgroup's start-up, while these D * B loads fly
+  after_issue(std::integral_constant<int, D * B>{});
   int i0 = 0;  // run index of the block in set 0
   do {
 #pragma unroll
@@ -568,22 +577,49 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
       }
       int bi = __builtin_amdgcn_readfirstlane(nx < n ? nx : n - 1);
       asm("" : "+s"(bi));
-      issue_block<B>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+      issue_block<B, false>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
       asm volatile("" ::: "memory");
     }
     i0 += D;
   } while (i0 < n);
 }
 
-// LDS layout of k_gemv_m1 for ranges of up to kmax block columns:
+// Direct global-to-LDS copies of 16 (4) bytes per lane: lane i writes at
+// LDS byte `off` (wavefront-uniform, from the dynamic LDS base) + 16 i (4 i).
+// Written as inline assembly because the compiler's builtin for them makes
+// it wait for each copy to land before the next instruction that reuses the
+// copy's address register, which serialises a run of copies; these have no
+// register results, and the kernel waits for them itself (vmcnt) before the
+// workgroup barrier that publishes the LDS data.  M0 carries the LDS address.
+__device__ __forceinline__ uint32_t lds_addr(uint32_t off) {
+  return (uint32_t)(uintptr_t)(lds_void*)(smem + off);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(const void* g, uint32_t off) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(off));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_copy4(const void* g, uint32_t off) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(off));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// LDS layout of k_gemv_m1 for ranges of ncl <= kmax block columns:
 //   [0, 256 kmax)             x slice, bf16
 //   [256 kmax, 336 kmax)      corr [kmax][20], f32
 //   [336 kmax, 340 kmax)      xsum [kmax], f32
 //   zero area of 256 bytes at the next 16-byte boundary
+//   scales [ncl][64] f32, then zero points [ncl][64] u8, of the range's blocks
 __host__ __device__ constexpr size_t m1_corr_offset(int kmax) { return (size_t)kmax * 256; }
 __host__ __device__ constexpr size_t m1_xsum_offset(int kmax) { return (size_t)kmax * 336; }
 __host__ __device__ constexpr size_t m1_zero_offset(int kmax) {
   return ((size_t)kmax * 340 + 15) & ~(size_t)15;
+}
+__host__ __device__ constexpr size_t m1_scale_offset(int kmax) { return m1_zero_offset(kmax) + 256; }
+__host__ __device__ constexpr size_t m1_lds_bytes(int kmax) {
+  return m1_scale_offset(kmax) + (size_t)kmax * (256 + 64);
 }
 
 // Workgroup `blk` (block row blk / split, K range blk % split) of the M == 1
@@ -599,6 +635,9 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   constexpr int kUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // x slice loads per thread
   constexpr int kCorr4 = kMaxCols * kCorrStride / 4;                 // float4s of the corr slice
   constexpr int kCorrUnits = (kCorr4 + kThreads - 1) / kThreads;
+  constexpr int kSUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // scale uint4s per thread
+  constexpr int kZUnits = (kMaxCols * 4 + kThreads - 1) / kThreads;   // zero-point uint4s
+  constexpr int kSumUnits = (kMaxCols + kThreads - 1) / kThreads;     // group sums
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -609,24 +648,10 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const size_t corr_off = m1_corr_offset(kmax), xsum_off = m1_xsum_offset(kmax);
   const uint32_t zero_off = (uint32_t)m1_zero_offset(kmax);
 
-  // One round trip, branch-free (clamped indices, results selected after):
-  // bit map and offsets (lane = column), then the range's slices of the
-  // reordered x, corrections and group sums.
+  // First round trip: bit map and offsets (lane = column).
   const int lc = min(lane, ncl - 1);
   const int blr = w.bits[rowbase + lc];
   const uint32_t ol = w.block_offset[rowbase + lc];
-  const uint4* xg4 = reinterpret_cast<const uint4*>(xg + (int64_t)c0 * kBlockCols);
-  uint4 xv[kUnits];
-#pragma unroll
-  for (int u = 0; u < kUnits; ++u) xv[u] = xg4[min(t + u * kThreads, ncl * 16 - 1)];
-  const float4* cg4 = reinterpret_cast<const float4*>(corr_g + (int64_t)c0 * kCorrStride);
-  float4 cv[kCorrUnits];
-#pragma unroll
-  for (int u = 0; u < kCorrUnits; ++u) cv[u] = cg4[min(t + u * kThreads, ncl * (kCorrStride / 4) - 1)];
-  const float sv = xsum_g[c0 + min(t, ncl - 1)];
-  // compiler-only barrier: issue all of the above now (the compiler would
-  // otherwise sink each load into the conditional LDS store that uses it)
-  asm volatile("" ::: "memory");
 
   const WaveRuns wr = wave_runs<NW>(lane < ncl ? blr : 0, wave, kWeightCostM1);
   uint32_t off[5];
@@ -634,33 +659,60 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   for (int k = 0; k < 5; ++k)
     off[k] = wr.n[k] > 0 ? __builtin_amdgcn_readlane(ol, __builtin_ctzll(wr.cols[k])) : 0u;
 
+  // Then, copied straight into LDS (no registers; the start-up barrier waits
+  // for them), the range's slices of the reordered x, corrections, group
+  // sums, scales (16 uint4 per column) and zero points (4 per column),
+  // issued just before the first run's code loads so that they travel with
+  // them.
+  const size_t s_off = m1_scale_offset(kmax);
+  const size_t z_off = s_off + 256 * (size_t)ncl;  // the zero points follow the range's scales
+  // the bit map and offsets have landed (the plan above used them): an
+  // explicit vmcnt(0) here tells the compiler so, and it then has no reason
+  // to wait for the copies below when it reuses those registers
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  auto stage16 = [&](const void* g, size_t lds_off, int n, auto Units) __attribute__((always_inline)) {
+    constexpr int kU = decltype(Units)::value;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int idx = t + u * kThreads;
+      if (idx < n)  // lane i of the wavefront lands 16 i bytes past the wavefront's base
+        lds_copy16(reinterpret_cast<const uint4*>(g) + idx, (uint32_t)lds_off + 16 * (idx - lane));
+    }
+  };
+  stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
+  stage16(corr_g + (int64_t)c0 * kCorrStride, corr_off, ncl * (kCorrStride / 4),
+          std::integral_constant<int, kCorrUnits>{});
+  stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
+  stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
+#pragma unroll
+  for (int u = 0; u < kSumUnits; ++u) {
+    const int idx = t + u * kThreads;
+    if (idx < ncl) lds_copy4(xsum_g + c0 + idx, (uint32_t)xsum_off + 4 * (idx - lane));
+  }
+  asm volatile("" ::: "memory");
+
   Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
          (uint32_t)corr_off, (uint32_t)xsum_off, 0u, 0u};
   cx.a_lane = (uint32_t)(16 * (lane >> 4));
   cx.zero_off = zero_off;
+  cx.s_off = (uint32_t)s_off;
+  cx.z_off = (uint32_t)z_off;
 
-  // Start-up: the slices go to LDS now; the workgroup barrier (waiting for
-  // this wavefront's LDS stores only) runs after the wavefront has issued
-  // the loads of its first run's first blocks, so their latency overlaps it.
-#pragma unroll
-  for (int u = 0; u < kUnits; ++u) {
-    const int idx = t + u * kThreads;
-    if (idx < ncl * 16) reinterpret_cast<uint4*>(smem)[idx] = xv[u];
-  }
-#pragma unroll
-  for (int u = 0; u < kCorrUnits; ++u) {
-    const int idx = t + u * kThreads;
-    if (idx < ncl * (kCorrStride / 4)) reinterpret_cast<float4*>(smem + corr_off)[idx] = cv[u];
-  }
-  if (t < ncl) reinterpret_cast<float*>(smem + xsum_off)[t] = sv;
+  // Start-up: the workgroup barrier runs after the wavefront has issued the
+  // loads of its first run's first blocks, so their latency overlaps it.  It
+  // waits for this wavefront's copies into LDS (every load but the last
+  // `issued`, which are that run's) and for its LDS stores.
   if (t < 64) reinterpret_cast<uint32_t*>(smem + zero_off)[t] = 0u;
   asm volatile("" ::: "memory");
-  auto startup = []() __attribute__((always_inline)) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  auto startup = [](auto Issued) __attribute__((always_inline)) {
+    constexpr int n = decltype(Issued)::value;
+    static_assert(n < 64, "vmcnt range");
+    // s_waitcnt vmcnt(n) expcnt(7) lgkmcnt(0); vmcnt is bits [3:0] and [15:14]
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  auto none = []() __attribute__((always_inline)) {};
+  auto none = [](auto) __attribute__((always_inline)) {};
 
   // runs of bitwidths 1, 2, 3, 4, 8 in order; the first non-empty one hosts the start-up
   float y1 = 0.f;
@@ -671,7 +723,7 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
     case 2: run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, startup); break;
     case 3: run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1, startup); break;
     case 4: run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1, startup); break;
-    default: startup(); break;
+    default: startup(std::integral_constant<int, 0>{}); break;
   }
   if (kfirst < 1 && wr.n[1] > 0) run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1, none);
   if (kfirst < 2 && wr.n[2] > 0) run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, none);
@@ -916,7 +968,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   size_t x_bytes;
   if (M == 1) {
     p.xs_stride = kr * kBlockCols;
-    x_bytes = m1_zero_offset(kr) + 256;
+    x_bytes = m1_lds_bytes(kr);
   } else {
     p.xs_stride = kr * kBlockCols + 8;  // +16 bytes per row against LDS bank conflicts
     x_bytes = (size_t)M * p.xs_stride * 2 + (size_t)M * kr * 4;
