@@ -18,6 +18,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <utility>
 
 #include "msq_dequant.h"
@@ -146,11 +147,23 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 // swizzle keeps the fragment reads free of bank conflicts).  0-bit blocks
 // skip the copies and the products.  y is scattered to original rows
 // through perm_row.
+//
+// Two tile shapes share this code (template parameter BR, block rows per
+// workgroup): BR = 4 as above; BR = 2, four wavefronts, with ONE x_r buffer:
+// every wavefront reads its A fragments of group c into registers first, a
+// barrier, then the copies of group c + 1 go into that same buffer (and the
+// other code buffer) while the products of group c run, and a second barrier
+// ends the group.  Its LDS (69 KiB) lets two workgroups share a CU, so one
+// workgroup's barrier waits and fragment-read bursts overlap the other's
+// products.
 constexpr int kBM = 128;
-constexpr int kBR = 4;
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
 constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
+template <int BR>
+struct TileCfg {
+  static constexpr int kWaves = 2 * BR;
+  static constexpr int kThreads = kWaves * 64;
+  static constexpr bool kSingleA = BR == 2;  // one x_r buffer, two barriers per group
+};
 
 
 __host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 128.f; }
@@ -158,7 +171,7 @@ __host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 1
 // One stage of the pipeline in LDS.
 struct Stage {
   uint4* a;      // x_r tile [kBM][16 chunks], swizzled
-  uint4* codes;  // [kBR][8 chunks][64 lanes]
+  uint4* codes;  // [BR][8 chunks][64 lanes]
 };
 
 // Chunk of a B-bit block holding (the low plane of) fragment F.
@@ -187,18 +200,21 @@ __device__ __forceinline__ bf16x8 b_lo(const uint4& c, const uint4& c2) {
 // basic block, so the scheduler interleaves them).  apk[kt] = this lane's
 // byte offset of its A fragment (m tile 0) for k-step kt; m tile mt is 4096
 // bytes further.
-template <int B>
-__device__ __forceinline__ void group_mfma(const Stage& st, int q, const uint32_t (&apk)[4],
-                                           const float (&sc)[4], f32x4 (&acc)[4][4]) {
-  const int lane = threadIdx.x & 63;
-  const uint4* cb = st.codes + q * 8 * 64 + lane;
+__device__ __forceinline__ void read_a(const Stage& st, const uint32_t (&apk)[4],
+                                       bf16x8 (&A)[4][4]) {
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(st.a);
-  bf16x8 A[4][4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
       A[kt][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(abase + apk[kt] + 4096 * mt));
+}
+
+template <int B>
+__device__ __forceinline__ void group_mfma(const Stage& st, int q, const bf16x8 (&A)[4][4],
+                                           const float (&sc)[4], f32x4 (&acc)[4][4]) {
+  const int lane = threadIdx.x & 63;
+  const uint4* cb = st.codes + q * 8 * 64 + lane;
   auto rstep = [&](auto RTc) __attribute__((always_inline)) {
     constexpr int rt = decltype(RTc)::value;
     constexpr int k0 = lo_chunk<B, 4 * rt>(), k1 = lo_chunk<B, 4 * rt + 3>();
@@ -257,7 +273,7 @@ __device__ __forceinline__ void load_scales(const WeightView& w, int r, int c, f
 // scales, zero points and S terms of the next batch are loaded while the
 // current one is built and multiplied.
 constexpr int kTermBytes = 4 * 64 * 16;  // one term of one block row: 4 row tiles x 1 KiB
-constexpr int kTUnits = kBR * 32 * 16 / kThreads;  // 4 rows per unit, units per thread
+constexpr int kTUnits = 4;  // units of 4 rows per thread: BR * 32 * 16 / (128 * BR)
 
 // Workgroup barrier that waits for the wavefront's LDS operations only (loads
 // from global memory stay in flight); the empty asm statements keep the
@@ -269,12 +285,17 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Tile (mtile, ntile) of one matrix: rows kBM mtile .., block rows kBR ntile ..
+// Tile (mtile, ntile) of one matrix: rows kBM mtile .., block rows BR ntile ..
+template <int BR>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                           const uint16_t* __restrict__ sxs, int M,
                                           const WeightView& w, float* __restrict__ y, int mtile,
                                           int ntile) {
-  __shared__ __align__(16) uint4 a0[kBM * 16], a1[kBM * 16];
+  constexpr int kBR = BR;
+  constexpr int kWaves = TileCfg<BR>::kWaves, kThreads = TileCfg<BR>::kThreads;
+  constexpr bool kSingleA = TileCfg<BR>::kSingleA;
+  static_assert(kTUnits * kThreads == kBR * 32 * 16, "T units per thread");
+  __shared__ __align__(16) uint4 a0[kBM * 16], a1[kSingleA ? 16 : kBM * 16];
   __shared__ __align__(16) uint4 c0s[kBR * 8 * 64], c1s[kBR * 8 * 64];
   __shared__ uint32_t toff[kBR][kTabG];
   __shared__ uint8_t tbits[kBR][kTabG];
@@ -288,7 +309,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   const int64_t K = w.K;
   const int G = w.NBc;
   const int tabG = min(G, kTabG);
-  const Stage st0{a0, c0s}, st1{a1, c1s};
+  const Stage st0{a0, c0s}, st1{kSingleA ? a0 : a1, c1s};
 
   // bitwidth and KiB offset of block (rb + q, c): LDS table, or global past it
   auto block_at = [&](int q, int c, uint32_t& off) __attribute__((always_inline)) -> int {
@@ -306,17 +327,19 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   };
 
   // Direct-to-LDS copies of group c into stage st: wavefront w copies rows
-  // 16w .. 16w+15 of the x_r tile (rows past M repeat row M - 1; their
-  // products are never stored), and wavefronts 2q, 2q + 1 alternate the code
-  // chunks of block q.
+  // kRows w .. kRows w + kRows - 1 of the x_r tile (rows past M repeat row
+  // M - 1; their products are never stored), and wavefronts 2q, 2q + 1
+  // alternate the code chunks of block q.
   auto copy_group = [&](const Stage& st, int c) __attribute__((always_inline)) {
+    constexpr int kRows = kBM / kWaves;
     const int g = lane >> 4, p = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * wave + 4 * i + g;
+    for (int i = 0; i < kRows / 4; ++i) {
+      const int row = kRows * wave + 4 * i + g;
       const int64_t mrow = min(m0 + row, (int64_t)M - 1);
       const uint16_t* src = xr + mrow * K + (int64_t)c * kBlockCols + 8 * (p ^ (row & 15));
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(st.a + (16 * wave + 4 * i) * 16), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(st.a + (kRows * wave + 4 * i) * 16), 16, 0,
+                                       0);
     }
     const int q = wave >> 1, half = wave & 1;
     uint32_t off;
@@ -355,18 +378,26 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // one group from stage st with the block's scales sc
-  auto compute = [&](const Stage& st, int c, const float (&sc)[4]) __attribute__((always_inline)) {
+  // one group from stage st (A fragments A) with the block's scales sc
+  auto products = [&](const Stage& st, int c, const bf16x8 (&A)[4][4], const float (&sc)[4])
+                      __attribute__((always_inline)) {
     uint32_t unused_off;
     const int b = block_at(wn, c, unused_off);
     switch (b) {
       case 0: break;
-      case 1: group_mfma<1>(st, wn, apk, sc, acc); break;
-      case 2: group_mfma<2>(st, wn, apk, sc, acc); break;
-      case 3: group_mfma<3>(st, wn, apk, sc, acc); break;
-      case 4: group_mfma<4>(st, wn, apk, sc, acc); break;
-      default: group_mfma<8>(st, wn, apk, sc, acc); break;
+      case 1: group_mfma<1>(st, wn, A, sc, acc); break;
+      case 2: group_mfma<2>(st, wn, A, sc, acc); break;
+      case 3: group_mfma<3>(st, wn, A, sc, acc); break;
+      case 4: group_mfma<4>(st, wn, A, sc, acc); break;
+      default: group_mfma<8>(st, wn, A, sc, acc); break;
     }
+  };
+  auto compute = [&](const Stage& st, int c, const float (&sc)[4]) __attribute__((always_inline)) {
+    uint32_t unused_off;
+    if (block_at(wn, c, unused_off) == 0) return;
+    bf16x8 A[4][4];
+    read_a(st, apk, A);
+    products(st, c, A, sc);
   };
   // own copies done, then the workgroup barrier (no memory fence: the copies
   // are the only producer and their completion is what is waited for)
@@ -382,6 +413,30 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   load_scales(w, r, 0, cur);
   stage_barrier();
 
+  if constexpr (kSingleA) {
+    // group c: A fragments from the one x_r buffer into registers, barrier,
+    // copies of group c + 1 (x_r into that buffer, codes into the other code
+    // buffer), products of group c, barrier
+    auto group = [&](const Stage& st, const Stage& nx, int c) __attribute__((always_inline)) {
+      uint32_t unused_off;
+      bf16x8 A[4][4];
+      if (block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
+      lds_barrier();
+      if (c + 1 < G) {
+        copy_group(nx, c + 1);
+        load_scales(w, r, c + 1, nxt);
+      }
+      products(st, c, A, cur);
+      stage_barrier();
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
+    };
+    for (int c = 0; c < G; c += 2) {
+      group(st0, st1, c);
+      if (c + 1 >= G) break;
+      group(st1, st0, c + 1);
+    }
+  } else
   for (int c = 0; c < G; c += 2) {
     // group c from stage 0, group c + 1 arriving in stage 1
     if (c + 1 < G) {
@@ -506,10 +561,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   }
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
+template <int BR>
+__global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
     float* __restrict__ y) {
-  gemm_tile(xr, sxs, M, w, y, blockIdx.x, blockIdx.y);
+  gemm_tile<BR>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y);
 }
 
 // ---- grouped calls: up to kGroupMax matrices at the same M -------------------------------
@@ -550,11 +606,22 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) 
   gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, q.staged, blockIdx.x % g.M);
 }
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
+template <int BR>
+__global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
     GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
   const int t = blockIdx.x - q.tile_begin;
-  gemm_tile(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles);
+  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles);
+}
+
+// Block rows per workgroup of the prefill GEMM (MSQ_GEMM_BR=2 or 4 overrides).
+int gemm_br() {
+  static const int br = [] {
+    const char* e = std::getenv("MSQ_GEMM_BR");
+    const int v = e ? std::atoi(e) : 0;
+    return v == 2 || v == 4 ? v : 2;
+  }();
+  return br;
 }
 
 }  // namespace
@@ -579,9 +646,10 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   g.M = (int)M;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   size_t lds = 0;
+  const int br = gemm_br();
   int64_t tiles = 0;
   for (int i = 0; i < count; ++i)
-    tiles += (M + kBM - 1) / kBM * ((w[i].NBr + kBR - 1) / kBR);
+    tiles += (M + kBM - 1) / kBM * ((w[i].NBr + br - 1) / br);
   if (tiles > 0x7FFFFFFF || M * count > 0x7FFFFFFF) {
     // beyond one launch's grid: each matrix on its own, in its own workspace
     for (int i = 0; i < count; ++i) {
@@ -606,13 +674,18 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
     if (q.staged) lds = std::max(lds, (size_t)K * 2);
     q.mtiles = (int)((M + kBM - 1) / kBM);
     q.tile_begin = (int)tiles;
-    tiles += (int64_t)q.mtiles * ((w[i].NBr + kBR - 1) / kBR);
+    tiles += (int64_t)q.mtiles * ((w[i].NBr + br - 1) / br);
   }
   hipLaunchKernelGGL(k_gather_x_group, dim3((unsigned)(M * count)), dim3(kGatherThreads), lds,
                      stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemm_group, dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
+  if (br == 2)
+    hipLaunchKernelGGL(k_gemm_group<2>, dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
+                       stream, g);
+  else
+    hipLaunchKernelGGL(k_gemm_group<4>, dim3((unsigned)tiles), dim3(TileCfg<4>::kThreads), 0,
+                       stream, g);
   return hipGetLastError();
 }
 
@@ -628,8 +701,14 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
                      stream, x, K, M, w.perm_col, xr, sxs, staged);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + kBR - 1) / kBR));
-  hipLaunchKernelGGL(k_gemm, grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y);
+  const int br = gemm_br();
+  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + br - 1) / br));
+  if (br == 2)
+    hipLaunchKernelGGL(k_gemm<2>, grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs, (int)M, w,
+                       y);
+  else
+    hipLaunchKernelGGL(k_gemm<4>, grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs, (int)M, w,
+                       y);
   return hipGetLastError();
 }
 
