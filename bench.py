@@ -27,7 +27,13 @@ Also reported, each timed in its own leg of the same run:
   roofline: the decode kernel on the largest linear (gate_proj), bytes per
             launch / average launch time, against 8 TB/s;
   cpu_baseline: the CPU oracle (numpy) decoding a bounded sample of block
-            rows of every linear, scaled to GB/s.
+            rows of every linear, scaled to GB/s;
+  configs : one record per (matrix, M) of the smaller workloads: Llama-3-8B
+            q_proj and MLP decodes at M = 1, 16, 64 (GB/s, fraction of HBM)
+            and the Llama-3-8B down_proj prefill at M = 512, 2048, 8192
+            (TFLOP/s, fraction of the matrix-core peak);
+  context : torch's dense bf16 GEMM (hipBLASLt) at prefill shapes and a 1 GiB
+            device copy, as what plain library code reaches on this GPU.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 
@@ -99,6 +105,123 @@ def prefill_flops(pw, M: int) -> int:
     return 2 * M * 64 * 128 * live
 
 
+def config_legs(msq, synth, torch, np, dev, log):
+    """Per-matrix lines of the smaller workloads: the Llama-3-8B q_proj and MLP
+    decodes (M = 1, 16, 64) and the Llama-3-8B down_proj prefill (M = 512, 2048,
+    8192).  Decodes rotate >= 1 GiB of weight copies inside one HIP graph per
+    (matrix, M); prefills run eagerly on two copies."""
+    out = []
+    for wname, Ms in (("llama3-8b-q_proj", (1,)), ("llama3-8b-mlp", (1, 16, 64)),
+                      ("llama3-8b-down_proj-prefill", (512, 2048, 8192))):
+        wl = synth.WORKLOADS[wname]
+        for mi_idx, m in enumerate(wl.matrices):
+            mi = synth.matrix_inputs(wname, mi_idx)
+            Wd = torch.from_numpy(mi.W.view(np.int16)).view(torch.bfloat16).to(dev)
+            pw = msq.quantize_pack(Wd, mi.bits, mi.perm_row, mi.perm_col)
+            del Wd
+            for M in Ms:
+                x = torch.from_numpy(mi.x(M).view(np.int16)).view(torch.bfloat16).to(dev)
+                y = torch.empty((M, pw.N), dtype=torch.float32, device=dev)
+                ws = torch.empty(max(msq.workspace_bytes(M, pw.N, pw.K), 256), dtype=torch.uint8,
+                                 device=dev)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                rec = {"workload": wname, "matrix": m.name, "N": m.N, "K": m.K, "M": M,
+                       "mean_bits": round(mi.mean_bits, 4)}
+                if M <= 64:
+                    R = max(2, min(256, int(np.ceil((1 << 30) / pw.packed_bytes))))
+                    cps = [pw] + [pw.clone() for _ in range(R - 1)]
+                    msq.gemm(x, pw, out=y, workspace=ws)
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g):
+                        for c in cps:
+                            msq.gemm(x, c, out=y, workspace=ws)
+                    g.replay()
+                    torch.cuda.synchronize()
+                    reps = 3
+                    e0.record()
+                    for _ in range(reps):
+                        g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / (reps * R)
+                    db = decode_bytes(pw, M)
+                    rec.update({"us_per_call": round(us, 3), "weight_copies": R,
+                                "gbps_effective": round(pw.packed_bytes / (us * 1e-6) / 1e9, 1),
+                                "hbm_frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
+                    del g, cps
+                else:
+                    cps = [pw, pw.clone()]
+                    msq.gemm(x, pw, out=y, workspace=ws)
+                    torch.cuda.synchronize()
+                    reps = 6
+                    e0.record()
+                    for k in range(reps):
+                        msq.gemm(x, cps[k % 2], out=y, workspace=ws)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / reps
+                    tf = prefill_flops(pw, M) / (us * 1e-6) / 1e12
+                    rec.update({"us_per_call": round(us, 1), "tflops": round(tf, 1),
+                                "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+                    del cps
+                log(f"{wname} {m.name} M={M}: " + ", ".join(f"{k}={v}" for k, v in rec.items()
+                                                             if k in ("us_per_call", "gbps_effective",
+                                                                      "hbm_frac", "tflops", "mfma_frac")))
+                out.append(rec)
+                del x, y, ws
+            del pw
+            torch.cuda.empty_cache()
+    return out
+
+
+def achievable_context(torch, dev, log):
+    """What plain library code reaches on the same GPU, as context for the
+    fractions (not a denominator): torch's dense bf16 GEMM (hipBLASLt) at the
+    prefill shapes, and a device-to-device copy of 1 GiB (read + write)."""
+    res = {}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    gemms = []
+    for name, M, N, K in (("llama3-8b down_proj", 2048, 4096, 14336),
+                          ("llama3-70b gate_proj", 2048, 28672, 8192),
+                          ("llama3-70b down_proj", 2048, 8192, 28672)):
+        a = torch.randn(M, K, device=dev).to(torch.bfloat16)
+        b = torch.randn(N, K, device=dev).to(torch.bfloat16)
+        c = torch.matmul(a, b.t())
+        torch.cuda.synchronize()
+        reps = 5
+        e0.record()
+        for _ in range(reps):
+            c = torch.matmul(a, b.t())
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        gemms.append({"shape": f"{name} M={M} N={N} K={K}", "us": round(us, 1), "tflops": round(tf, 1),
+                      "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        log(f"context: dense bf16 torch.matmul {name}: {tf:.0f} TFLOP/s")
+        del a, b, c
+    res["dense_bf16_gemm"] = gemms
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    res["device_copy_1GiB"] = {"us": round(us, 1), "gbps_read_plus_write": round(2 * n / (us * 1e-6) / 1e9, 1)}
+    log(f"context: device copy {2 * n / (us * 1e-6) / 1e9:.0f} GB/s read+write")
+    del src, dst
+    torch.cuda.empty_cache()
+    res["note"] = ("achievable context only; the fractions above use the published peaks "
+                   "(8 TB/s HBM, 2.5 PFLOP/s dense bf16)")
+    return res
+
+
 def cpu_baseline(inputs, target_s: float = 12.0):
     """The oracle decoding a sample of block rows of every linear (M = 1).
 
@@ -153,6 +276,8 @@ def main() -> int:
     ap.add_argument("--prefill-steps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-matrix lines of the smaller workloads and the context leg")
     ap.add_argument("--only-decode", default=None, metavar="NAME")
     ap.add_argument("--only-prefill", default=None, metavar="NAME")
     ap.add_argument("--calls", type=int, default=20)
@@ -396,6 +521,13 @@ def main() -> int:
             "gbps_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1),
             "note": "host-side descriptor validation included"}
 
+    configs, context = None, None
+    if not args.no_configs:
+        del copies
+        torch.cuda.empty_cache()
+        configs = config_legs(msq, synth, torch, np, dev, log)
+        context = achievable_context(torch, dev, log)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
@@ -418,6 +550,8 @@ def main() -> int:
         "pack": pack,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "configs": configs,
+        "context": context,
         "wall_s_timed": round(t_wall, 4),
     }
     print(json.dumps(out), flush=True)

@@ -52,7 +52,6 @@ __device__ __forceinline__ uint16_t bf16_rn(float v) {
   return (uint16_t)__builtin_bit_cast(uint32_t, h);
 }
 
-__host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31) & ~(int64_t)31; }
 
 // Row m of one matrix's gather.
 __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64_t K, int64_t M,
@@ -285,12 +284,16 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Tile (mtile, ntile) of one matrix: rows kBM mtile .., block rows BR ntile ..
+// Tile (mtile, ntile) of one matrix over groups g0 .. g1 - 1: rows kBM mtile
+// .., block rows BR ntile ...  part == nullptr: the tile holds all groups
+// and y is written (scattered through perm_row); otherwise the tile's share
+// of a K split goes to part[m][reordered row] (summed over the splits, in
+// split order, by the split-reduce kernel).
 template <int BR>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                           const uint16_t* __restrict__ sxs, int M,
                                           const WeightView& w, float* __restrict__ y, int mtile,
-                                          int ntile) {
+                                          int ntile, int g0, int g1, float* __restrict__ part) {
   constexpr int kBR = BR;
   constexpr int kWaves = TileCfg<BR>::kWaves, kThreads = TileCfg<BR>::kThreads;
   constexpr bool kSingleA = TileCfg<BR>::kSingleA;
@@ -308,18 +311,19 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   const int r = rb + wn;            // this wavefront's block row
   const int64_t K = w.K;
   const int G = w.NBc;
-  const int tabG = min(G, kTabG);
+  const int tabG = min(g1 - g0, kTabG);
   const Stage st0{a0, c0s}, st1{kSingleA ? a0 : a1, c1s};
 
-  // bitwidth and KiB offset of block (rb + q, c): LDS table, or global past it
+  // bitwidth and KiB offset of block (rb + q, c): LDS table (groups g0 ..
+  // g0 + kTabG - 1), or global past it
   auto block_at = [&](int q, int c, uint32_t& off) __attribute__((always_inline)) -> int {
     if (rb + q >= w.NBr) {
       off = 0;
       return 0;
     }
-    if (c < kTabG) {
-      off = __builtin_amdgcn_readfirstlane(toff[q][c]);
-      return __builtin_amdgcn_readfirstlane(tbits[q][c]);
+    if (c - g0 < kTabG) {
+      off = __builtin_amdgcn_readfirstlane(toff[q][c - g0]);
+      return __builtin_amdgcn_readfirstlane(tbits[q][c - g0]);
     }
     const int64_t blk = (int64_t)(rb + q) * w.NBc + c;
     off = __builtin_amdgcn_readfirstlane(w.block_offset[blk]);
@@ -352,11 +356,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                          (lds_void*)(st.codes + (q * 8 + t + half) * 64), 16, 0, 0);
   };
 
-  // the workgroup's bit map and offsets for the first tabG groups
+  // the workgroup's bit map and offsets for the first tabG groups of its range
   for (int i = tid; i < kBR * tabG; i += kThreads) {
     const int q = i / tabG, c = i - (i / tabG) * tabG;
     const int rr = rb + q;
-    const int64_t blk = (int64_t)(rr < w.NBr ? rr : 0) * w.NBc + c;
+    const int64_t blk = (int64_t)(rr < w.NBr ? rr : 0) * w.NBc + g0 + c;
     tbits[q][c] = rr < w.NBr ? w.bits[blk] : 0;
     toff[q][c] = rr < w.NBr ? w.block_offset[blk] : 0u;
   }
@@ -409,8 +413,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   };
 
   float cur[4], nxt[4];
-  copy_group(st0, 0);
-  load_scales(w, r, 0, cur);
+  copy_group(st0, g0);
+  load_scales(w, r, g0, cur);
   stage_barrier();
 
   if constexpr (kSingleA) {
@@ -422,7 +426,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       bf16x8 A[4][4];
       if (block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
       lds_barrier();
-      if (c + 1 < G) {
+      if (c + 1 < g1) {
         copy_group(nx, c + 1);
         load_scales(w, r, c + 1, nxt);
       }
@@ -431,25 +435,25 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
     };
-    for (int c = 0; c < G; c += 2) {
+    for (int c = g0; c < g1; c += 2) {
       group(st0, st1, c);
-      if (c + 1 >= G) break;
+      if (c + 1 >= g1) break;
       group(st1, st0, c + 1);
     }
   } else
-  for (int c = 0; c < G; c += 2) {
+  for (int c = g0; c < g1; c += 2) {
     // group c from stage 0, group c + 1 arriving in stage 1
-    if (c + 1 < G) {
+    if (c + 1 < g1) {
       copy_group(st1, c + 1);
       load_scales(w, r, c + 1, nxt);
     }
     compute(st0, c, cur);
     stage_barrier();
-    if (c + 1 >= G) break;
+    if (c + 1 >= g1) break;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
     // group c + 1 from stage 1, group c + 2 arriving in stage 0
-    if (c + 2 < G) {
+    if (c + 2 < g1) {
       copy_group(st0, c + 2);
       load_scales(w, r, c + 2, nxt);
     }
@@ -478,9 +482,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       const int q = u >> 9, gl = (u >> 4) & 31, n4 = 4 * (u & 15);
       const int64_t c = j0 + gl;
       const int rr = rb + q;
-      const bool live = rr < w.NBr && c < G;
+      const bool live = rr < w.NBr && c >= g0 && c < g1;
       const int64_t blk = live ? (int64_t)rr * w.NBc + c : 0;
-      lb[k] = !live ? 0 : (c < kTabG ? (int)tbits[q][c] : (int)w.bits[blk]);
+      lb[k] = !live ? 0 : (c - g0 < kTabG ? (int)tbits[q][c - g0] : (int)w.bits[blk]);
       ls[k] = *reinterpret_cast<const float4*>(w.scale + blk * kBlockRows + n4);
       lz[k] = *reinterpret_cast<const uint32_t*>(w.zero + blk * kBlockRows + n4);
     }
@@ -496,8 +500,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
         Sa[t][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(src + t * plane));
     }
   };
-  load_t(0);
-  for (int64_t j0 = 0; j0 < Gp; j0 += 32) {
+  // batches of 32 groups covering g0 .. g1 - 1 (T is zero outside the range)
+  const int64_t jb = g0 & ~31;
+  load_t(jb);
+  for (int64_t j0 = jb; j0 < g1; j0 += 32) {
     load_s(j0);
     lds_barrier();  // previous readers of the stage buffers are done
 #pragma unroll
@@ -521,7 +527,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
         *reinterpret_cast<uint16_t*>(tq(q) + 2 * kTermBytes + at) = t2;
       }
     }
-    if (j0 + 32 < Gp) load_t(j0 + 32);
+    if (j0 + 32 < g1) load_t(j0 + 32);
     lds_barrier();
     bf16x8 Tb[3][4];
 #pragma unroll
@@ -544,19 +550,20 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       }
   }
 
-  // epilogue: y[m][perm_row[n]]
+  // epilogue: y[m][perm_row[n]], or the split's partial part[m][n]
   if (r >= w.NBr) return;
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int64_t row = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
-    int col = w.perm_row[row];
+    int col = part ? (int)row : w.perm_row[row];
     col = min(max(col, 0), (int)w.N - 1);
+    float* out = part ? part : y;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 64 * wm + 16 * mt + 4 * (lane >> 4) + i;
-        if (m < M) y[m * w.N + col] = acc[mt][rt][i];
+        if (m < M) out[m * w.N + col] = acc[mt][rt][i];
       }
   }
 }
@@ -564,8 +571,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
 template <int BR>
 __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
-    float* __restrict__ y) {
-  gemm_tile<BR>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y);
+    float* __restrict__ y, float* __restrict__ part, int gper) {
+  // K split blockIdx.z: groups gper z .. ; partials plane z of part
+  const int g0 = blockIdx.z * gper, g1 = min(w.NBc, g0 + gper);
+  gemm_tile<BR>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
+                part ? part + (int64_t)blockIdx.z * M * w.N : nullptr);
 }
 
 // ---- grouped calls: up to kGroupMax matrices at the same M -------------------------------
@@ -611,7 +621,7 @@ __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_
     GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
   const int t = blockIdx.x - q.tile_begin;
-  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles);
+  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, nullptr);
 }
 
 // Block rows per workgroup of the prefill GEMM (MSQ_GEMM_BR=2 or 4 overrides).
@@ -624,9 +634,33 @@ int gemm_br() {
   return br;
 }
 
+// Launch shape of one GEMM call.  Fewer tiles than kFillTiles (two per CU)
+// split K into ranges of at least kMinSplitGroups groups (the correction
+// product works on batches of 32 groups, so shorter ranges waste it), the
+// ranges' partials summed by the split reduction.  MSQ_GEMM_SPLIT overrides
+// the split count.
+constexpr int64_t kFillTiles = 512;
+constexpr int64_t kMinSplitGroups = 8;
+struct GemmPlan {
+  int br, split, gper;
+};
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+  GemmPlan p{};
+  p.br = gemm_br();
+  const int64_t G = K / kBlockCols;
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N / kBlockRows + p.br - 1) / p.br);
+  const char* e = std::getenv("MSQ_GEMM_SPLIT");
+  int64_t split = e && *e ? std::atoi(e) : (tiles >= kFillTiles ? 1 : (kFillTiles + tiles - 1) / tiles);
+  split = std::min<int64_t>(split, std::max<int64_t>(1, G / kMinSplitGroups));
+  if (split < 1) split = 1;
+  p.gper = (int)((G + split - 1) / split);
+  p.split = (int)((G + p.gper - 1) / p.gper);
+  return p;
+}
+
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t M, int64_t K) {
+size_t gather_workspace_bytes(int64_t M, int64_t K) {
   const size_t xr = (size_t)M * K * 2;
   const size_t xr_al = (xr + 255) & ~(size_t)255;
   return xr_al + 3 * (size_t)M * (size_t)padded_groups(K / kBlockCols) * 2;
@@ -634,7 +668,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t K) {
 
 size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count) {
   size_t total = 0;
-  for (int i = 0; i < count; ++i) total += (gemm_workspace_bytes(M, w[i].K) + 255) & ~(size_t)255;
+  for (int i = 0; i < count; ++i)
+    total += (gemm_workspace_bytes(M, w[i].N, w[i].K) + 255) & ~(size_t)255;
   return total;
 }
 
@@ -650,12 +685,13 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   int64_t tiles = 0;
   for (int i = 0; i < count; ++i)
     tiles += (M + kBM - 1) / kBM * ((w[i].NBr + br - 1) / br);
-  if (tiles > 0x7FFFFFFF || M * count > 0x7FFFFFFF) {
-    // beyond one launch's grid: each matrix on its own, in its own workspace
+  if (tiles < kFillTiles || tiles > 0x7FFFFFFF || M * count > 0x7FFFFFFF) {
+    // too few tiles to fill the GPU (each call then splits K), or beyond one
+    // launch's grid: each matrix on its own, in its own workspace
     for (int i = 0; i < count; ++i) {
       const hipError_t e = launch_gemm(x[i], M, w[i], y[i], ws, stream);
       if (e != hipSuccess) return e;
-      ws += (gemm_workspace_bytes(M, w[i].K) + 255) & ~(size_t)255;
+      ws += (gemm_workspace_bytes(M, w[i].N, w[i].K) + 255) & ~(size_t)255;
     }
     return hipSuccess;
   }
@@ -668,7 +704,7 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
     q.xr = reinterpret_cast<uint16_t*>(ws);
     const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
     q.sxs = reinterpret_cast<uint16_t*>(ws + xr_bytes);
-    ws += (gemm_workspace_bytes(M, K) + 255) & ~(size_t)255;
+    ws += (gemm_workspace_bytes(M, w[i].N, K) + 255) & ~(size_t)255;
     q.y = y[i];
     q.staged = (size_t)K * 2 <= kGatherMaxLds;
     if (q.staged) lds = std::max(lds, (size_t)K * 2);
@@ -689,27 +725,49 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
-                       void* workspace, hipStream_t stream) {
+hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
+                           hipStream_t stream) {
   const int64_t K = w.K;
-  uint16_t* xr = reinterpret_cast<uint16_t*>(workspace);
+  uint16_t* xr = reinterpret_cast<uint16_t*>(ws);
   const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
-  uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + xr_bytes);
+  uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + xr_bytes);
   const size_t row_bytes = (size_t)K * 2;
   const int staged = row_bytes <= kGatherMaxLds;
   hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M), dim3(kGatherThreads), staged ? row_bytes : 0,
                      stream, x, K, M, w.perm_col, xr, sxs, staged);
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  const GemmPlan p = plan_gemm(M, N, K);
+  const size_t gather = (gather_workspace_bytes(M, K) + 255) & ~(size_t)255;
+  return gather + (p.split > 1 ? (size_t)p.split * M * N * 4 : 0);
+}
+
+hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
+                       void* workspace, hipStream_t stream) {
+  const int64_t K = w.K;
+  const GemmPlan p = plan_gemm(M, w.N, K);
+  uint16_t* xr = reinterpret_cast<uint16_t*>(workspace);
+  const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
+  uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + xr_bytes);
+  float* part = p.split > 1
+                    ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
+                                               ((gather_workspace_bytes(M, K) + 255) & ~(size_t)255))
+                    : nullptr;
+  hipError_t e = launch_gather_x(x, M, w, workspace, stream);
   if (e != hipSuccess) return e;
-  const int br = gemm_br();
-  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + br - 1) / br));
-  if (br == 2)
+  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + p.br - 1) / p.br),
+                  (unsigned)p.split);
+  if (p.br == 2)
     hipLaunchKernelGGL(k_gemm<2>, grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y);
+                       y, part, p.gper);
   else
     hipLaunchKernelGGL(k_gemm<4>, grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y);
-  return hipGetLastError();
+                       y, part, p.gper);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.split == 1) return e;
+  return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);
 }
 
 }  // namespace msq

@@ -10,9 +10,10 @@
 //     the blocks in packed order; the wavefronts cut that list into NW pieces
 //     of equal packed size, so each wavefront gets at most a few runs of
 //     same-bitwidth blocks.
-//  2. The activations, reordered through perm_col (the activation
-//     reordering of the "SFMP" abstract), are staged in LDS together with
-//     their per-group sums, used to fold the zero point.
+//  2. The activations, reordered through perm_col once per call by the
+//     gather kernel (the activation reordering of the "SFMP" abstract), are
+//     staged in LDS slice by slice together with their per-group sums, used
+//     to fold the zero point.
 //  3. Each wavefront walks its runs.  Inside a run the bitwidth is a
 //     compile-time constant, so the loads of the next blocks (codes, scales,
 //     zero points) are issued while the current block is unpacked and
@@ -26,9 +27,10 @@
 //     the last workgroup of the block row to finish; M > 1: by
 //     k_gemv_reduce), so results are bitwise reproducible.
 //
-// M == 1 has its own kernels (k_prep_m1 + k_gemv_m1): the activation gather
-// runs once per call instead of once per workgroup, the unpack avoids most
-// shifts, and each wavefront keeps 4 to 8 KiB of codes in flight.
+// M == 1 has its own kernels (k_prep_m1 + k_gemv_m1): the prep also forms
+// the per-bitwidth bias corrections, the unpack avoids most shifts, the
+// scales and zero points are staged in LDS, and each wavefront keeps 4 to
+// 8 KiB of codes in flight.
 //
 // Per-block precision and block layout: "ScaleBITS" summary page, section
 // Approach; RTN-g128 dequantization s * (q - z): section Limitations.
@@ -284,48 +286,44 @@ __device__ __forceinline__ void run_blocks(const Ctx& cx, const uint8_t* base, u
   }
 }
 
-// Gather x[m][perm_col[128*(c0+cl) + j]] into LDS xs[m][cl*128 + j] and the
-// per-group sums into xsum[m][cl].  Item = (m, 8-column chunk); 16 chunks
-// make a group and sit in 16 consecutive lanes, reduced with shuffles.
-__device__ __forceinline__ void gather_x(const uint16_t* __restrict__ x, int M, int64_t K,
-                                         const int32_t* __restrict__ perm_col, int c0, int ncl,
-                                         uint16_t* xs, int xs_stride, float* xsum, int kmax,
-                                         int nthreads) {
+// The workgroup's activation slice: rows 0 .. M-1 of the reordered x_r
+// (written once per call by the gather kernel) for block columns c0 ..
+// c0 + ncl - 1, copied into LDS with 16-byte loads, and the group sums
+// rebuilt from their three bf16 terms (S0 + S1 + S2 is exact in fp32).
+// The loads of kBatch items are issued before any store, and every thread
+// stores at its clamped item (threads past the end rewrite the last item
+// with the value they loaded from it), so no store is conditional.
+__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ xr,
+                                        const uint16_t* __restrict__ sxs, int M, int64_t K,
+                                        int64_t Gp, int c0, int ncl, uint16_t* xs, int xs_stride,
+                                        float* xsum, int kmax, int nthreads) {
+  constexpr int kBatch = 4;
   const int chunks = ncl * 16;
   const int items = M * chunks;
-  const int kk = (int)K - 1;
-  for (int base = 0; base < items; base += nthreads) {
-    const int it = base + (int)threadIdx.x;
-    float part = 0.f;
-    int m = 0, q = 0;
-    if (it < items) {
-      m = it / chunks;
-      q = it - m * chunks;
-      const int4* pc = reinterpret_cast<const int4*>(perm_col + (int64_t)c0 * kBlockCols + 8 * q);
-      const int4 p0 = pc[0], p1 = pc[1];
-      const uint16_t* xr = x + (int64_t)m * K;
-      const uint16_t u0 = xr[clampi(p0.x, kk)], u1 = xr[clampi(p0.y, kk)];
-      const uint16_t u2 = xr[clampi(p0.z, kk)], u3 = xr[clampi(p0.w, kk)];
-      const uint16_t u4 = xr[clampi(p1.x, kk)], u5 = xr[clampi(p1.y, kk)];
-      const uint16_t u6 = xr[clampi(p1.z, kk)], u7 = xr[clampi(p1.w, kk)];
-      uint4 v;
-      v.x = (uint32_t)u0 | ((uint32_t)u1 << 16);
-      v.y = (uint32_t)u2 | ((uint32_t)u3 << 16);
-      v.z = (uint32_t)u4 | ((uint32_t)u5 << 16);
-      v.w = (uint32_t)u6 | ((uint32_t)u7 << 16);
-      *reinterpret_cast<uint4*>(xs + (size_t)m * xs_stride + 8 * q) = v;
-      part = ((bf16f(u0) + bf16f(u1)) + (bf16f(u2) + bf16f(u3))) +
-             ((bf16f(u4) + bf16f(u5)) + (bf16f(u6) + bf16f(u7)));
-    }
-    // items of one group are 16 consecutive threads (chunks is a multiple of 16)
+  for (int base = threadIdx.x; base < items; base += kBatch * nthreads) {
+    uint4 v[kBatch];
+    int dst[kBatch];
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) part += __shfl_xor(part, d, 64);
-    if (it < items && (q & 15) == 0) xsum[m * kmax + (q >> 4)] = part;
+    for (int u = 0; u < kBatch; ++u) {
+      const int it = min(base + u * nthreads, items - 1);
+      const int m = it / chunks, q = it - (it / chunks) * chunks;
+      v[u] = reinterpret_cast<const uint4*>(xr + (int64_t)m * K + (int64_t)c0 * kBlockCols)[q];
+      dst[u] = m * xs_stride + 8 * q;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) *reinterpret_cast<uint4*>(xs + dst[u]) = v[u];
+  }
+  const int64_t plane = (int64_t)M * Gp;
+  for (int it = threadIdx.x; it < M * ncl; it += nthreads) {
+    const int m = it / ncl, c = it - (it / ncl) * ncl;
+    const uint16_t* s = sxs + (int64_t)m * Gp + c0 + c;
+    xsum[m * kmax + c] = (bf16f(s[0]) + bf16f(s[plane])) + bf16f(s[2 * plane]);
   }
 }
 
 template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x, int M,
+__global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ xr,
+                                                  const uint16_t* __restrict__ sxs, int M,
                                                   WeightView w, int split, int kmax, int xs_stride,
                                                   float* __restrict__ out, int direct) {
   const int lane = threadIdx.x & 63;
@@ -345,7 +343,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x
   // 2. activation slice
   Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, xs, xsum, xs_stride, kmax, M, 0u, 0u,
          0u, 0u};
-  gather_x(x, M, w.K, w.perm_col, c0, ncl, xs, xs_stride, xsum, kmax, NW * 64);
+  stage_x(xr, sxs, M, w.K, padded_groups(w.NBc), c0, ncl, xs, xs_stride, xsum, kmax, NW * 64);
   __syncthreads();
 
   f32x4 yacc[MT][4];
@@ -864,6 +862,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
 // last four only for M == 1.
 struct GemvWorkspace {
   float* part;
+  void* gather;  // M > 1: the gather kernel's x_r and split group sums
   uint16_t* xg;
   float* xsum;
   float* corr;
@@ -887,6 +886,7 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
   GemvWorkspace g{};
   g.part = reinterpret_cast<float*>(b);
   b += part_bytes(p, M, N);
+  if (M > 1) g.gather = b;
   if (M == 1) {
     const size_t nbc = (size_t)(K / kBlockCols);
     g.xg = reinterpret_cast<uint16_t*>(b);
@@ -910,11 +910,11 @@ hipError_t launch_m1(const GemvWorkspace& g, const WeightView& w, float* y, cons
 }
 
 template <int NW, int MT>
-hipError_t launch_cfg(const uint16_t* x, int M, const WeightView& w, float* dst,
-                      const GemvPlan& p, int direct, hipStream_t stream) {
+hipError_t launch_cfg(const uint16_t* xr, const uint16_t* sxs, int M, const WeightView& w,
+                      float* dst, const GemvPlan& p, int direct, hipStream_t stream) {
   const unsigned grid = (unsigned)(w.NBr * p.split);
-  hipLaunchKernelGGL((k_gemv<NW, MT>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, x, M, w,
-                     p.split, p.kr, p.xs_stride, dst, direct);
+  hipLaunchKernelGGL((k_gemv<NW, MT>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, xr, sxs, M,
+                     w, p.split, p.kr, p.xs_stride, dst, direct);
   return hipGetLastError();
 }
 
@@ -956,6 +956,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
       if (split > 8) split = 8;
     } else {
       split = (512 + NBr - 1) / NBr;
+      // with enough block rows, small M prefers fewer splits (less staging
+      // per workgroup and fewer partials): about one split per 4 rows of M
+      if (NBr >= 128) split = std::min<int>(split, std::max<int>(1, (int)((M + 3) / 4)));
     }
   }
   if (split > NBc) split = NBc;
@@ -975,7 +978,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   }
   const size_t red_bytes = (size_t)(p.nw - 1) * (size_t)M * kBlockRows * 4;
   p.lds_bytes = x_bytes > red_bytes ? x_bytes : red_bytes;
-  p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : 0);
+  p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : gather_workspace_bytes(M, K));
   return p;
 }
 
@@ -1057,19 +1060,32 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
     if (p.nw == 4) return launch_m1<4>(g, w, y, p, stream);
     if (p.nw == 16) return launch_m1<16>(g, w, y, p, stream);
     return launch_m1<8>(g, w, y, p, stream);
-  } else if (p.nw == 8) {
-    e = launch_cfg<8, 1>(x, (int)M, w, dst, p, direct, stream);
   } else {
-    switch (p.mt) {
-      case 2: e = launch_cfg<4, 2>(x, (int)M, w, dst, p, direct, stream); break;
-      case 3: e = launch_cfg<4, 3>(x, (int)M, w, dst, p, direct, stream); break;
-      default: e = launch_cfg<4, 4>(x, (int)M, w, dst, p, direct, stream); break;
+    // x reordered once per call, then staged slice by slice
+    e = launch_gather_x(x, M, w, g.gather, stream);
+    if (e != hipSuccess) return e;
+    const uint16_t* xr = reinterpret_cast<const uint16_t*>(g.gather);
+    const uint16_t* sxs = reinterpret_cast<const uint16_t*>(
+        reinterpret_cast<const uint8_t*>(g.gather) + align256((size_t)M * w.K * 2));
+    if (p.nw == 8) {
+      e = launch_cfg<8, 1>(xr, sxs, (int)M, w, dst, p, direct, stream);
+    } else {
+      switch (p.mt) {
+        case 2: e = launch_cfg<4, 2>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
+        case 3: e = launch_cfg<4, 3>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
+        default: e = launch_cfg<4, 4>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
+      }
     }
   }
   if (e != hipSuccess || direct) return e;
-  const int64_t total = M * w.N;
+  return launch_split_reduce(g.part, p.split, M, w.N, w.perm_row, y, stream);
+}
+
+hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t N,
+                               const int32_t* perm_row, float* y, hipStream_t stream) {
+  const int64_t total = M * N;
   hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
-                     g.part, p.split, (int)M, w.N, w.perm_row, y);
+                     part, split, (int)M, N, perm_row, y);
   return hipGetLastError();
 }
 

@@ -93,11 +93,11 @@ msq::WeightView view_of(const msq_weight* w) {
 size_t workspace_for(int64_t M, int64_t N, int64_t K, msq_kernel kernel) {
   if (M <= 0) return 0;
   const size_t gemv = M <= MSQ_GEMV_MAX_M ? msq::plan_gemv(M, N, K).workspace : 0;
-  const size_t gemm = msq::gemm_workspace_bytes(M, K);
+  const size_t gemm = msq::gemm_workspace_bytes(M, N, K);
   switch (kernel) {
     case MSQ_KERNEL_GEMV: return gemv;
     case MSQ_KERNEL_GEMM: return gemm;
-    default: return M <= MSQ_GEMV_MAX_M ? gemv : gemm;
+    default: return M <= MSQ_AUTO_GEMV_MAX_M ? gemv : gemm;
   }
 }
 
@@ -158,7 +158,7 @@ msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, f
   if (M == 0) return MSQ_OK;
   if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
   if (!x_bf16 || !y || !aligned(x_bf16, 16) || !aligned(y, 4)) return MSQ_ERR_INVALID_ARG;
-  if (kernel == MSQ_KERNEL_AUTO) kernel = M <= MSQ_GEMV_MAX_M ? MSQ_KERNEL_GEMV : MSQ_KERNEL_GEMM;
+  if (kernel == MSQ_KERNEL_AUTO) kernel = M <= MSQ_AUTO_GEMV_MAX_M ? MSQ_KERNEL_GEMV : MSQ_KERNEL_GEMM;
   if (kernel == MSQ_KERNEL_GEMV && M > MSQ_GEMV_MAX_M) return MSQ_ERR_UNSUPPORTED;
   const size_t need = workspace_for(M, w->N, w->K, kernel);
   if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
@@ -189,10 +189,11 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight* const* w, int
     const size_t one = msq_gemm_workspace_bytes(M, w[i]->N, w[i]->K);
     most = one > most ? one : most;
   }
-  // M == 1 and M > 64: every matrix keeps its own workspace during the one
-  // launch; 2 .. 64: the matrices run one after the other
+  // M == 1 and M > 16: every matrix keeps its own workspace (one launch for
+  // all, or split-K single calls); 2 .. 16: the matrices run one after the
+  // other
   if (M == 1) return msq::gemv_group_workspace_m1(v, count);
-  if (M > MSQ_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count);
+  if (M > MSQ_AUTO_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count);
   return most;
 }
 
@@ -210,7 +211,7 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
   if (M < 0) return MSQ_ERR_SHAPE;
   if (M == 0) return MSQ_OK;
   if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
-  if (M != 1 && M <= MSQ_GEMV_MAX_M) {
+  if (M != 1 && M <= MSQ_AUTO_GEMV_MAX_M) {
     // one matrix after the other, sharing the workspace (ordered on stream)
     for (int i = 0; i < count; ++i) {
       const msq_status st = msq_gemm(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, stream);

@@ -41,7 +41,7 @@ struct GemvPlan {
   int nw;           // wavefronts per workgroup
   int xs_stride;    // bf16 elements per LDS row of the activation slice
   size_t lds_bytes; // dynamic LDS per workgroup
-  size_t workspace; // bytes of fp32 partials (0 when split == 1)
+  size_t workspace; // bytes: fp32 partials (split > 1), then M == 1 prep or M > 1 gather buffers
 };
 // group_rows > 0: the plan of one matrix of a grouped launch whose matrices
 // have group_rows output rows in total (the K split then fills the GPU with
@@ -57,8 +57,24 @@ size_t gemv_group_workspace_m1(const WeightView* w, int count);
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
                                 int count, void* workspace, hipStream_t stream);
 
-// ---- prefill GEMM, any M (msq_gemm.hip)
-size_t gemm_workspace_bytes(int64_t M, int64_t K);
+// ---- activation gather for M > 1 (msq_gemm.hip): x_r[m][j] = x[m][perm_col[j]]
+// and the group sums of x_r split into three bf16 terms S0 + S1 + S2 (exact
+// fp32), [3][M][Gp] with Gp = the group count rounded up to 32.  It writes
+// gather_workspace_bytes(M, K) bytes at ws: x_r first, the sums 256-byte
+// aligned after it.
+__host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31) & ~(int64_t)31; }
+size_t gather_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
+                           hipStream_t stream);
+
+// ---- K-split reduction (msq_gemv.hip): y[m][perm_row[n]] = sum over splits,
+// in split order, of part[sp][m][n].
+hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t N,
+                               const int32_t* perm_row, float* y, hipStream_t stream);
+
+// ---- prefill GEMM, any M (msq_gemm.hip).  Workspace: the gather buffers,
+// then (when the call splits K to fill the GPU) fp32 partials.
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, hipStream_t stream);
 // Grouped prefill of count (1 .. 8) matrices at one M: one gather and one GEMM

@@ -101,6 +101,9 @@ extern "C" {
 #define MSQ_NO_BLOCK 0xFFFFFFFFu
 /* Largest M the decode (GEMV) kernel accepts. */
 #define MSQ_GEMV_MAX_M 64
+/* Largest M for which MSQ_KERNEL_AUTO picks the GEMV kernel; above it the
+ * GEMM (which splits K when its tiles cannot fill the GPU) is faster. */
+#define MSQ_AUTO_GEMV_MAX_M 16
 
 typedef enum {
   MSQ_OK = 0,
@@ -114,7 +117,7 @@ typedef enum {
 } msq_status;
 
 typedef enum {
-  MSQ_KERNEL_AUTO = 0,  /* GEMV for M <= MSQ_GEMV_MAX_M, GEMM otherwise */
+  MSQ_KERNEL_AUTO = 0,  /* GEMV for M <= MSQ_AUTO_GEMV_MAX_M, GEMM otherwise */
   MSQ_KERNEL_GEMV = 1,  /* decode kernel; M <= MSQ_GEMV_MAX_M */
   MSQ_KERNEL_GEMM = 2   /* prefill kernel; any M >= 1 */
 } msq_kernel;
@@ -208,9 +211,10 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int
  * activation-prep launch and one decode launch cover all matrices, their
  * workgroups running side by side ("TileQuant" abstract: local accumulation
  * to reduce memory traffic; the grouping itself is this library's).  At
- * M > 64 (prefill) one activation-gather launch and one GEMM launch cover
- * all matrices, the tiles of the smaller ones filling the compute units the
- * larger ones leave idle.  M in 2 .. 64: the matrices are computed one after
+ * M > 16, when the matrices' tiles fill the GPU (prefill), one
+ * activation-gather launch and one GEMM launch cover all matrices, the tiles
+ * of the smaller ones filling the compute units the larger ones leave idle;
+ * with fewer tiles, and at M in 2 .. 16, the matrices are computed one after
  * the other as by msq_gemm.  x,
  * w and y are host arrays of count device pointers / descriptors; x[i] may
  * repeat the same activation.  workspace must hold

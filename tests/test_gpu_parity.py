@@ -136,6 +136,7 @@ def test_m_boundary_sweep(msq, N, K, seed):
         check_y(msq, pw, c, ref, M, kernel="auto")
         if M <= 64:
             check_y(msq, pw, c, ref, M, kernel="gemm")
+            check_y(msq, pw, c, ref, M, kernel="gemv")
 
 
 @pytest.fixture(scope="module")
@@ -297,6 +298,42 @@ def test_group_matches_single_calls(msq, group_cases, monkeypatch, M):
             torch.cuda.synchronize()
             assert torch.equal(y, single), c.name
             check_y(msq, pw, c, ref, M, x=x)
+
+
+def test_group_prefill_one_launch(msq):
+    """Two 4096 x 1024 matrices at M = 1024 have enough tiles for the one grouped GEMM
+    launch (smaller groups run as split-K single calls): each output equals its single
+    call bit for bit and the oracle within tolerance."""
+    cases = []
+    for seed, dist in ((64, SMALL_DIST), (65, {2: .5, 4: .3, 8: .2})):
+        c = synth.random_case(4096, 1024, seed, dist=dist)
+        cases.append((c,) + check_pack(msq, c))
+    M = 1024
+    x = cases[0][0].x(M)
+    outs = msq.gemm_group([x, x], [pw for _, pw, _ in cases])
+    torch.cuda.synchronize()
+    for (c, pw, ref), y in zip(cases, outs):
+        single = msq.gemm(x, pw)
+        torch.cuda.synchronize()
+        assert torch.equal(y, single), c.name
+        check_y(msq, pw, c, ref, M, x=x)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 5, 8])
+def test_gemm_split_k(msq, monkeypatch, split):
+    """The GEMM with its K range cut into `split` pieces (ragged last piece for 3 and 5;
+    partials summed in split order by the reduction): oracle within tolerance at a
+    one-tile and a two-tile M, and reproducible."""
+    c = synth.random_case(256, 8192, 66, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    monkeypatch.setenv("MSQ_GEMM_SPLIT", str(split))
+    for M in (16, 130):
+        x = c.x(M)
+        check_y(msq, pw, c, ref, M, kernel="gemm", x=x)
+        a = msq.gemm(x, pw, kernel="gemm")
+        b = msq.gemm(x, pw, kernel="gemm")
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("M", [1, 130])
