@@ -952,7 +952,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   int split = env_int("MSQ_GEMV_SPLIT", 0);
   if (split <= 0) {
     if (M == 1) {
-      split = 512 / rows;
+      // about one workgroup of 8 wavefronts per CU: more K splits add start-ups
+      // and partials faster than they add memory parallelism
+      split = 256 / rows;
       if (split > 8) split = 8;
     } else {
       split = (512 + NBr - 1) / NBr;
