@@ -244,31 +244,72 @@ __device__ __forceinline__ void consume_block(const Ctx& cx, int cl, const Block
   }
 }
 
-// Blocks per batch of a B-bit run.  Larger M keeps more accumulators live,
-// so its batches are smaller.
-template <int B, int MT>
-constexpr int batch_of() {
-  if constexpr (MT == 1) return B <= 2 ? 2 : 1;
-  else return 1;
+// Blocks per register ring of a B-bit run: (depth - 1) * B KiB of codes stay
+// in flight while one block is consumed.  More rows of M keep more
+// accumulators live, so their rings are shallower.
+template <int B, int MT = 1>
+constexpr int ring_depth() {
+  if constexpr (MT == 1) return B == 1 ? 8 : (B == 2 ? 4 : (B == 8 ? 2 : 3));
+  else if constexpr (MT == 2) return B <= 4 ? 2 : 1;
+  else return B <= 2 ? 2 : 1;
 }
 
-// CNT consecutive blocks of a run (run indices i .. i+CNT-1, columns taken
-// from `cols` in order): issue all their loads, then consume them in order.
-// Straight-line code in which every load is consumed, so the wait counts are
-// static and no load stays in flight past the section.
-template <int B, int CNT, int MT>
-__device__ __forceinline__ void run_batch(const Ctx& cx, const uint8_t* base, int i, uint64_t& cols,
-                                          f32x4 (&yacc)[MT][4]) {
-  BlockRegs<B> br[CNT];
-  int cc[CNT];
+// A run of n >= 1 blocks of bitwidth B whose columns are the lowest n set
+// bits of `cols`, starting at `base` (this lane's 16 bytes of the run's first
+// chunk; block i of the run starts B * i KiB later).  A ring of D register
+// sets with fixed roles: set j holds blocks j, j + D, j + 2D, ...; after
+// block i is consumed, the loads of block i + D go into its set.  Issues are
+// unconditional (past the end of the run they repeat its last block, which
+// is never consumed) and the loop runs whole passes over the ring with its
+// only exit at the end of a pass, so every consume sees the same loads
+// outstanding in the same order and the wait counts stay static: D - 1
+// blocks in flight during each consume.  (An exit from the middle of the
+// unrolled body leaves structurized control-flow paths on which the
+// compiler cannot bound the outstanding loads, and it then waits for all.)
+// kScaleZero: the ring also loads each block's scales and zero points (two
+// more loads per block).  consume(column, registers) uses a block;
+// after_issue(integral_constant<loads issued>) runs once after the first D
+// blocks are issued.
+template <int B, int D, bool kScaleZero, typename Consume, typename AfterIssue>
+__device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
+                                         Consume&& consume, AfterIssue&& after_issue) {
+  constexpr int64_t kStride = 1024 * B;
+  BlockRegs<B> rs[D];
+  int cs[D];
+  // compiler-only barriers after the issues keep the loads where they are
+  // written (the compiler would otherwise sink them toward their first use)
 #pragma unroll
-  for (int j = 0; j < CNT; ++j) {
-    cc[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
-    cols &= cols - 1;
-    issue_block<B>(cx, base + (int64_t)(i + j) * (1024 * B), cc[j], br[j]);
+  for (int j = 0; j < D; ++j) {
+    if (j == 0 || j < n) {
+      cs[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
+      cols &= cols - 1;
+    } else {
+      cs[j] = cs[j - 1];
+    }
+    int bi = __builtin_amdgcn_readfirstlane(j < n ? j : n - 1);
+    asm("" : "+s"(bi));
+    issue_block<B, kScaleZero>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+    asm volatile("" ::: "memory");
   }
+  // the first run: the workgroup's start-up, while these loads fly
+  after_issue(std::integral_constant<int, D * (B + (kScaleZero ? 2 : 0))>{});
+  int i0 = 0;  // run index of the block in set 0
+  do {
 #pragma unroll
-  for (int j = 0; j < CNT; ++j) consume_block<B, MT>(cx, cc[j], br[j], yacc);
+    for (int j = 0; j < D; ++j) {
+      if (i0 + j < n) consume(cs[j], rs[j]);
+      const int nx = i0 + j + D;
+      if (nx < n) {
+        cs[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
+        cols &= cols - 1;
+      }
+      int bi = __builtin_amdgcn_readfirstlane(nx < n ? nx : n - 1);
+      asm("" : "+s"(bi));
+      issue_block<B, kScaleZero>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+      asm volatile("" ::: "memory");
+    }
+    i0 += D;
+  } while (i0 < n);
 }
 
 // A run of n blocks of bitwidth B whose columns are the lowest n set bits of
@@ -278,12 +319,12 @@ __device__ __forceinline__ void run_batch(const Ctx& cx, const uint8_t* base, in
 template <int B, int MT>
 __device__ __forceinline__ void run_blocks(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
                                            f32x4 (&yacc)[MT][4]) {
-  constexpr int BATCH = batch_of<B, MT>();
-  int i = 0;
-  for (; i + BATCH <= n; i += BATCH) run_batch<B, BATCH, MT>(cx, base, i, cols, yacc);
-  if constexpr (BATCH > 1) {
-    if (n - i >= 1) run_batch<B, 1, MT>(cx, base, i, cols, yacc);
-  }
+  ring_run<B, ring_depth<B, MT>(), true>(
+      cx, base, cols, n,
+      [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
+        consume_block<B, MT>(cx, cl, br, yacc);
+      },
+      [](auto) __attribute__((always_inline)) {});
 }
 
 // The workgroup's activation slice: rows 0 .. M-1 of the reordered x_r
@@ -520,66 +561,16 @@ __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockReg
   y1 += sc * ((v - corr) - (float)z * xsum);
 }
 
-// Blocks per register ring of a B-bit run: (depth - 1) * B KiB of codes stay
-// in flight while one block is consumed.
-template <int B>
-constexpr int ring_depth() {
-  return B == 1 ? 8 : (B == 2 ? 4 : (B == 8 ? 2 : 3));
-}
-
-// A run of n >= 1 blocks of bitwidth B whose columns are the lowest n set
-// bits of `cols`, starting at `base` (this lane's 16 bytes of the run's first
-// chunk; block i of the run starts B * i KiB later).  A ring of D register
-// sets with fixed roles: set j holds blocks j, j + D, j + 2D, ...; after
-// block i is consumed, the loads of block i + D go into its set.  Issues are
-// unconditional (past the end of the run they repeat its last block, which
-// is never consumed) and the loop runs whole passes over the ring with its
-// only exit at the end of a pass, so every consume sees the same loads
-// outstanding in the same order and the wait counts stay static: D - 1
-// blocks in flight during each consume.  (An exit from the middle of the
-// unrolled body leaves structurized control-flow paths on which the
-// compiler cannot bound the outstanding loads, and it then waits for all.)
+// M == 1 run: the ring of ring_depth<B>() blocks, codes only.
 template <int B, typename AfterIssue>
 __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
                                          float& y1, AfterIssue&& after_issue) {
-  constexpr int D = ring_depth<B>();
-  constexpr int64_t kStride = 1024 * B;
-  BlockRegs<B> rs[D];
-  int cs[D];
-  // compiler-only barriers after the issues keep the loads where they are
-  // written (the compiler would otherwise sink them toward their first use)
-#pragma unroll
-  for (int j = 0; j < D; ++j) {
-    if (j == 0 || j < n) {
-      cs[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
-      cols &= cols - 1;
-    } else {
-      cs[j] = cs[j - 1];
-    }
-    int bi = __builtin_amdgcn_readfirstlane(j < n ? j : n - 1);
-    asm("" : "+s"(bi));
-    issue_block<B, false>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
-    asm volatile("" ::: "memory");
-  }
-  // the first run: the workgroup's start-up, while these D * B loads fly
-  after_issue(std::integral_constant<int, D * B>{});
-  int i0 = 0;  // run index of the block in set 0
-  do {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      if (i0 + j < n) consume_m1<B>(cx, cs[j], rs[j], y1);
-      const int nx = i0 + j + D;
-      if (nx < n) {
-        cs[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
-        cols &= cols - 1;
-      }
-      int bi = __builtin_amdgcn_readfirstlane(nx < n ? nx : n - 1);
-      asm("" : "+s"(bi));
-      issue_block<B, false>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
-      asm volatile("" ::: "memory");
-    }
-    i0 += D;
-  } while (i0 < n);
+  ring_run<B, ring_depth<B>(), false>(
+      cx, base, cols, n,
+      [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
+        consume_m1<B>(cx, cl, br, y1);
+      },
+      after_issue);
 }
 
 // Direct global-to-LDS copies of 16 (4) bytes per lane: lane i writes at
