@@ -53,65 +53,85 @@ __device__ __forceinline__ uint16_t bf16_rn(float v) {
 }
 
 
-// Row m of one matrix's gather.
+// Chunks qs .. qe - 1 (whole groups) of row m of one matrix's gather.  The
+// x row is copied into LDS with direct-to-LDS loads (when staged), and the
+// perm_col loads of kBatch passes are issued before any of them is used.
 __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64_t K, int64_t M,
                                            const int32_t* __restrict__ perm_col,
                                            uint16_t* __restrict__ xr, uint16_t* __restrict__ sxs,
-                                           int staged, int64_t m) {
+                                           int staged, int64_t m, int64_t qs, int64_t qe) {
+  constexpr int kBatch = 4;
+  const int lane = threadIdx.x & 63;
   const int64_t chunks = K / 8;
   const int64_t Gp = padded_groups(K / kBlockCols);
   const uint16_t* xrow = x + m * K;
   uint16_t* srow = reinterpret_cast<uint16_t*>(smem);
   if (staged) {
     const uint4* src = reinterpret_cast<const uint4*>(xrow);
-    for (int64_t i = threadIdx.x; i < chunks; i += kGatherThreads)
-      reinterpret_cast<uint4*>(smem)[i] = src[i];
+    for (int64_t i = threadIdx.x; i < chunks; i += kGatherThreads)  // lane l lands at base + 16 l
+      __builtin_amdgcn_global_load_lds(src + i, (lds_void*)(smem + 16 * (i - lane)), 16, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   const uint16_t* from = staged ? srow : xrow;
   const int kk = (int)K - 1;
   const int64_t plane = M * Gp;
-  for (int64_t q0 = 0; q0 < Gp * 16; q0 += kGatherThreads) {
-    const int64_t q = q0 + threadIdx.x;
-    float part = 0.f;
-    if (q < chunks) {
-      const int4* pc = reinterpret_cast<const int4*>(perm_col + 8 * q);
-      const int4 p0 = pc[0], p1 = pc[1];
-      const uint16_t u0 = from[min(max(p0.x, 0), kk)], u1 = from[min(max(p0.y, 0), kk)];
-      const uint16_t u2 = from[min(max(p0.z, 0), kk)], u3 = from[min(max(p0.w, 0), kk)];
-      const uint16_t u4 = from[min(max(p1.x, 0), kk)], u5 = from[min(max(p1.y, 0), kk)];
-      const uint16_t u6 = from[min(max(p1.z, 0), kk)], u7 = from[min(max(p1.w, 0), kk)];
-      uint4 v;
-      v.x = (uint32_t)u0 | ((uint32_t)u1 << 16);
-      v.y = (uint32_t)u2 | ((uint32_t)u3 << 16);
-      v.z = (uint32_t)u4 | ((uint32_t)u5 << 16);
-      v.w = (uint32_t)u6 | ((uint32_t)u7 << 16);
-      reinterpret_cast<uint4*>(xr + m * K)[q] = v;
-      part = ((bf16f(u0) + bf16f(u1)) + (bf16f(u2) + bf16f(u3))) +
-             ((bf16f(u4) + bf16f(u5)) + (bf16f(u6) + bf16f(u7)));
-    }
-    // a group is 16 consecutive chunks, i.e. 16 consecutive threads
+  for (int64_t q0 = qs; q0 < qe; q0 += kBatch * kGatherThreads) {
+    int4 pa[kBatch], pb[kBatch];
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) part += __shfl_xor(part, d, 64);
-    if (q < Gp * 16 && (q & 15) == 0) {
-      const uint16_t t0 = bf16_rn(part);
-      const float r1 = part - bf16f(t0);
-      const uint16_t t1 = bf16_rn(r1);
-      const uint16_t t2 = bf16_rn(r1 - bf16f(t1));
-      uint16_t* dst = sxs + m * Gp + q / 16;
-      dst[0] = t0;
-      dst[plane] = t1;
-      dst[2 * plane] = t2;
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t q = min(q0 + u * kGatherThreads + threadIdx.x, chunks - 1);
+      const int4* pc = reinterpret_cast<const int4*>(perm_col + 8 * q);
+      pa[u] = pc[0];
+      pb[u] = pc[1];
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t q = q0 + u * kGatherThreads + threadIdx.x;
+      if (q0 + u * kGatherThreads >= qe) break;  // uniform
+      float part = 0.f;
+      if (q < chunks) {
+        const int4 p0 = pa[u], p1 = pb[u];
+        const uint16_t u0 = from[min(max(p0.x, 0), kk)], u1 = from[min(max(p0.y, 0), kk)];
+        const uint16_t u2 = from[min(max(p0.z, 0), kk)], u3 = from[min(max(p0.w, 0), kk)];
+        const uint16_t u4 = from[min(max(p1.x, 0), kk)], u5 = from[min(max(p1.y, 0), kk)];
+        const uint16_t u6 = from[min(max(p1.z, 0), kk)], u7 = from[min(max(p1.w, 0), kk)];
+        uint4 v;
+        v.x = (uint32_t)u0 | ((uint32_t)u1 << 16);
+        v.y = (uint32_t)u2 | ((uint32_t)u3 << 16);
+        v.z = (uint32_t)u4 | ((uint32_t)u5 << 16);
+        v.w = (uint32_t)u6 | ((uint32_t)u7 << 16);
+        reinterpret_cast<uint4*>(xr + m * K)[q] = v;
+        part = ((bf16f(u0) + bf16f(u1)) + (bf16f(u2) + bf16f(u3))) +
+               ((bf16f(u4) + bf16f(u5)) + (bf16f(u6) + bf16f(u7)));
+      }
+      // a group is 16 consecutive chunks, i.e. 16 consecutive threads
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) part += __shfl_xor(part, d, 64);
+      if (q < qe && (q & 15) == 0) {
+        const uint16_t t0 = bf16_rn(part);
+        const float r1 = part - bf16f(t0);
+        const uint16_t t1 = bf16_rn(r1);
+        const uint16_t t2 = bf16_rn(r1 - bf16f(t1));
+        uint16_t* dst = sxs + m * Gp + q / 16;
+        dst[0] = t0;
+        dst[plane] = t1;
+        dst[2 * plane] = t2;
+      }
     }
   }
 }
 
+// Row blockIdx.x, chunk slice blockIdx.y of gridDim.y (whole groups).
 __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __restrict__ x,
                                                              int64_t K, int64_t M,
                                                              const int32_t* __restrict__ perm_col,
                                                              uint16_t* __restrict__ xr,
                                                              uint16_t* __restrict__ sxs, int staged) {
-  gather_row(x, K, M, perm_col, xr, sxs, staged, blockIdx.x);
+  const int64_t Gp = padded_groups(K / kBlockCols);
+  const int64_t per = (Gp + gridDim.y - 1) / gridDim.y * 16;
+  const int64_t qs = (int64_t)blockIdx.y * per;
+  gather_row(x, K, M, perm_col, xr, sxs, staged, blockIdx.x, qs, min(qs + per, Gp * 16));
 }
 
 // ---- GEMM ------------------------------------------------------------------------------
@@ -613,7 +633,8 @@ __device__ __forceinline__ GemmJob pick_gemm_job(const GemmGroup& g, int b, bool
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, true);
-  gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, q.staged, blockIdx.x % g.M);
+  gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, q.staged, blockIdx.x % g.M, 0,
+             padded_groups(q.w.K / kBlockCols) * 16);
 }
 
 template <int BR>
@@ -733,8 +754,12 @@ hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, vo
   uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + xr_bytes);
   const size_t row_bytes = (size_t)K * 2;
   const int staged = row_bytes <= kGatherMaxLds;
-  hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M), dim3(kGatherThreads), staged ? row_bytes : 0,
-                     stream, x, K, M, w.perm_col, xr, sxs, staged);
+  // few rows: each row's groups are cut into slices of their own workgroups
+  // (every slice stages the whole row), so that small M still fills the GPU
+  const int64_t slices = std::max<int64_t>(
+      1, std::min<int64_t>(padded_groups(K / kBlockCols) / 16, 256 / std::max<int64_t>(M, 1)));
+  hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M, (unsigned)slices), dim3(kGatherThreads),
+                     staged ? row_bytes : 0, stream, x, K, M, w.perm_col, xr, sxs, staged);
   return hipGetLastError();
 }
 
