@@ -611,6 +611,7 @@ struct GemmJob {
   uint16_t* xr;
   uint16_t* sxs;
   float* y;
+  float* yr;       // non-null: the tiles write y in reordered order here (= y), un-permuted after
   int staged;      // gather: x row staged in LDS
   int mtiles;      // tiles along M
   int tile_begin;  // first tile of the job in the GEMM launch
@@ -642,7 +643,51 @@ __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_
     GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
   const int t = blockIdx.x - q.tile_begin;
-  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, nullptr);
+  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, q.yr);
+}
+
+// ---- row un-permutation ------------------------------------------------------------
+// The GEMM tiles cover consecutive reordered rows n, whose original columns
+// perm_row[n] of y are scattered: writing y[m][perm_row[n]] from the tiles
+// leaves every 64-byte line of y partly written by many workgroups, and the
+// partial lines reach HBM many times over (about 9x the bytes of y).  So the
+// tiles write y in reordered order into y itself, and one workgroup per row
+// then reads the whole row into registers and writes it back permuted, each
+// line completed by one workgroup while it sits in L2.
+constexpr int kUnpermuteThreads = 1024;
+constexpr int kUnpermutePer = 32;
+constexpr int64_t kUnpermuteMaxN = (int64_t)kUnpermutePer * kUnpermuteThreads;
+
+struct UnpermuteJob {
+  float* y;
+  const int32_t* perm_row;
+  int64_t N;
+};
+struct UnpermuteGroup {
+  UnpermuteJob job[kGroupMax];
+  int count;
+};
+
+// Row blockIdx.x of job blockIdx.y (N <= kUnpermuteMaxN): y[perm_row[n]] = y[n].
+__global__ __launch_bounds__(kUnpermuteThreads) void k_unpermute_rows(UnpermuteGroup g) {
+  UnpermuteJob q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k == (int)blockIdx.y) q = g.job[k];
+  float* row = q.y + (int64_t)blockIdx.x * q.N;
+  const int t = threadIdx.x;
+  float v[kUnpermutePer];
+  int dst[kUnpermutePer];
+#pragma unroll
+  for (int i = 0; i < kUnpermutePer; ++i) {
+    const int64_t n = min((int64_t)t + (int64_t)i * kUnpermuteThreads, q.N - 1);
+    v[i] = row[n];
+    dst[i] = min(max(q.perm_row[n], 0), (int)q.N - 1);
+  }
+  __syncthreads();  // the whole row is read before any of it is overwritten
+#pragma unroll
+  for (int i = 0; i < kUnpermutePer; ++i)
+    if ((int64_t)t + (int64_t)i * kUnpermuteThreads < q.N) row[dst[i]] = v[i];
 }
 
 // Block rows per workgroup of the prefill GEMM (MSQ_GEMM_BR=2 or 4 overrides).
@@ -727,6 +772,7 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
     q.sxs = reinterpret_cast<uint16_t*>(ws + xr_bytes);
     ws += (gemm_workspace_bytes(M, w[i].N, K) + 255) & ~(size_t)255;
     q.y = y[i];
+    q.yr = w[i].N <= kUnpermuteMaxN ? y[i] : nullptr;
     q.staged = (size_t)K * 2 <= kGatherMaxLds;
     if (q.staged) lds = std::max(lds, (size_t)K * 2);
     q.mtiles = (int)((M + kBM - 1) / kBM);
@@ -743,6 +789,14 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   else
     hipLaunchKernelGGL(k_gemm_group<4>, dim3((unsigned)tiles), dim3(TileCfg<4>::kThreads), 0,
                        stream, g);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  UnpermuteGroup u{};
+  for (int i = 0; i < count; ++i)
+    if (g.job[i].yr) u.job[u.count++] = UnpermuteJob{y[i], w[i].perm_row, w[i].N};
+  if (u.count == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, (unsigned)u.count), dim3(kUnpermuteThreads),
+                     0, stream, u);
   return hipGetLastError();
 }
 
@@ -784,15 +838,24 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + p.br - 1) / p.br),
                   (unsigned)p.split);
+  // one K range: the tiles write y in reordered order (into y), un-permuted after
+  const bool unpermute = p.split == 1 && w.N <= kUnpermuteMaxN;
+  float* out = p.split > 1 ? part : (unpermute ? y : nullptr);
   if (p.br == 2)
     hipLaunchKernelGGL(k_gemm<2>, grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y, part, p.gper);
+                       y, out, p.gper);
   else
     hipLaunchKernelGGL(k_gemm<4>, grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y, part, p.gper);
+                       y, out, p.gper);
   e = hipGetLastError();
-  if (e != hipSuccess || p.split == 1) return e;
-  return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);
+  if (e != hipSuccess) return e;
+  if (p.split > 1) return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);
+  if (!unpermute) return hipSuccess;
+  UnpermuteGroup u{};
+  u.job[0] = UnpermuteJob{y, w.perm_row, w.N};
+  u.count = 1;
+  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, 1u), dim3(kUnpermuteThreads), 0, stream, u);
+  return hipGetLastError();
 }
 
 }  // namespace msq
