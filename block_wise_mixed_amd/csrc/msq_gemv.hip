@@ -824,6 +824,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 // K-split reduction
 // ======================================================================================
 
+// Row blockIdx.x of the same sum, one workgroup per row.
+constexpr int kReduceRowThreads = 1024;
+__global__ __launch_bounds__(kReduceRowThreads) void k_gemv_reduce_rows(
+    const float* __restrict__ part, int split, int M, int64_t N, const int32_t* __restrict__ perm_row,
+    float* __restrict__ y) {
+  const int64_t m = blockIdx.x;
+  const int64_t plane = (int64_t)M * N;
+  for (int64_t n = threadIdx.x; n < N; n += kReduceRowThreads) {
+    const float* p = part + m * N + n;
+    float v = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= split; sp += 8) {
+      float t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = p[(sp + k) * plane];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v += t[k];
+    }
+    for (; sp < split; ++sp) v += p[sp * plane];
+    y[m * N + orig_row(perm_row, n, N)] = v;
+  }
+}
+
 // y[m][perm_row[n]] = sum over splits (in order) of partial[sp][m][n].
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int split,
                                                      int M, int64_t N,
@@ -1076,6 +1099,15 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
 
 hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t N,
                                const int32_t* perm_row, float* y, hipStream_t stream) {
+  if (M >= 256) {
+    // one workgroup per row (enough rows to fill the GPU): every 64-byte line
+    // of the row is completed by one workgroup while it sits in L2
+    // (workgroups sharing a row would each leave it partly written, and
+    // partial lines reach HBM many times over)
+    hipLaunchKernelGGL(k_gemv_reduce_rows, dim3((unsigned)M), dim3(kReduceRowThreads), 0, stream,
+                       part, split, (int)M, N, perm_row, y);
+    return hipGetLastError();
+  }
   const int64_t total = M * N;
   hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
                      part, split, (int)M, N, perm_row, y);
