@@ -77,8 +77,7 @@ struct Ctx {
   int xs_stride;         // bf16 elements per LDS row
   int kmax;              // block columns per workgroup (row length of xsum)
   int M;
-  uint32_t corr_off;     // M == 1: LDS byte offset of corr [kmax][20]
-  uint32_t xsum_off;     // M == 1: LDS byte offset of xsum [kmax]
+  uint32_t sums_off;     // M == 1: LDS byte offset of the k-step sums [kmax][4] f32
   uint32_t a_lane;       // M == 1: LDS byte offset of this lane's A operand in column 0
   uint32_t zero_off;     // M == 1: LDS byte offset of the zero area (A operand of dead lanes)
   uint32_t s_off;        // M == 1: LDS byte offset of the range's scales [ncl][64] f32
@@ -447,28 +446,25 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x
 // M == 1
 // ======================================================================================
 //
-// k_prep_m1 reorders x once per call into the workspace: xg[j] = x[perm_col[j]],
-// the group sums xsum[c] and, per block column c, the bias corrections
-//     corr[c][4*k + rt] = sum_kt exp_bias(b_k, 4*rt + kt) * S_c[kt]
-// for (b_0 .. b_4) = (1, 2, 3, 4, 8), where S_c[kt] is the sum of the 32
-// reordered columns of k-step kt.  k_gemv_m1 copies its range of these
-// contiguous arrays into LDS with 16-byte loads.
+// k_prep_m1 reorders x once per call into the workspace: xg[j] = x[perm_col[j]]
+// and, per block column c, the k-step sums S_c[kt] (kt = 0..3, each over 32
+// reordered columns).  k_gemv_m1 copies its range of both into LDS with
+// 16-byte loads; per block it forms the group sum and the bias correction
+//     corr = sum_kt exp_bias(b, 4*rt + kt) * S_c[kt]
+// (rt = the lane's row tile) from them.
 //
 // M == 1 uses one row of the 16-row A operand: lanes with (l & 15) == 0 read
 // x, the others read a zero area, and the 64 row results of a block come out
 // in lanes 0..15 of the four row-tile accumulators (rows_to_lanes moves row
 // 16*rt + n to lane 16*rt + n).
 
-constexpr int kBitsM1[5] = {1, 2, 3, 4, 8};
-constexpr int kCorrStride = 20;  // corr entries per block column: 5 bitwidths x 4 row tiles
 
 // One wavefront per block column; lane l handles columns 2l, 2l + 1.
 // Workgroup `blk` of the prep of one matrix.
 __device__ __forceinline__ void prep_m1(const uint16_t* __restrict__ x, int64_t K,
                                         const int32_t* __restrict__ perm_col,
-                                        uint16_t* __restrict__ xg, float* __restrict__ xsum,
-                                        float* __restrict__ corr, uint32_t* __restrict__ counters,
-                                        int ncounters, int blk) {
+                                        uint16_t* __restrict__ xg, float4* __restrict__ sums,
+                                        uint32_t* __restrict__ counters, int ncounters, int blk) {
   const int lane = threadIdx.x & 63;
   const int64_t gid = (int64_t)blk * 256 + threadIdx.x;
   if (gid < ncounters) counters[gid] = 0u;
@@ -485,21 +481,15 @@ __device__ __forceinline__ void prep_m1(const uint16_t* __restrict__ x, int64_t 
   for (int d = 1; d < 16; d <<= 1) s += __shfl_xor(s, d, 64);
   const float s0 = __shfl(s, 0, 64), s1 = __shfl(s, 16, 64);
   const float s2 = __shfl(s, 32, 64), s3 = __shfl(s, 48, 64);
-  if (lane < kCorrStride) {
-    const int b = kBitsM1[lane >> 2], rt = lane & 3;
-    corr[c * kCorrStride + lane] = exp_bias(b, 4 * rt) * s0 + exp_bias(b, 4 * rt + 1) * s1 +
-                                   exp_bias(b, 4 * rt + 2) * s2 + exp_bias(b, 4 * rt + 3) * s3;
-  }
-  if (lane == 0) xsum[c] = (s0 + s1) + (s2 + s3);
+  if (lane == 0) sums[c] = float4{s0, s1, s2, s3};
 }
 
 __global__ __launch_bounds__(256) void k_prep_m1(const uint16_t* __restrict__ x, int64_t K,
                                                  const int32_t* __restrict__ perm_col,
                                                  uint16_t* __restrict__ xg,
-                                                 float* __restrict__ xsum,
-                                                 float* __restrict__ corr,
+                                                 float4* __restrict__ sums,
                                                  uint32_t* __restrict__ counters, int ncounters) {
-  prep_m1(x, K, perm_col, xg, xsum, corr, counters, ncounters, blockIdx.x);
+  prep_m1(x, K, perm_col, xg, sums, counters, ncounters, blockIdx.x);
 }
 
 // Route element 0 of v0..v3, lanes 0..15 (rows 16*rt + l of row tile rt;
@@ -534,10 +524,12 @@ __device__ __forceinline__ void block_product_m1(const uint4 (&ch)[B], const bf1
 }
 
 // Unpack, multiply and fold one block (column cl) into y1 (row `lane`):
-//     y1 += s * ((sum_k (bias_k + q_k) x_k - corr) - z * sum_k x_k).
+//     y1 += s * ((sum_k (bias_k + q_k) x_k - corr) - z * sum_k x_k),
+// corr = sum_kt bias[kt] * S[kt] with this lane's biases `bias` (row tile
+// lane >> 4, bitwidth B) and the column's k-step sums S.
 template <int B>
 __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockRegs<B>& br,
-                                           float& y1) {
+                                           float& y1, const float4& bias) {
   const int lane = threadIdx.x & 63;
   // A operands: lanes 0, 16, 32, 48 read x; the others read the zero area
   bf16x8 A[4];
@@ -551,11 +543,9 @@ __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockReg
   f32x4 acc[4];
   block_product_m1<B>(br.ch, A, acc);
   const float v = rows_to_lanes(acc[0][0], acc[1][0], acc[2][0], acc[3][0]);
-  constexpr int kidx = B == 1 ? 0 : (B == 2 ? 1 : (B == 3 ? 2 : (B == 4 ? 3 : 4)));
-  // 24-bit multiply (v_mul_u32_u24), for the same reason as the shift above
-  const float corr = *reinterpret_cast<const float*>(
-      smem + cx.corr_off + __umul24((uint32_t)cl, 4u * kCorrStride) + 16 * kidx + 4 * (lane >> 4));
-  const float xsum = *reinterpret_cast<const float*>(smem + cx.xsum_off + 4 * (uint32_t)cl);
+  const float4 S = *reinterpret_cast<const float4*>(smem + cx.sums_off + ((uint32_t)cl << 4));
+  const float corr = bias.x * S.x + bias.y * S.y + bias.z * S.z + bias.w * S.w;
+  const float xsum = (S.x + S.y) + (S.z + S.w);
   const float sc = *reinterpret_cast<const float*>(smem + cx.s_off + ((uint32_t)cl << 8) + 4 * lane);
   const uint32_t z = smem[cx.z_off + ((uint32_t)cl << 6) + lane];
   y1 += sc * ((v - corr) - (float)z * xsum);
@@ -565,10 +555,19 @@ __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockReg
 template <int B, typename AfterIssue>
 __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
                                          float& y1, AfterIssue&& after_issue) {
+  // this lane's unpack biases of k-steps 0..3 (row tile lane >> 4)
+  const int rt = (threadIdx.x & 63) >> 4;
+  auto pick = [rt](auto KTc) __attribute__((always_inline)) {
+    constexpr int kt = decltype(KTc)::value;
+    return rt == 0 ? exp_bias(B, kt)
+                   : (rt == 1 ? exp_bias(B, 4 + kt) : (rt == 2 ? exp_bias(B, 8 + kt) : exp_bias(B, 12 + kt)));
+  };
+  const float4 bias{pick(std::integral_constant<int, 0>{}), pick(std::integral_constant<int, 1>{}),
+                    pick(std::integral_constant<int, 2>{}), pick(std::integral_constant<int, 3>{})};
   ring_run<B, ring_depth<B>(), false>(
       cx, base, cols, n,
       [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
-        consume_m1<B>(cx, cl, br, y1);
+        consume_m1<B>(cx, cl, br, y1, bias);
       },
       after_issue);
 }
@@ -595,17 +594,14 @@ __device__ __forceinline__ void lds_copy4(const void* g, uint32_t off) {
 }
 #pragma clang diagnostic pop
 
-// LDS layout of k_gemv_m1 for ranges of ncl <= kmax block columns:
+// LDS layout of k_gemv_m1 for ranges of ncl <= kmax block columns (38 KB at
+// kmax = 64: four 8-wavefront workgroups fit a CU):
 //   [0, 256 kmax)             x slice, bf16
-//   [256 kmax, 336 kmax)      corr [kmax][20], f32
-//   [336 kmax, 340 kmax)      xsum [kmax], f32
-//   zero area of 256 bytes at the next 16-byte boundary
+//   [256 kmax, 272 kmax)      k-step sums [kmax][4], f32
+//   zero area of 256 bytes
 //   scales [ncl][64] f32, then zero points [ncl][64] u8, of the range's blocks
-__host__ __device__ constexpr size_t m1_corr_offset(int kmax) { return (size_t)kmax * 256; }
-__host__ __device__ constexpr size_t m1_xsum_offset(int kmax) { return (size_t)kmax * 336; }
-__host__ __device__ constexpr size_t m1_zero_offset(int kmax) {
-  return ((size_t)kmax * 340 + 15) & ~(size_t)15;
-}
+__host__ __device__ constexpr size_t m1_sums_offset(int kmax) { return (size_t)kmax * 256; }
+__host__ __device__ constexpr size_t m1_zero_offset(int kmax) { return (size_t)kmax * 272; }
 __host__ __device__ constexpr size_t m1_scale_offset(int kmax) { return m1_zero_offset(kmax) + 256; }
 __host__ __device__ constexpr size_t m1_lds_bytes(int kmax) {
   return m1_scale_offset(kmax) + (size_t)kmax * (256 + 64);
@@ -615,18 +611,15 @@ __host__ __device__ constexpr size_t m1_lds_bytes(int kmax) {
 // decode of one matrix.
 template <int NW>
 __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
-                                        const float* __restrict__ xsum_g,
-                                        const float* __restrict__ corr_g, const WeightView& w,
+                                        const float4* __restrict__ sums_g, const WeightView& w,
                                         int split, int kmax, float* __restrict__ part,
                                         float* __restrict__ y, uint32_t* __restrict__ counters,
                                         int blk) {
   constexpr int kThreads = NW * 64;
   constexpr int kUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // x slice loads per thread
-  constexpr int kCorr4 = kMaxCols * kCorrStride / 4;                 // float4s of the corr slice
-  constexpr int kCorrUnits = (kCorr4 + kThreads - 1) / kThreads;
+  constexpr int kSumsUnits = (kMaxCols + kThreads - 1) / kThreads;    // k-step sum float4s
   constexpr int kSUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // scale uint4s per thread
   constexpr int kZUnits = (kMaxCols * 4 + kThreads - 1) / kThreads;   // zero-point uint4s
-  constexpr int kSumUnits = (kMaxCols + kThreads - 1) / kThreads;     // group sums
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -634,7 +627,7 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const int c0 = sp * kmax;
   const int ncl = min(w.NBc, c0 + kmax) - c0;
   const int64_t rowbase = (int64_t)r * w.NBc + c0;
-  const size_t corr_off = m1_corr_offset(kmax), xsum_off = m1_xsum_offset(kmax);
+  const size_t sums_off = m1_sums_offset(kmax);
   const uint32_t zero_off = (uint32_t)m1_zero_offset(kmax);
 
   // First round trip: bit map and offsets (lane = column).
@@ -669,19 +662,13 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
     }
   };
   stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
-  stage16(corr_g + (int64_t)c0 * kCorrStride, corr_off, ncl * (kCorrStride / 4),
-          std::integral_constant<int, kCorrUnits>{});
+  stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
   stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
   stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
-#pragma unroll
-  for (int u = 0; u < kSumUnits; ++u) {
-    const int idx = t + u * kThreads;
-    if (idx < ncl) lds_copy4(xsum_g + c0 + idx, (uint32_t)xsum_off + 4 * (idx - lane));
-  }
   asm volatile("" ::: "memory");
 
   Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
-         (uint32_t)corr_off, (uint32_t)xsum_off, 0u, 0u};
+         (uint32_t)sums_off, 0u, 0u};
   cx.a_lane = (uint32_t)(16 * (lane >> 4));
   cx.zero_off = zero_off;
   cx.s_off = (uint32_t)s_off;
@@ -754,10 +741,9 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
-    const uint16_t* __restrict__ xg, const float* __restrict__ xsum_g,
-    const float* __restrict__ corr_g, WeightView w, int split, int kmax, float* __restrict__ part,
-    float* __restrict__ y, uint32_t* __restrict__ counters) {
-  gemv_m1<NW>(xg, xsum_g, corr_g, w, split, kmax, part, y, counters, blockIdx.x);
+    const uint16_t* __restrict__ xg, const float4* __restrict__ sums_g, WeightView w, int split,
+    int kmax, float* __restrict__ part, float* __restrict__ y, uint32_t* __restrict__ counters) {
+  gemv_m1<NW>(xg, sums_g, w, split, kmax, part, y, counters, blockIdx.x);
 }
 
 // ---- grouped M == 1 calls: up to kGroupMax matrices per launch ---------------------------
@@ -773,8 +759,7 @@ struct M1Job {
   WeightView w;
   const uint16_t* x;
   uint16_t* xg;
-  float* xsum;
-  float* corr;
+  float4* sums;
   float* part;
   float* y;
   uint32_t* counters;
@@ -808,7 +793,7 @@ __device__ __forceinline__ M1Job pick_job(const M1Group& g, int j) {
 
 __global__ __launch_bounds__(256) void k_prep_m1_group(M1Group g) {
   const M1Job q = pick_job(g, group_job(g, blockIdx.x, true));
-  prep_m1(q.x, q.w.K, q.w.perm_col, q.xg, q.xsum, q.corr, q.counters, q.ncounters,
+  prep_m1(q.x, q.w.K, q.w.perm_col, q.xg, q.sums, q.counters, q.ncounters,
           blockIdx.x - q.prep_begin);
 }
 
@@ -816,7 +801,7 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1_group(
     M1Group g) {
   const M1Job q = pick_job(g, group_job(g, blockIdx.x, false));
-  gemv_m1<NW>(q.xg, q.xsum, q.corr, q.w, q.split, q.kr, q.part, q.y, q.counters,
+  gemv_m1<NW>(q.xg, q.sums, q.w, q.split, q.kr, q.part, q.y, q.counters,
               blockIdx.x - q.wg_begin);
 }
 
@@ -871,15 +856,14 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
   y[m * N + orig_row(perm_row, n, N)] = v;
 }
 
-// Workspace layout of one call: [partials | xg | xsum | corr | counters],
-// each part 256-byte aligned; the partials only with several splits, the
-// last four only for M == 1.
+// Workspace layout of one call: [partials | xg | sums | counters] (M == 1)
+// or [partials | gather buffers] (M > 1), each part 256-byte aligned; the
+// partials only with several splits.
 struct GemvWorkspace {
   float* part;
   void* gather;  // M > 1: the gather kernel's x_r and split group sums
   uint16_t* xg;
-  float* xsum;
-  float* corr;
+  float4* sums;
   uint32_t* counters;
 };
 
@@ -891,8 +875,7 @@ size_t part_bytes(const GemvPlan& p, int64_t M, int64_t N) {
 
 size_t m1_prep_bytes(int64_t N, int64_t K) {
   const size_t nbc = (size_t)(K / kBlockCols), nbr = (size_t)(N / kBlockRows);
-  return align256((size_t)K * 2) + align256(nbc * 4) + align256(nbc * kCorrStride * 4) +
-         align256(nbr * 4);
+  return align256((size_t)K * 2) + align256(nbc * 16) + align256(nbr * 4);
 }
 
 GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K) {
@@ -905,10 +888,8 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
     const size_t nbc = (size_t)(K / kBlockCols);
     g.xg = reinterpret_cast<uint16_t*>(b);
     b += align256((size_t)K * 2);
-    g.xsum = reinterpret_cast<float*>(b);
-    b += align256(nbc * 4);
-    g.corr = reinterpret_cast<float*>(b);
-    b += align256(nbc * kCorrStride * 4);
+    g.sums = reinterpret_cast<float4*>(b);
+    b += align256(nbc * 16);
     g.counters = reinterpret_cast<uint32_t*>(b);
   }
   return g;
@@ -918,8 +899,8 @@ template <int NW>
 hipError_t launch_m1(const GemvWorkspace& g, const WeightView& w, float* y, const GemvPlan& p,
                      hipStream_t stream) {
   const unsigned grid = (unsigned)(w.NBr * p.split);
-  hipLaunchKernelGGL((k_gemv_m1<NW>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, g.xg, g.xsum,
-                     g.corr, w, p.split, p.kr, g.part, y, g.counters);
+  hipLaunchKernelGGL((k_gemv_m1<NW>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, g.xg, g.sums,
+                     w, p.split, p.kr, g.part, y, g.counters);
   return hipGetLastError();
 }
 
@@ -1031,8 +1012,7 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
     q.w = w[i];
     q.x = x[i];
     q.xg = gw.xg;
-    q.xsum = gw.xsum;
-    q.corr = gw.corr;
+    q.sums = gw.sums;
     q.part = gw.part;
     q.y = y[i];
     q.counters = gw.counters;
@@ -1070,7 +1050,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
     const int ncounters = p.split > 1 ? (int)w.NBr : 0;
     const int64_t grid = std::max<int64_t>((nbc + 3) / 4, (ncounters + 255) / 256);
     hipLaunchKernelGGL(k_prep_m1, dim3((unsigned)grid), dim3(256), 0, stream, x, w.K, w.perm_col,
-                       g.xg, g.xsum, g.corr, g.counters, ncounters);
+                       g.xg, g.sums, g.counters, ncounters);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.nw == 4) return launch_m1<4>(g, w, y, p, stream);
