@@ -465,8 +465,8 @@ def main() -> int:
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic,
-                "kernel": "msq_gemm M=1 on gate_proj 28672x8192: k_prep_m1 + k_gemv_m1 (one call, "
-                          "launch gaps included)",
+                "kernel": "msq_gemm M=1 on gate_proj 28672x8192: k_gemv_m1 reordering x in its "
+                          "workgroups (one launch per call, launch gaps included)",
                 "bytes_per_launch": per_launch, "avg_launch_us": round(launch_us, 3),
                 "kernel_sha": sha}
     log(f"roofline: {launch_us:.2f} us/launch, {achieved:.0f} GB/s")

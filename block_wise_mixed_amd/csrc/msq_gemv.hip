@@ -600,26 +600,42 @@ __device__ __forceinline__ void lds_copy4(const void* g, uint32_t off) {
 //   [256 kmax, 272 kmax)      k-step sums [kmax][4], f32
 //   zero area of 256 bytes
 //   scales [ncl][64] f32, then zero points [ncl][64] u8, of the range's blocks
+//   gathering workgroups only: the x row in original order, bf16 [128 kmax]
 __host__ __device__ constexpr size_t m1_sums_offset(int kmax) { return (size_t)kmax * 256; }
 __host__ __device__ constexpr size_t m1_zero_offset(int kmax) { return (size_t)kmax * 272; }
 __host__ __device__ constexpr size_t m1_scale_offset(int kmax) { return m1_zero_offset(kmax) + 256; }
 __host__ __device__ constexpr size_t m1_lds_bytes(int kmax) {
   return m1_scale_offset(kmax) + (size_t)kmax * (256 + 64);
 }
+__host__ __device__ constexpr size_t m1_xrow_offset(int kmax) { return m1_lds_bytes(kmax); }
+__host__ __device__ constexpr size_t m1_lds_bytes_gather(int kmax) {
+  return m1_xrow_offset(kmax) + (size_t)kmax * 256;
+}
 
 // Workgroup `blk` (block row blk / split, K range blk % split) of the M == 1
-// decode of one matrix.
-template <int NW>
+// decode of one matrix.  Two sources of the reordered x and its k-step sums:
+// the prep kernel's output (xg, sums_g), or, with `gather` set (one K range,
+// split == 1, so the workgroup needs all of x), x itself: the workgroup
+// copies the x row into LDS and reorders it there through perm_col while
+// its first code loads are in flight, so that no prep launch is needed.
+// Both give the same bits: the reordered values are copies, and the k-step
+// sums are formed by the same pairwise addition tree.
+template <int NW, bool kGather>
 __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
-                                        const float4* __restrict__ sums_g, const WeightView& w,
-                                        int split, int kmax, float* __restrict__ part,
-                                        float* __restrict__ y, uint32_t* __restrict__ counters,
-                                        int blk) {
+                                        const float4* __restrict__ sums_g,
+                                        const uint16_t* __restrict__ x,
+                                        const WeightView& w, int split, int kmax,
+                                        float* __restrict__ part, float* __restrict__ y,
+                                        uint32_t* __restrict__ counters, int blk) {
   constexpr int kThreads = NW * 64;
   constexpr int kUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // x slice loads per thread
   constexpr int kSumsUnits = (kMaxCols + kThreads - 1) / kThreads;    // k-step sum float4s
   constexpr int kSUnits = (kMaxCols * 16 + kThreads - 1) / kThreads;  // scale uint4s per thread
   constexpr int kZUnits = (kMaxCols * 4 + kThreads - 1) / kThreads;   // zero-point uint4s
+  // gathering: perm_col uint4s per thread (4 reordered columns each)
+  // (gathering needs at least 8 wavefronts: fewer would hold too many registers)
+  constexpr int kPermUnits = (kMaxCols * 32 + kThreads - 1) / kThreads;
+  static_assert(!kGather || kPermUnits <= 4, "gathering workgroups have at least 8 wavefronts");
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -630,10 +646,33 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const size_t sums_off = m1_sums_offset(kmax);
   const uint32_t zero_off = (uint32_t)m1_zero_offset(kmax);
 
+  // Gathering: the x row, straight into LDS, ahead of the first round trip
+  // (so the waits for the bit map below cover it too).
+  const int nperm = ncl * 32;  // uint4s of perm_col in the range (c0 == 0)
+  const size_t xrow_off = m1_xrow_offset(kmax);
+  if constexpr (kGather) {
+#pragma unroll
+    for (int u = 0; u < kUnits; ++u) {
+      const int idx = t + u * kThreads;
+      if (idx < ncl * 16)
+        lds_copy16(reinterpret_cast<const uint4*>(x) + idx, (uint32_t)xrow_off + 16 * (idx - lane));
+    }
+    asm volatile("" ::: "memory");
+  }
   // First round trip: bit map and offsets (lane = column).
   const int lc = min(lane, ncl - 1);
   const int blr = w.bits[rowbase + lc];
   const uint32_t ol = w.block_offset[rowbase + lc];
+  // Gathering: with them, this thread's perm_col entries (4 per unit; the
+  // loads are unconditional, past the end they repeat the last uint4, so
+  // every wavefront issues the same count).
+  uint4 pc[kGather ? kPermUnits : 1];
+  if constexpr (kGather) {
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < kPermUnits; ++u)
+      pc[u] = reinterpret_cast<const uint4*>(w.perm_col)[min(t + u * kThreads, nperm - 1)];
+  }
 
   const WaveRuns wr = wave_runs<NW>(lane < ncl ? blr : 0, wave, kWeightCostM1);
   uint32_t off[5];
@@ -649,9 +688,29 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const size_t s_off = m1_scale_offset(kmax);
   const size_t z_off = s_off + 256 * (size_t)ncl;  // the zero points follow the range's scales
   // the bit map and offsets have landed (the plan above used them): an
-  // explicit vmcnt(0) here tells the compiler so, and it then has no reason
-  // to wait for the copies below when it reuses those registers
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // explicit wait here tells the compiler so, and it then has no reason
+  // to wait for the copies below when it reuses those registers (gathering:
+  // all but the perm_col loads and the x row copies issued after them)
+  // Gathering: the perm_col entries, clamped into [0, K) and packed to 16
+  // bits (K <= 128 kMaxCols <= 65536), are parked in the x slice area, in
+  // the 8 bytes that the same thread later fills with the four reordered
+  // values, so that they hold no registers while the ring's loads are in
+  // flight.  This waits for their loads, issued with the bit map's (an
+  // explicit vmcnt(0), for the reason above: every load so far has landed).
+  if constexpr (kGather) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    const int kk = (int)w.K - 1;
+    static_assert(kBlockCols * kMaxCols <= 65536, "16-bit column indices");
+#pragma unroll
+    for (int u = 0; u < kPermUnits; ++u) {
+      const int i = t + u * kThreads;
+      const uint2 pk{(uint32_t)clampi((int)pc[u].x, kk) | ((uint32_t)clampi((int)pc[u].y, kk) << 16),
+                     (uint32_t)clampi((int)pc[u].z, kk) | ((uint32_t)clampi((int)pc[u].w, kk) << 16)};
+      if (i < nperm) *reinterpret_cast<uint2*>(smem + 8 * (size_t)i) = pk;
+    }
+  } else {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
   auto stage16 = [&](const void* g, size_t lds_off, int n, auto Units) __attribute__((always_inline)) {
     constexpr int kU = decltype(Units)::value;
 #pragma unroll
@@ -661,8 +720,10 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
         lds_copy16(reinterpret_cast<const uint4*>(g) + idx, (uint32_t)lds_off + 16 * (idx - lane));
     }
   };
-  stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
-  stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
+  if constexpr (!kGather) {
+    stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
+    stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
+  }
   stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
   stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
   asm volatile("" ::: "memory");
@@ -680,13 +741,39 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   // `issued`, which are that run's) and for its LDS stores.
   if (t < 64) reinterpret_cast<uint32_t*>(smem + zero_off)[t] = 0u;
   asm volatile("" ::: "memory");
-  auto startup = [](auto Issued) __attribute__((always_inline)) {
+  auto startup = [&](auto Issued) __attribute__((always_inline)) {
     constexpr int n = decltype(Issued)::value;
     static_assert(n < 64, "vmcnt range");
     // s_waitcnt vmcnt(n) expcnt(7) lgkmcnt(0); vmcnt is bits [3:0] and [15:14]
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if constexpr (kGather) {
+      // x row in LDS: reorder it into the x slice (xg[j] = x[perm_col[j]])
+      // and form the k-step sums.  Thread unit u holds reordered columns
+      // 4i .. 4i + 3 (i = t + u kThreads); eight consecutive units make a
+      // k-step of 32.  Pairwise tree: (x0 + x1) + (x2 + x3) per unit, then
+      // across the eight units by xor distance 1, 2, 4 (the prep kernel's
+      // tree over the same pairs).
+#pragma unroll
+      for (int u = 0; u < kPermUnits; ++u) {
+        const int i = t + u * kThreads;
+        const uint16_t* xrow = reinterpret_cast<const uint16_t*>(smem + xrow_off);
+        const uint2 pk = *reinterpret_cast<const uint2*>(smem + 8 * (size_t)min(i, nperm - 1));
+        const uint16_t u0 = xrow[pk.x & 0xFFFFu], u1 = xrow[pk.x >> 16];
+        const uint16_t u2 = xrow[pk.y & 0xFFFFu], u3 = xrow[pk.y >> 16];
+        float s = (bf16f(u0) + bf16f(u1)) + (bf16f(u2) + bf16f(u3));
+        s += __shfl_xor(s, 1, 64);
+        s += __shfl_xor(s, 2, 64);
+        s += __shfl_xor(s, 4, 64);
+        if (i < nperm) {
+          *reinterpret_cast<uint2*>(smem + 8 * (size_t)i) =
+              uint2{(uint32_t)u0 | ((uint32_t)u1 << 16), (uint32_t)u2 | ((uint32_t)u3 << 16)};
+          if ((t & 7) == 0) reinterpret_cast<float*>(smem + sums_off)[i >> 3] = s;
+        }
+      }
+      __syncthreads();
+    }
   };
   auto none = [](auto) __attribute__((always_inline)) {};
 
@@ -739,11 +826,12 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   y[orig_row(w.perm_row, row, w.N)] = tot;
 }
 
-template <int NW>
+template <int NW, bool kGather>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
-    const uint16_t* __restrict__ xg, const float4* __restrict__ sums_g, WeightView w, int split,
-    int kmax, float* __restrict__ part, float* __restrict__ y, uint32_t* __restrict__ counters) {
-  gemv_m1<NW>(xg, sums_g, w, split, kmax, part, y, counters, blockIdx.x);
+    const uint16_t* __restrict__ xg, const float4* __restrict__ sums_g,
+    const uint16_t* __restrict__ x, WeightView w, int split, int kmax, float* __restrict__ part,
+    float* __restrict__ y, uint32_t* __restrict__ counters) {
+  gemv_m1<NW, kGather>(xg, sums_g, x, w, split, kmax, part, y, counters, blockIdx.x);
 }
 
 // ---- grouped M == 1 calls: up to kGroupMax matrices per launch ---------------------------
@@ -764,6 +852,7 @@ struct M1Job {
   float* y;
   uint32_t* counters;
   int split, kr, ncounters;
+  int gather;  // the decode workgroups reorder x themselves (no prep workgroups)
   int prep_begin, wg_begin;
 };
 
@@ -801,8 +890,16 @@ template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1_group(
     M1Group g) {
   const M1Job q = pick_job(g, group_job(g, blockIdx.x, false));
-  gemv_m1<NW>(q.xg, q.sums, q.w, q.split, q.kr, q.part, q.y, q.counters,
-              blockIdx.x - q.wg_begin);
+  // the branch is uniform over the workgroup
+  if constexpr (NW >= 8) {
+    if (q.gather) {
+      gemv_m1<NW, true>(nullptr, nullptr, q.x, q.w, q.split, q.kr, q.part, q.y, q.counters,
+                        blockIdx.x - q.wg_begin);
+      return;
+    }
+  }
+  gemv_m1<NW, false>(q.xg, q.sums, nullptr, q.w, q.split, q.kr, q.part, q.y, q.counters,
+                     blockIdx.x - q.wg_begin);
 }
 
 // ======================================================================================
@@ -895,12 +992,33 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
   return g;
 }
 
+// M == 1 calls without a K split reorder x inside the decode workgroups
+// (no prep launch) when the wavefront count allows it; the boundary has
+// checked that x and perm_col are 16-byte aligned, as the gathering
+// workgroups read them.  MSQ_M1_GATHER=0 turns it off (tuning).
+bool m1_gathers(const GemvPlan& p) {
+  const char* v = std::getenv("MSQ_M1_GATHER");
+  const bool enabled = !(v && *v && std::atoi(v) == 0);
+  return enabled && p.split == 1 && p.nw >= 8;
+}
+
+size_t m1_launch_lds(const GemvPlan& p, bool gather) {
+  return gather ? m1_lds_bytes_gather(p.kr) : p.lds_bytes;
+}
+
 template <int NW>
-hipError_t launch_m1(const GemvWorkspace& g, const WeightView& w, float* y, const GemvPlan& p,
-                     hipStream_t stream) {
+hipError_t launch_m1(const GemvWorkspace& g, const uint16_t* x, bool gather, const WeightView& w,
+                     float* y, const GemvPlan& p, hipStream_t stream) {
   const unsigned grid = (unsigned)(w.NBr * p.split);
-  hipLaunchKernelGGL((k_gemv_m1<NW>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, g.xg, g.sums,
-                     w, p.split, p.kr, g.part, y, g.counters);
+  if constexpr (NW >= 8) {
+    if (gather) {
+      hipLaunchKernelGGL((k_gemv_m1<NW, true>), dim3(grid), dim3(NW * 64), m1_launch_lds(p, true),
+                         stream, nullptr, nullptr, x, w, p.split, p.kr, g.part, y, g.counters);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_gemv_m1<NW, false>), dim3(grid), dim3(NW * 64), m1_launch_lds(p, false),
+                     stream, g.xg, g.sums, nullptr, w, p.split, p.kr, g.part, y, g.counters);
   return hipGetLastError();
 }
 
@@ -1019,16 +1137,21 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
     q.split = p.split;
     q.kr = p.kr;
     q.ncounters = p.split > 1 ? (int)w[i].NBr : 0;
+    q.gather = m1_gathers(p) ? 1 : 0;
     q.prep_begin = prep_total;
     q.wg_begin = wg_total;
     const int64_t nbc = w[i].K / kBlockCols;
-    prep_total += (int)std::max<int64_t>((nbc + 3) / 4, (q.ncounters + 255) / 256);
+    if (!q.gather) prep_total += (int)std::max<int64_t>((nbc + 3) / 4, (q.ncounters + 255) / 256);
     wg_total += (int)(w[i].NBr * p.split);
-    lds = std::max(lds, p.lds_bytes);
+    lds = std::max(lds, m1_launch_lds(p, q.gather != 0));
   }
-  hipLaunchKernelGGL(k_prep_m1_group, dim3((unsigned)prep_total), dim3(256), 0, stream, g);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // prep workgroups only for the jobs that do not gather (a job with an
+  // empty range shares its begin with the next job, which group_job picks)
+  if (prep_total > 0) {
+    hipLaunchKernelGGL(k_prep_m1_group, dim3((unsigned)prep_total), dim3(256), 0, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (nw == 4)
     hipLaunchKernelGGL((k_gemv_m1_group<4>), dim3((unsigned)wg_total), dim3(256), lds, stream, g);
   else if (nw == 16)
@@ -1045,17 +1168,21 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
   float* dst = direct ? y : g.part;
   hipError_t e;
   if (M == 1) {
-    // the split counters are cleared here, only needed with several splits
-    const int64_t nbc = w.K / kBlockCols;
-    const int ncounters = p.split > 1 ? (int)w.NBr : 0;
-    const int64_t grid = std::max<int64_t>((nbc + 3) / 4, (ncounters + 255) / 256);
-    hipLaunchKernelGGL(k_prep_m1, dim3((unsigned)grid), dim3(256), 0, stream, x, w.K, w.perm_col,
-                       g.xg, g.sums, g.counters, ncounters);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (p.nw == 4) return launch_m1<4>(g, w, y, p, stream);
-    if (p.nw == 16) return launch_m1<16>(g, w, y, p, stream);
-    return launch_m1<8>(g, w, y, p, stream);
+    const bool gather = m1_gathers(p);
+    if (!gather) {
+      // x reordered once for all workgroups; the split counters are cleared
+      // here, only needed with several splits
+      const int64_t nbc = w.K / kBlockCols;
+      const int ncounters = p.split > 1 ? (int)w.NBr : 0;
+      const int64_t grid = std::max<int64_t>((nbc + 3) / 4, (ncounters + 255) / 256);
+      hipLaunchKernelGGL(k_prep_m1, dim3((unsigned)grid), dim3(256), 0, stream, x, w.K, w.perm_col,
+                         g.xg, g.sums, g.counters, ncounters);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (p.nw == 4) return launch_m1<4>(g, x, gather, w, y, p, stream);
+    if (p.nw == 16) return launch_m1<16>(g, x, gather, w, y, p, stream);
+    return launch_m1<8>(g, x, gather, w, y, p, stream);
   } else {
     // x reordered once per call, then staged slice by slice
     e = launch_gather_x(x, M, w, g.gather, stream);

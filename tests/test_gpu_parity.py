@@ -166,6 +166,60 @@ def test_decode_launch_shapes(msq, shape_cases, monkeypatch, name, split, waves)
         check_y(msq, pw, c, ref, 1)
 
 
+def _bf16_cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+@pytest.mark.parametrize("waves", [8, 16])
+@pytest.mark.parametrize("N,K,seed", [(256, 8192, 70), (192, 1024, 71), (64, 128, 72),
+                                      (320, 640, 73)])
+def test_decode_gather_matches_prep(msq, monkeypatch, N, K, seed, waves):
+    """M = 1 without a K split: the decode workgroups reorder x themselves (no prep
+    launch).  The result equals the prep-kernel path bit for bit (the reordered values
+    are copies and the k-step sums use the same addition tree) and the oracle within
+    tolerance; 64, 8, 1 and 5 block columns per row (ragged perm_col loads)."""
+    c = synth.random_case(N, K, seed, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")
+    monkeypatch.setenv("MSQ_GEMV_WAVES", str(waves))
+    x = _bf16_cuda(c.x(1))
+    monkeypatch.setenv("MSQ_M1_GATHER", "0")
+    y_prep = msq.gemm(x, pw)
+    monkeypatch.setenv("MSQ_M1_GATHER", "1")
+    y_gather = msq.gemm(x, pw)
+    y_again = msq.gemm(x, pw)
+    torch.cuda.synchronize()
+    assert torch.equal(y_gather, y_prep)
+    assert torch.equal(y_again, y_prep)
+    check_y(msq, pw, c, ref, 1)
+
+
+def test_group_decode_gather_mixed(msq, group_cases, monkeypatch):
+    """A grouped M = 1 call whose jobs split between gathering workgroups (one K range)
+    and the prep launch (a 16384-wide matrix needs two K ranges; placed first, in the
+    middle and last): every output equals its single call on the prep path bit for
+    bit, twice in a row, and the oracle within tolerance."""
+    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")
+    wide = synth.random_case(128, 16384, 74, dist=SMALL_DIST)
+    cases = list(group_cases) + [(wide,) + check_pack(msq, wide)]
+    xs_all = [_bf16_cuda(c.x(1)) for c, _, _ in cases]
+    for order in ((4, 0, 1, 2, 3), (0, 1, 4, 2, 3), (0, 1, 2, 3, 4)):
+        sel = [cases[i] for i in order]
+        xs = [xs_all[i] for i in order]
+        pws = [pw for _, pw, _ in sel]
+        _log(f"group decode, job order {order}")
+        for rep in range(2):
+            monkeypatch.setenv("MSQ_M1_GATHER", "1")
+            outs = msq.gemm_group(xs, pws)
+            monkeypatch.setenv("MSQ_M1_GATHER", "0")
+            singles = [msq.gemm(x, pw) for x, pw in zip(xs, pws)]
+            torch.cuda.synchronize()
+            for (c, _, _), y, s in zip(sel, outs, singles):
+                assert torch.equal(y, s), c.name
+    for c, pw, ref in cases:
+        check_y(msq, pw, c, ref, 1)
+
+
 @pytest.mark.parametrize("N,K,seed", [(192, 512, 0), (512, 4096, 1)])
 def test_integer_lattice_is_exact(msq, N, K, seed):
     c, xgen = synth.lattice_case(N, K, seed, dist={0: .1, 1: .2, 2: .2, 3: .2, 4: .2, 8: .1})
