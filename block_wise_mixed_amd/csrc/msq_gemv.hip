@@ -244,11 +244,15 @@ __device__ __forceinline__ void consume_block(const Ctx& cx, int cl, const Block
 }
 
 // Blocks per register ring of a B-bit run: (depth - 1) * B KiB of codes stay
-// in flight while one block is consumed.  More rows of M keep more
-// accumulators live, so their rings are shallower.
+// in flight while one block is consumed.  Thousands of wavefronts share
+// HBM, so shallow rings already keep more in flight than it needs; deeper
+// ones only lengthen the queues that every workgroup's start-up waits in
+// (M == 1 on a 70B layer: 4/2/2/2/2 blocks for 1/2/3/4/8 bits measured ~6%
+// faster than 8/4/3/3/2).  More rows of M keep more accumulators live, so
+// their rings are shallower still.
 template <int B, int MT = 1>
 constexpr int ring_depth() {
-  if constexpr (MT == 1) return B == 1 ? 8 : (B == 2 ? 4 : (B == 8 ? 2 : 3));
+  if constexpr (MT == 1) return B == 1 ? 4 : 2;
   else if constexpr (MT == 2) return B <= 4 ? 2 : 1;
   else return B <= 2 ? 2 : 1;
 }
@@ -258,11 +262,13 @@ constexpr int ring_depth() {
 // chunk; block i of the run starts B * i KiB later).  A ring of D register
 // sets with fixed roles: set j holds blocks j, j + D, j + 2D, ...; after
 // block i is consumed, the loads of block i + D go into its set.  Issues are
-// unconditional (past the end of the run they repeat its last block, which
-// is never consumed) and the loop runs whole passes over the ring with its
-// only exit at the end of a pass, so every consume sees the same loads
+// unconditional and the loop runs whole passes over the ring with its only
+// exit at the end of a pass, so every consume sees the same loads
 // outstanding in the same order and the wait counts stay static: D - 1
-// blocks in flight during each consume.  (An exit from the middle of the
+// blocks in flight during each consume.  Past the end of the run an issue
+// is a stand-in that is never consumed: the same loads with every lane's
+// address masked to the start of the codes (one cache line per load
+// instead of a KiB; no branch, so the loads keep their form).  (An exit from the middle of the
 // unrolled body leaves structurized control-flow paths on which the
 // compiler cannot bound the outstanding loads, and it then waits for all.)
 // kScaleZero: the ring also loads each block's scales and zero points (two
@@ -275,6 +281,11 @@ __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uin
   constexpr int64_t kStride = 1024 * B;
   BlockRegs<B> rs[D];
   int cs[D];
+  const int64_t lane_off = base - cx.codes;  // this lane's offset of the run's first block
+  // block bi of the run, or (live false) the stand-in address
+  auto slot = [&](bool live, int bi) __attribute__((always_inline)) {
+    return cx.codes + ((lane_off + (int64_t)bi * kStride) & -(int64_t)live);
+  };
   // compiler-only barriers after the issues keep the loads where they are
   // written (the compiler would otherwise sink them toward their first use)
 #pragma unroll
@@ -285,9 +296,9 @@ __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uin
     } else {
       cs[j] = cs[j - 1];
     }
-    int bi = __builtin_amdgcn_readfirstlane(j < n ? j : n - 1);
+    int bi = __builtin_amdgcn_readfirstlane(j);
     asm("" : "+s"(bi));
-    issue_block<B, kScaleZero>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+    issue_block<B, kScaleZero>(cx, slot(j < n, bi), cs[j], rs[j]);
     asm volatile("" ::: "memory");
   }
   // the first run: the workgroup's start-up, while these loads fly
@@ -302,9 +313,9 @@ __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uin
         cs[j] = __builtin_amdgcn_readfirstlane(__builtin_ctzll(cols));
         cols &= cols - 1;
       }
-      int bi = __builtin_amdgcn_readfirstlane(nx < n ? nx : n - 1);
+      int bi = __builtin_amdgcn_readfirstlane(nx);
       asm("" : "+s"(bi));
-      issue_block<B, kScaleZero>(cx, base + (int64_t)bi * kStride, cs[j], rs[j]);
+      issue_block<B, kScaleZero>(cx, slot(nx < n, bi), cs[j], rs[j]);
       asm volatile("" ::: "memory");
     }
     i0 += D;
