@@ -652,11 +652,12 @@ __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_
 // leaves every 64-byte line of y partly written by many workgroups, and the
 // partial lines reach HBM many times over (about 9x the bytes of y).  So the
 // tiles write y in reordered order into y itself, and one workgroup per row
-// then reads the whole row into registers and writes it back permuted, each
-// line completed by one workgroup while it sits in L2.
+// then permutes the row through LDS: coalesced reads of the row (and of
+// perm_row, which stays in L2 across rows), the scatter as LDS stores, and
+// coalesced writes of the permuted row back in place.
 constexpr int kUnpermuteThreads = 1024;
-constexpr int kUnpermutePer = 32;
-constexpr int64_t kUnpermuteMaxN = (int64_t)kUnpermutePer * kUnpermuteThreads;
+constexpr int kUnpermuteBatch = 8;  // loads in flight per thread
+constexpr int64_t kUnpermuteMaxN = 32768;  // the row in LDS: 128 KiB
 
 struct UnpermuteJob {
   float* y;
@@ -668,26 +669,32 @@ struct UnpermuteGroup {
   int count;
 };
 
-// Row blockIdx.x of job blockIdx.y (N <= kUnpermuteMaxN): y[perm_row[n]] = y[n].
+// Row blockIdx.x of job blockIdx.y (N <= kUnpermuteMaxN, dynamic LDS of at
+// least 4 N bytes): y[perm_row[n]] = y[n].
 __global__ __launch_bounds__(kUnpermuteThreads) void k_unpermute_rows(UnpermuteGroup g) {
   UnpermuteJob q = g.job[0];
 #pragma unroll
   for (int k = 1; k < kGroupMax; ++k)
     if (k == (int)blockIdx.y) q = g.job[k];
   float* row = q.y + (int64_t)blockIdx.x * q.N;
+  float* lrow = reinterpret_cast<float*>(smem);
+  const int N = (int)q.N;
   const int t = threadIdx.x;
-  float v[kUnpermutePer];
-  int dst[kUnpermutePer];
+  for (int base = t; base < N; base += kUnpermuteBatch * kUnpermuteThreads) {
+    float v[kUnpermuteBatch];
+    int dst[kUnpermuteBatch];
 #pragma unroll
-  for (int i = 0; i < kUnpermutePer; ++i) {
-    const int64_t n = min((int64_t)t + (int64_t)i * kUnpermuteThreads, q.N - 1);
-    v[i] = row[n];
-    dst[i] = min(max(q.perm_row[n], 0), (int)q.N - 1);
+    for (int i = 0; i < kUnpermuteBatch; ++i) {
+      const int n = min(base + i * kUnpermuteThreads, N - 1);
+      v[i] = row[n];
+      dst[i] = min(max(q.perm_row[n], 0), N - 1);
+    }
+#pragma unroll
+    for (int i = 0; i < kUnpermuteBatch; ++i)
+      if (base + i * kUnpermuteThreads < N) lrow[dst[i]] = v[i];
   }
-  __syncthreads();  // the whole row is read before any of it is overwritten
-#pragma unroll
-  for (int i = 0; i < kUnpermutePer; ++i)
-    if ((int64_t)t + (int64_t)i * kUnpermuteThreads < q.N) row[dst[i]] = v[i];
+  __syncthreads();  // the whole row is read (and scattered) before any of it is overwritten
+  for (int n = t; n < N; n += kUnpermuteThreads) row[n] = lrow[n];
 }
 
 // Block rows per workgroup of the prefill GEMM (MSQ_GEMM_BR=2 or 4 overrides).
@@ -792,11 +799,15 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   UnpermuteGroup u{};
+  int64_t maxn = 0;
   for (int i = 0; i < count; ++i)
-    if (g.job[i].yr) u.job[u.count++] = UnpermuteJob{y[i], w[i].perm_row, w[i].N};
+    if (g.job[i].yr) {
+      u.job[u.count++] = UnpermuteJob{y[i], w[i].perm_row, w[i].N};
+      maxn = std::max(maxn, w[i].N);
+    }
   if (u.count == 0) return hipSuccess;
   hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, (unsigned)u.count), dim3(kUnpermuteThreads),
-                     0, stream, u);
+                     (size_t)maxn * 4, stream, u);
   return hipGetLastError();
 }
 
@@ -854,7 +865,8 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
   UnpermuteGroup u{};
   u.job[0] = UnpermuteJob{y, w.perm_row, w.N};
   u.count = 1;
-  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, 1u), dim3(kUnpermuteThreads), 0, stream, u);
+  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, 1u), dim3(kUnpermuteThreads),
+                     (size_t)w.N * 4, stream, u);
   return hipGetLastError();
 }
 

@@ -917,13 +917,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 // K-split reduction
 // ======================================================================================
 
-// Row blockIdx.x of the same sum, one workgroup per row.
+// Row blockIdx.x of the same sum, one workgroup per row.  kLds: the row is
+// permuted through LDS (4 N bytes of dynamic LDS) and written back with
+// coalesced stores; otherwise each sum is stored at its original column.
 constexpr int kReduceRowThreads = 1024;
+constexpr int64_t kReduceRowMaxLdsN = 32768;
+template <bool kLds>
 __global__ __launch_bounds__(kReduceRowThreads) void k_gemv_reduce_rows(
     const float* __restrict__ part, int split, int M, int64_t N, const int32_t* __restrict__ perm_row,
     float* __restrict__ y) {
   const int64_t m = blockIdx.x;
   const int64_t plane = (int64_t)M * N;
+  float* lrow = reinterpret_cast<float*>(smem);
   for (int64_t n = threadIdx.x; n < N; n += kReduceRowThreads) {
     const float* p = part + m * N + n;
     float v = 0.f;
@@ -936,7 +941,14 @@ __global__ __launch_bounds__(kReduceRowThreads) void k_gemv_reduce_rows(
       for (int k = 0; k < 8; ++k) v += t[k];
     }
     for (; sp < split; ++sp) v += p[sp * plane];
-    y[m * N + orig_row(perm_row, n, N)] = v;
+    if constexpr (kLds)
+      lrow[orig_row(perm_row, n, N)] = v;
+    else
+      y[m * N + orig_row(perm_row, n, N)] = v;
+  }
+  if constexpr (kLds) {
+    __syncthreads();
+    for (int64_t n = threadIdx.x; n < N; n += kReduceRowThreads) y[m * N + n] = lrow[n];
   }
 }
 
@@ -1222,8 +1234,12 @@ hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t 
     // of the row is completed by one workgroup while it sits in L2
     // (workgroups sharing a row would each leave it partly written, and
     // partial lines reach HBM many times over)
-    hipLaunchKernelGGL(k_gemv_reduce_rows, dim3((unsigned)M), dim3(kReduceRowThreads), 0, stream,
-                       part, split, (int)M, N, perm_row, y);
+    if (N <= kReduceRowMaxLdsN)
+      hipLaunchKernelGGL(k_gemv_reduce_rows<true>, dim3((unsigned)M), dim3(kReduceRowThreads),
+                         (size_t)N * 4, stream, part, split, (int)M, N, perm_row, y);
+    else
+      hipLaunchKernelGGL(k_gemv_reduce_rows<false>, dim3((unsigned)M), dim3(kReduceRowThreads), 0,
+                         stream, part, split, (int)M, N, perm_row, y);
     return hipGetLastError();
   }
   const int64_t total = M * N;
