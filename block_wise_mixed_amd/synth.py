@@ -215,3 +215,20 @@ def lattice_case(N: int, K: int, seed: int, dist: Dict[int, float] | None = None
         return f32_to_bf16_bits(gx.integers(-x_range, x_range + 1, size=(M, K)).astype(np.float32))
 
     return mi, xgen
+
+
+# ---- synthetic block scores for the bit allocation --------------------------------------
+
+ALLOC_LEVELS = (0, 1, 2, 3, 4, 8)
+
+
+def draw_alloc_utility(n_blocks: int, seed: int, sigma: float = 1.5,
+                       lo: float = 1e-3, hi: float = 1e3) -> np.ndarray:
+    """Per-block utilities u[i][l] (fp32, [n_blocks][6]) for bitwidths 0, 1, 2, 3, 4, 8:
+    u = -w_i * 4^-b, the expected squared RTN error of a block whose sensitivity w_i
+    is log-normal (clipped to [lo, hi]); the error falls 4x per added bit.  A
+    stand-in for the pages' first-order sensitivities, which need trained weights."""
+    g = np.random.default_rng([0xA110C, seed])
+    w = np.clip(np.exp(g.normal(0.0, sigma, n_blocks)), lo, hi)
+    b = np.asarray(ALLOC_LEVELS, dtype=np.float64)
+    return (-w[:, None] * np.power(4.0, -b)[None, :]).astype(np.float32)
