@@ -222,6 +222,31 @@ def achievable_context(torch, dev, log):
     return res
 
 
+def alloc_leg(msq, synth, torch, log):
+    """Bitwidth allocation (batched greedy) for every block of a Llama-3-70B-shaped
+    model (80 layers of the seven linears: 8355840 blocks of 64x128) at an average
+    of 2.1 bits, on synthetic utilities; wall time of msq_allocate_bits, which
+    synchronises with the host after every iteration."""
+    blocks = 80 * (2 * 8192 * 8192 + 2 * 1024 * 8192 + 3 * 28672 * 8192) // (64 * 128)
+    u = torch.from_numpy(synth.draw_alloc_utility(blocks, 70)).cuda()
+    budget = int(2.1 * blocks)
+    ws = torch.empty(msq.alloc_workspace_bytes(blocks), dtype=torch.uint8, device=u.device)
+    msq.allocate_bits(u, budget, workspace=ws)
+    torch.cuda.synchronize()
+    times, iters = [], 0
+    for _ in range(3):
+        t0 = time.perf_counter()
+        bits, iters = msq.allocate_bits(u, budget, workspace=ws)
+        times.append(time.perf_counter() - t0)
+    ms = 1e3 * sorted(times)[1]
+    mean_bits = float(bits.double().mean())
+    log(f"alloc: {blocks} blocks, {iters} iterations, {ms:.1f} ms, mean {mean_bits:.4f} bits")
+    del u, ws, bits
+    return {"blocks": blocks, "budget_mean_bits": 2.1, "mean_bits": round(mean_bits, 4),
+            "iterations": iters, "ms": round(ms, 2),
+            "note": "batched greedy over a 70B model's blocks, synthetic utilities; median of 3"}
+
+
 def cpu_baseline(inputs, target_s: float = 12.0):
     """The oracle decoding a sample of block rows of every linear (M = 1).
 
@@ -521,6 +546,8 @@ def main() -> int:
             "gbps_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1),
             "note": "host-side descriptor validation included"}
 
+    alloc = alloc_leg(msq, synth, torch, log)
+
     configs, context = None, None
     if not args.no_configs:
         del copies
@@ -548,6 +575,7 @@ def main() -> int:
         "decode_separate_calls": decode_single,
         "prefill": prefill,
         "pack": pack,
+        "alloc": alloc,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "configs": configs,

@@ -24,7 +24,8 @@ import numpy as np
 
 __all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspace_bytes",
            "gemm_group", "group_workspace_bytes", "GROUP_MAX",
-           "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M"]
+           "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M",
+           "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS"]
 
 FORMAT_VERSION = 1
 GEMV_MAX_M = 64
@@ -86,6 +87,10 @@ def load_library():
     lib.msq_gemm_group.argtypes = [ctypes.POINTER(vp), i64, ctypes.POINTER(ctypes.POINTER(_Weight)),
                                    ctypes.POINTER(vp), ctypes.c_int, vp, sz, vp]
     lib.msq_gemm_group.restype = ctypes.c_int
+    lib.msq_alloc_workspace_bytes.argtypes = [i64]
+    lib.msq_alloc_workspace_bytes.restype = sz
+    lib.msq_allocate_bits.argtypes = [vp, i64, i64, vp, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.msq_allocate_bits.restype = ctypes.c_int
     lib.msq_status_string.argtypes = [ctypes.c_int]
     lib.msq_status_string.restype = ctypes.c_char_p
     lib.msq_format_version.argtypes = []
@@ -294,3 +299,32 @@ def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, st
                            out.data_ptr() if M > 0 else None, ws_ptr, workspace.numel(),
                            KERNELS[kernel], _stream_handle(stream)), "msq_gemm")
     return out
+
+
+ALLOC_LEVELS = (0, 1, 2, 3, 4, 8)
+
+
+def alloc_workspace_bytes(n_blocks: int) -> int:
+    return int(load_library().msq_alloc_workspace_bytes(int(n_blocks)))
+
+
+def allocate_bits(utility, budget_bits: int, workspace=None, stream=None):
+    """Bitwidth per block under a budget (msq_allocate_bits).  utility: fp32
+    [n_blocks][6] for bitwidths ALLOC_LEVELS (numpy or torch).  Returns (bits as a
+    uint8 device tensor [n_blocks], batched iterations)."""
+    torch = _torch()
+    lib = load_library()
+    u = torch.as_tensor(utility)
+    if u.dtype != torch.float32 or u.dim() != 2 or u.shape[1] != len(ALLOC_LEVELS):
+        raise ValueError("utility must be float32 [n_blocks][6]")
+    u = u.to("cuda").contiguous()
+    n = int(u.shape[0])
+    bits = torch.empty(n, dtype=torch.uint8, device=u.device)
+    need = alloc_workspace_bytes(n)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=u.device)
+    iters = ctypes.c_int32(0)
+    _check(lib.msq_allocate_bits(u.data_ptr(), n, int(budget_bits), bits.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), ctypes.byref(iters),
+                                 _stream_handle(stream)), "msq_allocate_bits")
+    return bits, int(iters.value)

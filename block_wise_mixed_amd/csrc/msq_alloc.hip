@@ -1,0 +1,279 @@
+// Bitwidth allocation per 64x128 block under a memory budget: the batched
+// greedy knapsack ("ScaleBITS" summary page, sections Approach and Key
+// results: a batched approximation to classic greedy, 16 to 36 iterations).
+//
+// Every iteration, for every block that can still move up a level:
+//   k_alloc_keys   the cost d of its next step and the fp32 ratio
+//                  (u[l+1] - u[l]) / d as an order-preserving 32-bit key;
+//   radix sort     keys descending with the block index as value (the sort is
+//                  stable, so equal ratios keep ascending block order);
+//   k_alloc_costs  the step costs in sorted order, then an inclusive scan;
+//   k_alloc_select the longest sorted prefix whose cost is at most half the
+//                  remaining budget R (binary search over the scan), or, when
+//                  that is empty, the first sorted step that fits R (min
+//                  reduction); R and the iteration's status updated on the
+//                  device;
+//   k_alloc_apply  the chosen blocks move up one level.
+// The host reads the status back after each iteration and stops when an
+// iteration takes nothing.  Blocks that cannot move (already at 8 bits) get
+// key 0 and cost 0: they sort after every real step and are never moved.
+#include <hip/hip_runtime.h>
+#include <hipcub/hipcub.hpp>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "msq.h"
+
+namespace msq {
+namespace {
+
+constexpr int kLevels = 6;
+__constant__ int kLevelBits[kLevels] = {0, 1, 2, 3, 4, 8};
+
+struct AllocStatus {
+  int64_t remaining;  // budget left, bits
+  int64_t taken;      // bits spent by the last iteration
+  int32_t count;      // sorted positions [0, count) move up (count = -1: none)
+  int32_t single;     // or just this sorted position (-1: none)
+};
+
+// IEEE float -> uint32 with the same order (no NaNs: the inputs are checked).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0: equal ratios get equal keys
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__global__ __launch_bounds__(256) void k_alloc_init(uint8_t* __restrict__ lev, int64_t n,
+                                                    AllocStatus* st, int64_t budget) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) lev[i] = 0;
+  if (i == 0) *st = AllocStatus{budget, 0, 0, -1};
+}
+
+__global__ __launch_bounds__(256) void k_alloc_keys(const float* __restrict__ u,
+                                                    const uint8_t* __restrict__ lev, int64_t n,
+                                                    uint32_t* __restrict__ key,
+                                                    int32_t* __restrict__ idx,
+                                                    int32_t* __restrict__ cost) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int l = lev[i];
+  uint32_t k = 0u;
+  int d = 0;
+  if (l < kLevels - 1) {
+    d = kLevelBits[l + 1] - kLevelBits[l];
+    const float gain = u[i * kLevels + l + 1] - u[i * kLevels + l];
+    k = order_key(gain / (float)d);
+  }
+  key[i] = k;
+  idx[i] = (int32_t)i;
+  cost[i] = d;
+}
+
+__global__ __launch_bounds__(256) void k_alloc_costs(const int32_t* __restrict__ sorted_idx,
+                                                     const int32_t* __restrict__ cost, int64_t n,
+                                                     int32_t* __restrict__ sorted_cost) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p < n) sorted_cost[p] = cost[sorted_idx[p]];
+}
+
+constexpr int kSelectThreads = 1024;
+
+__global__ __launch_bounds__(kSelectThreads) void k_alloc_select(
+    const int32_t* __restrict__ scan, const int32_t* __restrict__ sorted_cost, int64_t n,
+    AllocStatus* st) {
+  __shared__ int32_t s_count;
+  __shared__ int32_t s_first[kSelectThreads / 64];
+  const int64_t R = st->remaining;
+  const int64_t half = R / 2;
+  if (threadIdx.x == 0) {
+    // scan is non-decreasing: count = number of positions with scan <= half
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if ((int64_t)scan[mid] <= half) lo = mid + 1; else hi = mid;
+    }
+    s_count = (int32_t)lo;
+  }
+  __syncthreads();
+  const int32_t count = s_count;
+  // a prefix of only blocks that cannot move takes nothing
+  const int64_t prefix_bits = count > 0 ? (int64_t)scan[count - 1] : 0;
+  if (prefix_bits > 0) {
+    if (threadIdx.x == 0) {
+      st->remaining = R - prefix_bits;
+      st->taken = prefix_bits;
+      st->count = count;
+      st->single = -1;
+    }
+    return;
+  }
+  // first sorted step that fits R
+  int32_t first = INT32_MAX;
+  for (int64_t p = threadIdx.x; p < n; p += kSelectThreads) {
+    const int32_t d = sorted_cost[p];
+    if (d > 0 && d <= R) {
+      first = (int32_t)p;
+      break;
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
+  if ((threadIdx.x & 63) == 0) s_first[threadIdx.x >> 6] = first;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t f = INT32_MAX;
+    for (int k = 0; k < kSelectThreads / 64; ++k) f = min(f, s_first[k]);
+    if (f == INT32_MAX) {
+      st->taken = 0;
+      st->count = -1;
+      st->single = -1;
+    } else {
+      const int32_t d = sorted_cost[f];
+      st->remaining = R - d;
+      st->taken = d;
+      st->count = -1;
+      st->single = f;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_alloc_apply(const int32_t* __restrict__ sorted_idx,
+                                                     const int32_t* __restrict__ sorted_cost,
+                                                     int64_t n, const AllocStatus* st,
+                                                     uint8_t* __restrict__ lev) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= n) return;
+  const bool move = p < st->count || p == st->single;
+  if (move && sorted_cost[p] > 0) lev[sorted_idx[p]] += 1;
+}
+
+__global__ __launch_bounds__(256) void k_alloc_bits(const uint8_t* __restrict__ lev, int64_t n,
+                                                    uint8_t* __restrict__ bits) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) bits[i] = (uint8_t)kLevelBits[lev[i]];
+}
+
+// Finite utilities only: a NaN has no place in the order.
+__global__ __launch_bounds__(256) void k_alloc_check(const float* __restrict__ u, int64_t total,
+                                                     int32_t* __restrict__ bad) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < total && !isfinite(u[i])) atomicOr(bad, 1);
+}
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct AllocLayout {
+  size_t key_in, key_out, idx_in, idx_out, cost, sorted_cost, scan, lev, status, bad, temp,
+      temp_bytes, total;
+};
+
+AllocLayout alloc_layout(int64_t n) {
+  AllocLayout L{};
+  size_t sort_temp = 0, scan_temp = 0;
+  hipcub::DeviceRadixSort::SortPairsDescending(nullptr, sort_temp, (const uint32_t*)nullptr,
+                                               (uint32_t*)nullptr, (const int32_t*)nullptr,
+                                               (int32_t*)nullptr, (int)n);
+  hipcub::DeviceScan::InclusiveSum(nullptr, scan_temp, (const int32_t*)nullptr, (int32_t*)nullptr,
+                                   (int)n);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.key_in = take(4 * (size_t)n);
+  L.key_out = take(4 * (size_t)n);
+  L.idx_in = take(4 * (size_t)n);
+  L.idx_out = take(4 * (size_t)n);
+  L.cost = take(4 * (size_t)n);
+  L.sorted_cost = take(4 * (size_t)n);
+  L.scan = take(4 * (size_t)n);
+  L.lev = take((size_t)n);
+  L.status = take(sizeof(AllocStatus));
+  L.bad = take(4);
+  L.temp_bytes = std::max(sort_temp, scan_temp);
+  L.temp = take(L.temp_bytes);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+}  // namespace msq
+
+using namespace msq;
+
+extern "C" size_t msq_alloc_workspace_bytes(int64_t n_blocks) {
+  if (n_blocks <= 0 || n_blocks > MSQ_ALLOC_MAX_BLOCKS) return 0;
+  return alloc_layout(n_blocks).total;
+}
+
+extern "C" msq_status msq_allocate_bits(const float* utility, int64_t n_blocks, int64_t budget_bits,
+                                        uint8_t* bits, void* workspace, size_t workspace_bytes,
+                                        int32_t* iterations, hipStream_t stream) {
+  if (!utility || !bits || !workspace || (reinterpret_cast<uintptr_t>(utility) & 3) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255))
+    return MSQ_ERR_INVALID_ARG;
+  if (n_blocks <= 0 || n_blocks > MSQ_ALLOC_MAX_BLOCKS || budget_bits < 0) return MSQ_ERR_SHAPE;
+  const AllocLayout L = alloc_layout(n_blocks);
+  if (workspace_bytes < L.total) return MSQ_ERR_BUFFER_TOO_SMALL;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  auto at = [&](size_t off) { return ws + off; };
+  uint32_t* key_in = reinterpret_cast<uint32_t*>(at(L.key_in));
+  uint32_t* key_out = reinterpret_cast<uint32_t*>(at(L.key_out));
+  int32_t* idx_in = reinterpret_cast<int32_t*>(at(L.idx_in));
+  int32_t* idx_out = reinterpret_cast<int32_t*>(at(L.idx_out));
+  int32_t* cost = reinterpret_cast<int32_t*>(at(L.cost));
+  int32_t* sorted_cost = reinterpret_cast<int32_t*>(at(L.sorted_cost));
+  int32_t* scan = reinterpret_cast<int32_t*>(at(L.scan));
+  uint8_t* lev = at(L.lev);
+  AllocStatus* st = reinterpret_cast<AllocStatus*>(at(L.status));
+  int32_t* bad = reinterpret_cast<int32_t*>(at(L.bad));
+  void* temp = at(L.temp);
+  const int n = (int)n_blocks;
+  const unsigned grid = (unsigned)((n_blocks + 255) / 256);
+  const int64_t total = n_blocks * kLevels;
+
+  // utilities must be finite
+  int32_t h_bad = 0;
+  if (hipMemcpyAsync(bad, &h_bad, 4, hipMemcpyHostToDevice, stream) != hipSuccess)
+    return MSQ_ERR_HIP;
+  hipLaunchKernelGGL(k_alloc_check, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     utility, total, bad);
+  if (hipMemcpyAsync(&h_bad, bad, 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MSQ_ERR_HIP;
+  if (h_bad) return MSQ_ERR_INVALID_ARG;
+
+  hipLaunchKernelGGL(k_alloc_init, dim3(grid), dim3(256), 0, stream, lev, n_blocks, st, budget_bits);
+  int32_t iters = 0;
+  // every iteration moves at least one block up a level: at most 5 n iterations
+  for (int64_t guard = 0; guard <= 5 * n_blocks; ++guard) {
+    hipLaunchKernelGGL(k_alloc_keys, dim3(grid), dim3(256), 0, stream, utility, lev, n_blocks,
+                       key_in, idx_in, cost);
+    size_t tb = L.temp_bytes;
+    if (hipcub::DeviceRadixSort::SortPairsDescending(temp, tb, key_in, key_out, idx_in, idx_out, n,
+                                                     0, 32, stream) != hipSuccess)
+      return MSQ_ERR_HIP;
+    hipLaunchKernelGGL(k_alloc_costs, dim3(grid), dim3(256), 0, stream, idx_out, cost, n_blocks,
+                       sorted_cost);
+    tb = L.temp_bytes;
+    if (hipcub::DeviceScan::InclusiveSum(temp, tb, sorted_cost, scan, n, stream) != hipSuccess)
+      return MSQ_ERR_HIP;
+    hipLaunchKernelGGL(k_alloc_select, dim3(1), dim3(kSelectThreads), 0, stream, scan, sorted_cost,
+                       n_blocks, st);
+    hipLaunchKernelGGL(k_alloc_apply, dim3(grid), dim3(256), 0, stream, idx_out, sorted_cost,
+                       n_blocks, st, lev);
+    AllocStatus h{};
+    if (hipGetLastError() != hipSuccess ||
+        hipMemcpyAsync(&h, st, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return MSQ_ERR_HIP;
+    if (h.taken == 0) break;
+    ++iters;
+  }
+  hipLaunchKernelGGL(k_alloc_bits, dim3(grid), dim3(256), 0, stream, lev, n_blocks, bits);
+  if (hipGetLastError() != hipSuccess) return MSQ_ERR_HIP;
+  if (iterations) *iterations = iters;
+  return MSQ_OK;
+}

@@ -225,6 +225,37 @@ msq_status msq_gemm_group(const uint16_t *const *x_bf16, int64_t M,
                           const msq_weight *const *w, float *const *y, int count,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* ---- bitwidth allocation under a memory budget ---------------------------
+ * Chooses a bitwidth per 64x128 block, from {0, 1, 2, 3, 4, 8}, so as to
+ * maximise the sum of per-block utilities with the sum of the chosen bits at
+ * most the budget: the knapsack over block bitwidths that the ScaleBITS
+ * summary page (sections Approach and Key results) solves with a batched
+ * approximation to greedy.  The pages give no batching rule; this library's
+ * reading: each iteration orders every block's next one-level step by fp32
+ * ratio (u[l+1] - u[l]) / (bits[l+1] - bits[l]) descending, ties by block
+ * index ascending, and moves up the longest prefix of that order whose cost
+ * is at most floor(R / 2) of the remaining budget R, or, when that prefix is
+ * empty, the first step that fits R; it stops when no step fits.  All
+ * blocks start at 0 bits.
+ *
+ * utility: device fp32 [n_blocks][6] (levels 0, 1, 2, 3, 4, 8 bits), finite,
+ *   4-byte aligned; read only.  bits: device uint8 [n_blocks], written.
+ * budget_bits: sum over blocks of the allowed bits per weight (for an average
+ *   of b bits, floor(b * n_blocks)); counts codes only.
+ * workspace: device, 256-byte aligned, at least msq_alloc_workspace_bytes.
+ * iterations: host int32 receiving the number of batched iterations; may be
+ *   NULL.
+ * Blocking: the host reads a small status back after every iteration and
+ *   returns when the allocation is written (stream synchronised).
+ * Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer, a non-finite
+ *   utility), MSQ_ERR_SHAPE (n_blocks outside [1, MSQ_ALLOC_MAX_BLOCKS] or a
+ *   negative budget), MSQ_ERR_BUFFER_TOO_SMALL, MSQ_ERR_HIP. */
+#define MSQ_ALLOC_MAX_BLOCKS (1 << 28)
+size_t msq_alloc_workspace_bytes(int64_t n_blocks);
+msq_status msq_allocate_bits(const float *utility, int64_t n_blocks, int64_t budget_bits,
+                             uint8_t *bits, void *workspace, size_t workspace_bytes,
+                             int32_t *iterations, hipStream_t stream);
+
 /* Static English text for a status code; never NULL. */
 const char *msq_status_string(msq_status status);
 

@@ -200,3 +200,22 @@ def test_group_workspace_sizes(lib):
     assert lib.msq_gemm_group_workspace_bytes(0, arr, 3) == 0
     assert lib.msq_gemm_group_workspace_bytes(1, arr, 0) == 0
     assert lib.msq_gemm_group_workspace_bytes(1, arr, 9) == 0
+
+
+def test_alloc_host_checks(lib):
+    """Bit allocation: workspace sizing and argument checks, before any GPU work."""
+    import ctypes
+    lib.msq_alloc_workspace_bytes.restype = ctypes.c_size_t
+    lib.msq_alloc_workspace_bytes.argtypes = [ctypes.c_int64]
+    assert lib.msq_alloc_workspace_bytes(0) == 0
+    assert lib.msq_alloc_workspace_bytes((1 << 28) + 1) == 0
+    assert lib.msq_alloc_workspace_bytes(1000) >= 7 * 4 * 1000 + 1000
+    f = lib.msq_allocate_bits
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, 10, 5, None, None, 0, None, None) == 1          # null pointers
+    assert f(256, 10, 5, 256, 257, 1 << 20, None, None) == 1       # misaligned workspace
+    assert f(256, 0, 5, 256, 256, 1 << 20, None, None) == 2        # no blocks
+    assert f(256, 10, -1, 256, 256, 1 << 20, None, None) == 2      # negative budget
+    assert f(256, 10, 5, 256, 256, 16, None, None) == 5            # workspace too small
