@@ -232,3 +232,16 @@ def draw_alloc_utility(n_blocks: int, seed: int, sigma: float = 1.5,
     w = np.clip(np.exp(g.normal(0.0, sigma, n_blocks)), lo, hi)
     b = np.asarray(ALLOC_LEVELS, dtype=np.float64)
     return (-w[:, None] * np.power(4.0, -b)[None, :]).astype(np.float32)
+
+
+def draw_saliency(N: int, K: int, seed: int, integer: bool = False) -> np.ndarray:
+    """Per-weight saliency S[n][k] >= 0, fp32 [N][K]: w^2 * a_k^2 with w ~ N(0, 1) and
+    per-column activation scales a_k log-normal (sigma 1), the usual activation-aware
+    stand-in for the pages' sensitivities; `integer` gives small integers 0..15 (row
+    and column sums then exact in fp32 in any order)."""
+    g = np.random.default_rng([0x5A11, seed])
+    if integer:
+        return g.integers(0, 16, (N, K)).astype(np.float32)
+    a = np.exp(g.normal(0.0, 1.0, K))
+    w = g.standard_normal((N, K))
+    return (w * w * (a * a)[None, :]).astype(np.float32)
