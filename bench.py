@@ -247,6 +247,29 @@ def alloc_leg(msq, synth, torch, log):
             "note": "batched greedy over a 70B model's blocks, synthetic utilities; median of 3"}
 
 
+def reorder_leg(msq, torch, log):
+    """Channel reordering for one gate_proj-shaped saliency map (28672 x 8192 fp32,
+    940 MB, read once): time per call over 5 calls bracketed by events."""
+    N, K = 28672, 8192
+    S = torch.rand((N, K), dtype=torch.float32, device="cuda")
+    ws = torch.empty(int(msq.load_library().msq_reorder_workspace_bytes(N, K)), dtype=torch.uint8,
+                     device="cuda")
+    msq.reorder_channels(S, workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        msq.reorder_channels(S, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    gbps = N * K * 4 / (ms * 1e-3) / 1e9
+    log(f"reorder: {N}x{K} saliency, {ms:.3f} ms, {gbps:.0f} GB/s of saliency read")
+    del S, ws
+    return {"N": N, "K": K, "ms": round(ms, 4), "gbps_saliency": round(gbps, 1),
+            "note": "row and column sums in one pass over the fp32 map, two radix sorts"}
+
+
 def cpu_baseline(inputs, target_s: float = 12.0):
     """The oracle decoding a sample of block rows of every linear (M = 1).
 
@@ -547,6 +570,7 @@ def main() -> int:
             "note": "host-side descriptor validation included"}
 
     alloc = alloc_leg(msq, synth, torch, log)
+    reorder = reorder_leg(msq, torch, log)
 
     configs, context = None, None
     if not args.no_configs:
@@ -576,6 +600,7 @@ def main() -> int:
         "prefill": prefill,
         "pack": pack,
         "alloc": alloc,
+        "reorder": reorder,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "configs": configs,

@@ -25,7 +25,7 @@ import numpy as np
 __all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspace_bytes",
            "gemm_group", "group_workspace_bytes", "GROUP_MAX",
            "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M",
-           "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS"]
+           "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS", "reorder_channels"]
 
 FORMAT_VERSION = 1
 GEMV_MAX_M = 64
@@ -91,6 +91,10 @@ def load_library():
     lib.msq_alloc_workspace_bytes.restype = sz
     lib.msq_allocate_bits.argtypes = [vp, i64, i64, vp, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
     lib.msq_allocate_bits.restype = ctypes.c_int
+    lib.msq_reorder_workspace_bytes.argtypes = [i64, i64]
+    lib.msq_reorder_workspace_bytes.restype = sz
+    lib.msq_reorder_channels.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, sz, vp]
+    lib.msq_reorder_channels.restype = ctypes.c_int
     lib.msq_status_string.argtypes = [ctypes.c_int]
     lib.msq_status_string.restype = ctypes.c_char_p
     lib.msq_format_version.argtypes = []
@@ -328,3 +332,24 @@ def allocate_bits(utility, budget_bits: int, workspace=None, stream=None):
                                  workspace.data_ptr(), workspace.numel(), ctypes.byref(iters),
                                  _stream_handle(stream)), "msq_allocate_bits")
     return bits, int(iters.value)
+
+
+def reorder_channels(saliency, reorder_rows: bool = True, workspace=None, stream=None):
+    """(perm_row, perm_col) as int32 device tensors from a saliency map fp32 [N][K]
+    (msq_reorder_channels): rows and columns by total saliency, descending."""
+    torch = _torch()
+    lib = load_library()
+    S = torch.as_tensor(saliency)
+    if S.dtype != torch.float32 or S.dim() != 2:
+        raise ValueError("saliency must be float32 [N][K]")
+    S = S.to("cuda").contiguous()
+    N, K = int(S.shape[0]), int(S.shape[1])
+    pr = torch.empty(N, dtype=torch.int32, device=S.device)
+    pc = torch.empty(K, dtype=torch.int32, device=S.device)
+    need = int(lib.msq_reorder_workspace_bytes(N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=S.device)
+    _check(lib.msq_reorder_channels(S.data_ptr(), N, K, int(bool(reorder_rows)), pr.data_ptr(),
+                                    pc.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                    _stream_handle(stream)), "msq_reorder_channels")
+    return pr, pc

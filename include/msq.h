@@ -256,6 +256,33 @@ msq_status msq_allocate_bits(const float *utility, int64_t n_blocks, int64_t bud
                              uint8_t *bits, void *workspace, size_t workspace_bytes,
                              int32_t *iterations, hipStream_t stream);
 
+/* ---- bi-directional channel reordering -----------------------------------
+ * perm_row and perm_col for msq_quantize_pack from a per-weight saliency map:
+ * rows and columns are ordered by their total saliency, descending, ties by
+ * index ascending, so that salient weights gather in the leading block rows
+ * and block columns.  The ScaleBITS summary page (section Approach) reorders
+ * channels in both directions so that sensitive weights cluster into
+ * block-aligned regions, and (section Limitations) leaves the Q and K
+ * projections out of the row reordering: reorder_rows = 0 gives the identity
+ * perm_row.  The SFMP abstract aggregates salient weights by row and column
+ * reordering.  The pages give no rule; sorting by total saliency is this
+ * library's reading.
+ *
+ * saliency: device fp32 [N][K] row-major, >= 0 and finite (not checked),
+ *   16-byte aligned; N a multiple of 64 up to MSQ_REORDER_MAX_N, K a multiple
+ *   of 128 up to MSQ_REORDER_MAX_K.  perm_row: device int32 [N], perm_col:
+ *   device int32 [K], written (gather convention: reordered row i is
+ *   original row perm_row[i]).  Row and column sums are fp32 in a fixed
+ *   order, so the result is reproducible.  Asynchronous on the stream.
+ * Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer), MSQ_ERR_SHAPE,
+ *   MSQ_ERR_BUFFER_TOO_SMALL, MSQ_ERR_HIP. */
+#define MSQ_REORDER_MAX_N (1 << 20)
+#define MSQ_REORDER_MAX_K 32768
+size_t msq_reorder_workspace_bytes(int64_t N, int64_t K);
+msq_status msq_reorder_channels(const float *saliency, int64_t N, int64_t K, int reorder_rows,
+                                int32_t *perm_row, int32_t *perm_col, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code; never NULL. */
 const char *msq_status_string(msq_status status);
 

@@ -219,3 +219,22 @@ def test_alloc_host_checks(lib):
     assert f(256, 0, 5, 256, 256, 1 << 20, None, None) == 2        # no blocks
     assert f(256, 10, -1, 256, 256, 1 << 20, None, None) == 2      # negative budget
     assert f(256, 10, 5, 256, 256, 16, None, None) == 5            # workspace too small
+
+
+def test_reorder_host_checks(lib):
+    """Channel reordering: workspace sizing and argument checks, before any GPU work."""
+    import ctypes
+    lib.msq_reorder_workspace_bytes.restype = ctypes.c_size_t
+    lib.msq_reorder_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert lib.msq_reorder_workspace_bytes(64, 100) == 0        # K not a multiple of 128
+    assert lib.msq_reorder_workspace_bytes(0, 128) == 0
+    assert lib.msq_reorder_workspace_bytes(64, 65536) == 0      # K above the LDS limit
+    assert lib.msq_reorder_workspace_bytes(256, 512) >= 4 * (256 + 512)
+    f = lib.msq_reorder_channels
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert f(None, 64, 128, 1, 256, 256, 256, 1 << 20, None) == 1
+    assert f(264, 64, 128, 1, 256, 256, 256, 1 << 20, None) == 1   # saliency not 16-byte aligned
+    assert f(256, 65, 128, 1, 256, 256, 256, 1 << 20, None) == 2
+    assert f(256, 64, 128, 1, 256, 256, 256, 16, None) == 5
