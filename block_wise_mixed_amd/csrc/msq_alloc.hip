@@ -5,14 +5,15 @@
 // Every iteration, for every block that can still move up a level:
 //   k_alloc_keys   the cost d of its next step and the fp32 ratio
 //                  (u[l+1] - u[l]) / d as an order-preserving 32-bit key;
-//   radix sort     keys descending with the block index as value (the sort is
-//                  stable, so equal ratios keep ascending block order);
+//   radix sort     keys descending with 8 x block index + step cost as value
+//                  (the sort is stable, so equal ratios keep ascending block
+//                  order);
 //   k_alloc_costs  the step costs in sorted order, then an inclusive scan;
 //   k_alloc_select the longest sorted prefix whose cost is at most half the
 //                  remaining budget R (binary search over the scan), or, when
-//                  that is empty, the first sorted step that fits R (min
-//                  reduction); R and the iteration's status updated on the
-//                  device;
+//                  that is empty, k_alloc_first / k_alloc_finish: the first
+//                  sorted step that fits R (atomic minimum over the grid); R
+//                  and the iteration's status updated on the device;
 //   k_alloc_apply  the chosen blocks move up one level.
 // The host reads the status back after each iteration and stops when an
 // iteration takes nothing.  Blocks that cannot move (already at 8 bits) get
@@ -36,6 +37,8 @@ struct AllocStatus {
   int64_t taken;      // bits spent by the last iteration
   int32_t count;      // sorted positions [0, count) move up (count = -1: none)
   int32_t single;     // or just this sorted position (-1: none)
+  int32_t first;      // first-fit search: smallest qualifying position (INT32_MAX: none)
+  int32_t pending;    // the prefix was empty: the first-fit search decides
 };
 
 // IEEE float -> uint32 with the same order (no NaNs: the inputs are checked).
@@ -48,14 +51,14 @@ __global__ __launch_bounds__(256) void k_alloc_init(uint8_t* __restrict__ lev, i
                                                     AllocStatus* st, int64_t budget) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) lev[i] = 0;
-  if (i == 0) *st = AllocStatus{budget, 0, 0, -1};
+  if (i == 0) *st = AllocStatus{budget, 0, 0, -1, INT32_MAX, 0};
 }
 
+// The sort value carries the block index and the step cost: 8 i + d.
 __global__ __launch_bounds__(256) void k_alloc_keys(const float* __restrict__ u,
                                                     const uint8_t* __restrict__ lev, int64_t n,
                                                     uint32_t* __restrict__ key,
-                                                    int32_t* __restrict__ idx,
-                                                    int32_t* __restrict__ cost) {
+                                                    int32_t* __restrict__ val) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const int l = lev[i];
@@ -67,85 +70,82 @@ __global__ __launch_bounds__(256) void k_alloc_keys(const float* __restrict__ u,
     k = order_key(gain / (float)d);
   }
   key[i] = k;
-  idx[i] = (int32_t)i;
-  cost[i] = d;
+  val[i] = (int32_t)(8 * i + d);
 }
 
-__global__ __launch_bounds__(256) void k_alloc_costs(const int32_t* __restrict__ sorted_idx,
-                                                     const int32_t* __restrict__ cost, int64_t n,
-                                                     int32_t* __restrict__ sorted_cost) {
+__global__ __launch_bounds__(256) void k_alloc_costs(const int32_t* __restrict__ sorted_val,
+                                                     int64_t n, int32_t* __restrict__ sorted_cost) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (p < n) sorted_cost[p] = cost[sorted_idx[p]];
+  if (p < n) sorted_cost[p] = sorted_val[p] & 7;
 }
 
-constexpr int kSelectThreads = 1024;
-
-__global__ __launch_bounds__(kSelectThreads) void k_alloc_select(
-    const int32_t* __restrict__ scan, const int32_t* __restrict__ sorted_cost, int64_t n,
-    AllocStatus* st) {
-  __shared__ int32_t s_count;
-  __shared__ int32_t s_first[kSelectThreads / 64];
+// One thread: the longest sorted prefix within floor(R / 2) (binary search
+// over the non-decreasing scan).  When it takes nothing, the first-fit
+// search (k_alloc_first, k_alloc_finish) decides.
+__global__ __launch_bounds__(64) void k_alloc_select(const int32_t* __restrict__ scan, int64_t n,
+                                                    AllocStatus* st) {
+  if (threadIdx.x != 0) return;
   const int64_t R = st->remaining;
   const int64_t half = R / 2;
-  if (threadIdx.x == 0) {
-    // scan is non-decreasing: count = number of positions with scan <= half
-    int64_t lo = 0, hi = n;
-    while (lo < hi) {
-      const int64_t mid = (lo + hi) / 2;
-      if ((int64_t)scan[mid] <= half) lo = mid + 1; else hi = mid;
-    }
-    s_count = (int32_t)lo;
+  int64_t lo = 0, hi = n;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if ((int64_t)scan[mid] <= half) lo = mid + 1; else hi = mid;
   }
-  __syncthreads();
-  const int32_t count = s_count;
+  const int32_t count = (int32_t)lo;
   // a prefix of only blocks that cannot move takes nothing
   const int64_t prefix_bits = count > 0 ? (int64_t)scan[count - 1] : 0;
+  st->first = INT32_MAX;
   if (prefix_bits > 0) {
-    if (threadIdx.x == 0) {
-      st->remaining = R - prefix_bits;
-      st->taken = prefix_bits;
-      st->count = count;
-      st->single = -1;
-    }
-    return;
-  }
-  // first sorted step that fits R
-  int32_t first = INT32_MAX;
-  for (int64_t p = threadIdx.x; p < n; p += kSelectThreads) {
-    const int32_t d = sorted_cost[p];
-    if (d > 0 && d <= R) {
-      first = (int32_t)p;
-      break;
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) first = min(first, __shfl_xor(first, off, 64));
-  if ((threadIdx.x & 63) == 0) s_first[threadIdx.x >> 6] = first;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t f = INT32_MAX;
-    for (int k = 0; k < kSelectThreads / 64; ++k) f = min(f, s_first[k]);
-    if (f == INT32_MAX) {
-      st->taken = 0;
-      st->count = -1;
-      st->single = -1;
-    } else {
-      const int32_t d = sorted_cost[f];
-      st->remaining = R - d;
-      st->taken = d;
-      st->count = -1;
-      st->single = f;
-    }
+    st->remaining = R - prefix_bits;
+    st->taken = prefix_bits;
+    st->count = count;
+    st->single = -1;
+    st->pending = 0;
+  } else {
+    st->count = -1;
+    st->single = -1;
+    st->pending = 1;
   }
 }
 
-__global__ __launch_bounds__(256) void k_alloc_apply(const int32_t* __restrict__ sorted_idx,
-                                                     const int32_t* __restrict__ sorted_cost,
+// First sorted step that fits R (only when the prefix was empty).
+__global__ __launch_bounds__(256) void k_alloc_first(const int32_t* __restrict__ sorted_cost,
+                                                     int64_t n, AllocStatus* st) {
+  if (!st->pending) return;
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t R = st->remaining;
+  const bool fits = p < n && sorted_cost[p] > 0 && sorted_cost[p] <= R;
+  // one atomic per wavefront: its lowest qualifying position
+  const uint64_t m = __ballot(fits);
+  if (m != 0 && (threadIdx.x & 63) == 0) {
+    const int64_t q = (p & ~(int64_t)63) + __builtin_ctzll(m);
+    atomicMin(&st->first, (int32_t)q);
+  }
+}
+
+__global__ __launch_bounds__(64) void k_alloc_finish(const int32_t* __restrict__ sorted_cost,
+                                                     AllocStatus* st) {
+  if (threadIdx.x != 0 || !st->pending) return;
+  const int32_t f = st->first;
+  if (f == INT32_MAX) {
+    st->taken = 0;
+  } else {
+    const int32_t d = sorted_cost[f];
+    st->remaining -= d;
+    st->taken = d;
+    st->single = f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_alloc_apply(const int32_t* __restrict__ sorted_val,
                                                      int64_t n, const AllocStatus* st,
                                                      uint8_t* __restrict__ lev) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= n) return;
   const bool move = p < st->count || p == st->single;
-  if (move && sorted_cost[p] > 0) lev[sorted_idx[p]] += 1;
+  const int32_t v = sorted_val[p];
+  if (move && (v & 7) > 0) lev[v >> 3] += 1;
 }
 
 __global__ __launch_bounds__(256) void k_alloc_bits(const uint8_t* __restrict__ lev, int64_t n,
@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256) void k_alloc_check(const float* __restrict__ u
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct AllocLayout {
-  size_t key_in, key_out, idx_in, idx_out, cost, sorted_cost, scan, lev, status, bad, temp,
-      temp_bytes, total;
+  size_t key_in, key_out, val_in, val_out, sorted_cost, scan, lev, status, bad, temp, temp_bytes,
+      total;
 };
 
 AllocLayout alloc_layout(int64_t n) {
@@ -184,9 +184,8 @@ AllocLayout alloc_layout(int64_t n) {
   };
   L.key_in = take(4 * (size_t)n);
   L.key_out = take(4 * (size_t)n);
-  L.idx_in = take(4 * (size_t)n);
-  L.idx_out = take(4 * (size_t)n);
-  L.cost = take(4 * (size_t)n);
+  L.val_in = take(4 * (size_t)n);
+  L.val_out = take(4 * (size_t)n);
   L.sorted_cost = take(4 * (size_t)n);
   L.scan = take(4 * (size_t)n);
   L.lev = take((size_t)n);
@@ -221,9 +220,8 @@ extern "C" msq_status msq_allocate_bits(const float* utility, int64_t n_blocks, 
   auto at = [&](size_t off) { return ws + off; };
   uint32_t* key_in = reinterpret_cast<uint32_t*>(at(L.key_in));
   uint32_t* key_out = reinterpret_cast<uint32_t*>(at(L.key_out));
-  int32_t* idx_in = reinterpret_cast<int32_t*>(at(L.idx_in));
-  int32_t* idx_out = reinterpret_cast<int32_t*>(at(L.idx_out));
-  int32_t* cost = reinterpret_cast<int32_t*>(at(L.cost));
+  int32_t* val_in = reinterpret_cast<int32_t*>(at(L.val_in));
+  int32_t* val_out = reinterpret_cast<int32_t*>(at(L.val_out));
   int32_t* sorted_cost = reinterpret_cast<int32_t*>(at(L.sorted_cost));
   int32_t* scan = reinterpret_cast<int32_t*>(at(L.scan));
   uint8_t* lev = at(L.lev);
@@ -250,20 +248,21 @@ extern "C" msq_status msq_allocate_bits(const float* utility, int64_t n_blocks, 
   // every iteration moves at least one block up a level: at most 5 n iterations
   for (int64_t guard = 0; guard <= 5 * n_blocks; ++guard) {
     hipLaunchKernelGGL(k_alloc_keys, dim3(grid), dim3(256), 0, stream, utility, lev, n_blocks,
-                       key_in, idx_in, cost);
+                       key_in, val_in);
     size_t tb = L.temp_bytes;
-    if (hipcub::DeviceRadixSort::SortPairsDescending(temp, tb, key_in, key_out, idx_in, idx_out, n,
+    if (hipcub::DeviceRadixSort::SortPairsDescending(temp, tb, key_in, key_out, val_in, val_out, n,
                                                      0, 32, stream) != hipSuccess)
       return MSQ_ERR_HIP;
-    hipLaunchKernelGGL(k_alloc_costs, dim3(grid), dim3(256), 0, stream, idx_out, cost, n_blocks,
+    hipLaunchKernelGGL(k_alloc_costs, dim3(grid), dim3(256), 0, stream, val_out, n_blocks,
                        sorted_cost);
     tb = L.temp_bytes;
     if (hipcub::DeviceScan::InclusiveSum(temp, tb, sorted_cost, scan, n, stream) != hipSuccess)
       return MSQ_ERR_HIP;
-    hipLaunchKernelGGL(k_alloc_select, dim3(1), dim3(kSelectThreads), 0, stream, scan, sorted_cost,
-                       n_blocks, st);
-    hipLaunchKernelGGL(k_alloc_apply, dim3(grid), dim3(256), 0, stream, idx_out, sorted_cost,
-                       n_blocks, st, lev);
+    hipLaunchKernelGGL(k_alloc_select, dim3(1), dim3(64), 0, stream, scan, n_blocks, st);
+    hipLaunchKernelGGL(k_alloc_first, dim3(grid), dim3(256), 0, stream, sorted_cost, n_blocks, st);
+    hipLaunchKernelGGL(k_alloc_finish, dim3(1), dim3(64), 0, stream, sorted_cost, st);
+    hipLaunchKernelGGL(k_alloc_apply, dim3(grid), dim3(256), 0, stream, val_out, n_blocks, st,
+                       lev);
     AllocStatus h{};
     if (hipGetLastError() != hipSuccess ||
         hipMemcpyAsync(&h, st, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess ||

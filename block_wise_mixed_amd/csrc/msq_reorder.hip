@@ -11,7 +11,8 @@
 //                    sums reduced in a fixed order (thread, wavefront tree,
 //                    wavefronts in order); column partials per slice to the
 //                    workspace;
-//   k_reorder_cols   column sums over the slices in slice order;
+//   k_reorder_cols   column sums over the slices (16 slice groups per
+//                    column, each in slice order, then the groups in order);
 //   k_reorder_keys   order-preserving keys and indices;
 //   radix sort       keys descending, indices as values (stable: ties keep
 //                    ascending index) -> perm_row, perm_col.
@@ -75,14 +76,26 @@ __global__ __launch_bounds__(kSumThreads) void k_reorder_sums(const float* __res
     reinterpret_cast<float4*>(col_part + (int64_t)blockIdx.x * K)[c] = reinterpret_cast<float4*>(acc)[c];
 }
 
+// Column sums over the slices: workgroup = 16 columns x 16 slice groups;
+// group g adds slices g, g + 16, ... in order, then the 16 group sums are
+// added in group order (a fixed order: reproducible).
+constexpr int kColGroups = 16;
 __global__ __launch_bounds__(256) void k_reorder_cols(const float* __restrict__ col_part,
                                                       int slices, int64_t K,
                                                       float* __restrict__ col_sum) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= K) return;
+  __shared__ float part[kColGroups][16];
+  const int cl = threadIdx.x & 15, g = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
   float s = 0.f;
-  for (int k = 0; k < slices; ++k) s += col_part[(int64_t)k * K + c];
-  col_sum[c] = s;
+  if (c < K)
+    for (int k = g; k < slices; k += kColGroups) s += col_part[(int64_t)k * K + c];
+  part[g][cl] = s;
+  __syncthreads();
+  if (g == 0 && c < K) {
+    float t = 0.f;
+    for (int k = 0; k < kColGroups; ++k) t += part[k][cl];
+    col_sum[c] = t;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_reorder_keys(const float* __restrict__ score, int64_t n,
@@ -172,7 +185,7 @@ extern "C" msq_status msq_reorder_channels(const float* saliency, int64_t N, int
   const size_t lds = 4 * (size_t)K + 16 * (size_t)p.rows_per_slice;
   hipLaunchKernelGGL(k_reorder_sums, dim3((unsigned)p.slices), dim3(kSumThreads), lds, stream,
                      saliency, N, K, p.rows_per_slice, row_sum, col_part);
-  hipLaunchKernelGGL(k_reorder_cols, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_reorder_cols, dim3((unsigned)((K + 15) / 16)), dim3(256), 0, stream,
                      col_part, p.slices, K, col_sum);
   auto sort = [&](const float* score, int64_t n, int32_t* out) {
     hipLaunchKernelGGL(k_reorder_keys, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
