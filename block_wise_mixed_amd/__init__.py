@@ -256,9 +256,10 @@ def group_workspace_bytes(M: int, pws) -> int:
 
 
 def gemm_group(xs, pws, outs=None, workspace=None, stream=None):
-    """[x_i . W_i^T] for up to GROUP_MAX packed weights in one call (M == 1: one prep
-    and one decode launch for all of them; M > 64: one gather and one GEMM launch).  xs: one activation per weight (the same
-    tensor may repeat); returns the list of fp32 [M][N_i] outputs."""
+    """[x_i . W_i^T] for up to GROUP_MAX packed weights in one call (M == 1: one decode
+    launch for all of them, plus one prep launch if some have several K ranges; large M:
+    one gather and one GEMM launch).  xs: one activation per weight (the same tensor may
+    repeat); returns the list of fp32 [M][N_i] outputs."""
     torch = _torch()
     lib = load_library()
     pws = list(pws)

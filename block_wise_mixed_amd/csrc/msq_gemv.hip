@@ -27,10 +27,11 @@
 //     the last workgroup of the block row to finish; M > 1: by
 //     k_gemv_reduce), so results are bitwise reproducible.
 //
-// M == 1 has its own kernels (k_prep_m1 + k_gemv_m1): the prep also forms
-// the per-bitwidth bias corrections, the unpack avoids most shifts, the
-// scales and zero points are staged in LDS, and each wavefront keeps 4 to
-// 8 KiB of codes in flight.
+// M == 1 has its own kernels (k_gemv_m1, after k_prep_m1 only when K is
+// split into several ranges): the reordered x comes with per-column k-step
+// sums for the bias corrections, the unpack avoids most shifts, the scales
+// and zero points are staged in LDS, and each wavefront keeps 2 to 4 KiB of
+// codes in flight.
 //
 // Per-block precision and block layout: "ScaleBITS" summary page, section
 // Approach; RTN-g128 dequantization s * (q - z): section Limitations.
@@ -459,8 +460,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x
 //
 // k_prep_m1 reorders x once per call into the workspace: xg[j] = x[perm_col[j]]
 // and, per block column c, the k-step sums S_c[kt] (kt = 0..3, each over 32
-// reordered columns).  k_gemv_m1 copies its range of both into LDS with
-// 16-byte loads; per block it forms the group sum and the bias correction
+// reordered columns); with one K range k_gemv_m1 forms both itself.
+// k_gemv_m1 copies its range of both into LDS with 16-byte loads; per block
+// it forms the group sum and the bias correction
 //     corr = sum_kt exp_bias(b, 4*rt + kt) * S_c[kt]
 // (rt = the lane's row tile) from them.
 //
@@ -846,12 +848,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
 }
 
 // ---- grouped M == 1 calls: up to kGroupMax matrices per launch ---------------------------
-// One prep launch and one decode launch cover all matrices of the group (for
-// example the q, k, v projections of a layer, which read the same x); the
-// workgroups of the matrices run side by side, so small matrices no longer
-// leave the GPU idle for a launch of their own.  Job j owns the workgroups
-// [prep_begin, prep_begin of j + 1) of the prep launch and
-// [wg_begin, wg_begin of j + 1) of the decode launch.
+// One decode launch covers all matrices of the group (for example the q, k,
+// v projections of a layer, which read the same x), plus one prep launch for
+// the jobs with several K ranges; the workgroups of the matrices run side by
+// side, so small matrices no longer leave the GPU idle for a launch of their
+// own.  Job j owns the workgroups [prep_begin, prep_begin of j + 1) of the
+// prep launch (none when it reorders x itself) and [wg_begin, wg_begin of
+// j + 1) of the decode launch.
 constexpr int kGroupMax = 8;
 
 struct M1Job {

@@ -50,8 +50,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows = 0);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 
-// Grouped M == 1 decode of count (1 .. 8) matrices in one prep and one decode
-// launch; the workspace holds each matrix's single-call workspace in turn.
+// Grouped M == 1 decode of count (1 .. 8) matrices in one decode launch (and
+// one prep launch for those with several K ranges); the workspace holds each
+// matrix's single-call workspace in turn.
 constexpr int kGemvGroupMax = 8;
 size_t gemv_group_workspace_m1(const WeightView* w, int count);
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,

@@ -208,8 +208,9 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int
 /* y[i] = x[i] . W_i^T for count matrices (1 .. MSQ_GROUP_MAX), each exactly
  * as msq_gemm computes it.  For the decode step of a layer, whose q, k, v
  * projections (and gate, up) read the same activation: at M == 1 one
- * activation-prep launch and one decode launch cover all matrices, their
- * workgroups running side by side ("TileQuant" abstract: local accumulation
+ * decode launch covers all matrices, their workgroups running side by side
+ * (matrices whose K is split into several ranges add one activation-prep
+ * launch for all of them; the others reorder x inside their workgroups) ("TileQuant" abstract: local accumulation
  * to reduce memory traffic; the grouping itself is this library's).  At
  * M > 16, when the matrices' tiles fill the GPU (prefill), one
  * activation-gather launch and one GEMM launch cover all matrices, the tiles
