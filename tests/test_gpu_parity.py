@@ -292,9 +292,14 @@ def test_full_size_sampled(msq, workload, matrix):
     torch.cuda.empty_cache()
 
 
-def test_graph_replay_matches_eager(msq):
+@pytest.mark.parametrize("split", ["auto", "1"])
+def test_graph_replay_matches_eager(msq, monkeypatch, split):
     """The decode and prefill calls are captured in HIP graphs by bench.py: every replay,
-    with eager work in between, must equal the eager result bit for bit."""
+    with eager work in between, must equal the eager result bit for bit (at M = 1 with
+    the automatic K split and with one K range, where the decode workgroups reorder x
+    themselves)."""
+    if split != "auto":
+        monkeypatch.setenv("MSQ_GEMV_SPLIT", split)
     c = synth.random_case(1024, 4096, 50, dist=SMALL_DIST)
     pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
     for M in (1, 16, 200):
@@ -406,9 +411,14 @@ def test_group_sizes(msq, group_cases, M):
         msq.gemm_group([x] * (msq.GROUP_MAX + 1), [pw] * (msq.GROUP_MAX + 1))
 
 
-def test_group_graph_replay_matches_eager(msq, group_cases):
+@pytest.mark.parametrize("split", ["auto", "1"])
+def test_group_graph_replay_matches_eager(msq, group_cases, monkeypatch, split):
     """bench.py captures grouped decode calls in HIP graphs: every replay, with eager
-    work in between on the same workspace, must equal the eager result bit for bit."""
+    work in between on the same workspace, must equal the eager result bit for bit;
+    with the automatic split (prep launch, split counters) and with one K range (the
+    workgroups reorder x themselves)."""
+    if split != "auto":
+        monkeypatch.setenv("MSQ_GEMV_SPLIT", split)
     pws = [pw for _, pw, _ in group_cases]
     x_shared = torch.from_numpy(group_cases[0][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
     x_last = torch.from_numpy(group_cases[3][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
