@@ -28,6 +28,12 @@ What it computes, step by step
                     scattered back through perm_row so it is in original row
                     order.
 
+16-bit blocks ("TileQuant" abstract: tiles kept at 16 bits beside 8-bit
+ones) are a passthrough: the codes are the bf16 bit patterns of the reordered
+weights in the same layout (one fragment per 1 KiB chunk), s = z = 0, and
+W-hat is the bf16 weight itself (format version 2 = version 1 plus these
+blocks; pinned by the identity W-hat == W and the bit-by-bit packer).
+
 Readings where the pages are silent (all stated in the library header too):
 64 rows along N x 128 columns along K per block; asymmetric RTN with the range
 widened to include 0 (lo = min(0, min w), hi = max(0, max w)); integer zero
@@ -54,10 +60,11 @@ import numpy as np
 
 BLOCK_ROWS = 64
 BLOCK_COLS = 128
-ALLOWED_BITS = (0, 1, 2, 3, 4, 8)
-SEGMENT_ORDER = (1, 2, 3, 4, 8)
+ALLOWED_BITS = (0, 1, 2, 3, 4, 8, 16)
+SEGMENT_ORDER = (1, 2, 3, 4, 8, 16)
+PASSTHROUGH_BITS = 16
 NO_BLOCK = 0xFFFFFFFF
-FORMAT_VERSION = 1
+FORMAT_VERSION = 2
 
 
 # --------------------------------------------------------------------------- inputs
@@ -76,7 +83,7 @@ def validate(N: int, K: int, bits: np.ndarray, perm_row: np.ndarray, perm_col: n
     if bits.shape != (N // BLOCK_ROWS, K // BLOCK_COLS):
         raise ValueError(f"bits shape {bits.shape} != {(N // BLOCK_ROWS, K // BLOCK_COLS)}")
     if not np.isin(bits, ALLOWED_BITS).all():
-        raise ValueError("bits must be in {0,1,2,3,4,8}")
+        raise ValueError("bits must be in {0,1,2,3,4,8,16}")
     for name, p, n in (("perm_row", perm_row, N), ("perm_col", perm_col, K)):
         p = np.asarray(p)
         if p.shape != (n,) or not np.array_equal(np.sort(p), np.arange(n)):
@@ -115,7 +122,7 @@ def group_params(Wr: np.ndarray, bits: np.ndarray) -> Tuple[np.ndarray, np.ndarr
     hi = np.maximum(np.float32(0.0), g.max(axis=2))
     b = row_bits(bits)
     qmax = (np.left_shift(1, b) - 1).astype(np.float32)
-    live = b > 0
+    live = (b > 0) & (b != PASSTHROUGH_BITS)  # 16-bit blocks keep bf16 values: s = z = 0
     d = (hi - lo).astype(np.float32)
     s = np.zeros((R, G), dtype=np.float32)
     s[live] = d[live] / qmax[live]
@@ -127,8 +134,19 @@ def group_params(Wr: np.ndarray, bits: np.ndarray) -> Tuple[np.ndarray, np.ndarr
 
 
 def quantize_codes(Wr: np.ndarray, bits: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """Codes q = clamp(rint(fl(w / s)) + z, 0, qmax) as uint8 [R][K]; 0 where s == 0."""
+    """Codes q = clamp(rint(fl(w / s)) + z, 0, qmax) as uint16 [R][K]; 0 where s == 0;
+    in 16-bit blocks the bf16 bit pattern of w itself (passthrough, "TileQuant"
+    abstract: tiles kept at 16 bits)."""
     Wr = np.asarray(Wr, dtype=np.float32)
+    R, K = Wr.shape
+    G = K // BLOCK_COLS
+    out = _rtn_codes(Wr, bits, s, z).astype(np.uint16)
+    pt = np.repeat(row_bits(bits) == PASSTHROUGH_BITS, BLOCK_COLS, axis=1)
+    out[pt] = (Wr.view(np.uint32)[pt] >> 16).astype(np.uint16)
+    return out
+
+
+def _rtn_codes(Wr: np.ndarray, bits: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
     R, K = Wr.shape
     G = K // BLOCK_COLS
     g = Wr.reshape(R, G, BLOCK_COLS)
@@ -208,12 +226,12 @@ def _unpack_plane(words: np.ndarray, b: int) -> np.ndarray:
     widx, shift = _layout_maps(b)
     nblk = words.shape[0]
     return ((words[:, widx.ravel()] >> shift.ravel()[None, :]) & np.uint32((1 << b) - 1)) \
-        .astype(np.uint8).reshape(nblk, BLOCK_ROWS, BLOCK_COLS)
+        .astype(np.uint16 if b == PASSTHROUGH_BITS else np.uint8).reshape(nblk, BLOCK_ROWS, BLOCK_COLS)
 
 
 def pack_blocks(q_blocks: np.ndarray, b: int) -> np.ndarray:
     """Bytes of b-bit blocks: q_blocks [nblk][64][128] -> uint8 [nblk][1024*b]."""
-    q_blocks = np.asarray(q_blocks, dtype=np.uint8)
+    q_blocks = np.asarray(q_blocks, dtype=np.uint16 if b == PASSTHROUGH_BITS else np.uint8)
     if b == 3:
         words = np.concatenate([_pack_plane(q_blocks & 3, 2), _pack_plane(q_blocks >> 2, 1)], axis=1)
     else:
@@ -254,7 +272,7 @@ def pack(q: np.ndarray, bits: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
 def unpack(codes: np.ndarray, bits: np.ndarray, off: np.ndarray) -> np.ndarray:
     """Inverse of pack: codes [N][K] (0 in 0-bit blocks)."""
     nbr, nbc = bits.shape
-    q = np.zeros((nbr, nbc, BLOCK_ROWS, BLOCK_COLS), dtype=np.uint8)
+    q = np.zeros((nbr, nbc, BLOCK_ROWS, BLOCK_COLS), dtype=np.uint16)
     for b in SEGMENT_ORDER:
         rs, cs = np.nonzero(bits == b)
         if rs.size == 0:
@@ -267,12 +285,18 @@ def unpack(codes: np.ndarray, bits: np.ndarray, off: np.ndarray) -> np.ndarray:
 
 # --------------------------------------------------------------------------- product
 
-def dequantize(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
-    """W-hat[i][j] = s[i][j/128] * (q[i][j] - z[i][j/128]) in fp64 (exact)."""
+def dequantize(q: np.ndarray, s: np.ndarray, z: np.ndarray,
+               bits: np.ndarray | None = None) -> np.ndarray:
+    """W-hat[i][j] = s[i][j/128] * (q[i][j] - z[i][j/128]) in fp64 (exact); in 16-bit
+    blocks (bits given) the bf16 value whose bit pattern q holds."""
     R, K = q.shape
     G = K // BLOCK_COLS
     qd = q.astype(np.float64).reshape(R, G, BLOCK_COLS) - z.astype(np.float64)[:, :, None]
-    return (s.astype(np.float64)[:, :, None] * qd).reshape(R, K)
+    out = (s.astype(np.float64)[:, :, None] * qd).reshape(R, K)
+    if bits is not None:
+        pt = np.repeat(row_bits(bits) == PASSTHROUGH_BITS, BLOCK_COLS, axis=1)
+        out[pt] = bf16_to_f32(np.asarray(q, dtype=np.uint16)[pt]).astype(np.float64)
+    return out
 
 
 def matmul(x_f32: np.ndarray, What_r: np.ndarray, perm_col: np.ndarray,
@@ -330,7 +354,7 @@ def reference_gemm(x_bits: np.ndarray, qres: dict, perm_row: np.ndarray,
     All block rows covered: [M][N] in original row order.  A subset of block
     rows: [M][len(rows)], column t belonging to original output row
     perm_row[qres['rows'][t]]."""
-    What = dequantize(qres["q"], qres["s"], qres["z"])
+    What = dequantize(qres["q"], qres["s"], qres["z"], qres["bits"])
     K = What.shape[1]
     x = bf16_to_f32(np.asarray(x_bits, dtype=np.uint16).reshape(-1, K))
     if What.shape[0] == len(perm_row):

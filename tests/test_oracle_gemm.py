@@ -36,6 +36,11 @@ def brute_force_y(W_bits, bits, perm_row, perm_col, x_bits):
             vals = [W[orow][oc] for oc in cols]
             if b == 0:
                 continue
+            if b == 16:  # passthrough: the bf16 weight itself
+                for jj, oc in enumerate(cols):
+                    for m in range(M):
+                        y[m][orow] += x[m][oc] * float(vals[jj])
+                continue
             lo = min(f32(0), min(vals))
             hi = max(f32(0), max(vals))
             qmax = f32((1 << b) - 1)
@@ -54,7 +59,7 @@ def brute_force_y(W_bits, bits, perm_row, perm_col, x_bits):
 @pytest.mark.parametrize("N,K,M,seed", [(64, 128, 1, 0), (128, 256, 2, 1), (64, 256, 3, 2),
                                          (128, 128, 1, 3)])
 def test_matches_triple_loop(N, K, M, seed):
-    c = synth.random_case(N, K, seed, dist={0: .15, 1: .15, 2: .2, 3: .2, 4: .15, 8: .15})
+    c = synth.random_case(N, K, seed, dist={0: .1, 1: .15, 2: .2, 3: .2, 4: .1, 8: .1, 16: .15})
     x = c.x(M)
     r = oracle.quantize(c.W, c.bits, c.perm_row, c.perm_col)
     y = oracle.reference_gemm(x, r, c.perm_row, c.perm_col)
@@ -144,3 +149,14 @@ def test_empty_batch():
     r = oracle.quantize(c.W, c.bits, c.perm_row, c.perm_col)
     y = oracle.reference_gemm(np.zeros((0, 128), np.uint16), r, c.perm_row, c.perm_col)
     assert y.shape == (0, 64)
+
+
+def test_passthrough_blocks_are_exact():
+    """16-bit blocks: W-hat equals W bit for bit (bf16 kept), scale and zero stored as 0."""
+    c = synth.random_case(128, 512, 9, dist={16: .6, 2: .4})
+    r = oracle.quantize(c.W, c.bits, c.perm_row, c.perm_col)
+    Wh = oracle.dequantize(r["q"], r["s"], r["z"], r["bits"])
+    pt = np.repeat(np.repeat(c.bits == 16, 64, axis=0), 128, axis=1)
+    Wr = oracle.bf16_to_f32(c.W)[np.ix_(c.perm_row, c.perm_col)]
+    assert pt.any() and np.array_equal(Wh[pt], Wr[pt].astype(np.float64))
+    assert (r["s"][np.repeat(c.bits == 16, 64, axis=0)] == 0).all()

@@ -42,10 +42,10 @@ def slow_pack_block(q, b):
     return np.frombuffer(bytes(out), dtype=np.uint8)
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8, 16])
 def test_vectorized_pack_matches_bit_by_bit(b):
     g = np.random.default_rng(b)
-    q = g.integers(0, 1 << b, size=(3, 64, 128)).astype(np.uint8)
+    q = g.integers(0, 1 << b, size=(3, 64, 128)).astype(np.uint16 if b == 16 else np.uint8)
     fast = oracle.pack_blocks(q, b)
     for i in range(3):
         assert np.array_equal(fast[i], slow_pack_block(q[i], b))
@@ -80,10 +80,10 @@ def test_layout_is_a_bijection(b):
         assert list(on) == [_bit_address(ib, jb, k, b)]
 
 
-@pytest.mark.parametrize("b", [1, 2, 3, 4, 8])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 8, 16])
 def test_unpack_inverts_pack(b):
     g = np.random.default_rng(10 + b)
-    q = g.integers(0, 1 << b, size=(5, 64, 128)).astype(np.uint8)
+    q = g.integers(0, 1 << b, size=(5, 64, 128)).astype(np.uint16 if b == 16 else np.uint8)
     assert np.array_equal(oracle.unpack_blocks(oracle.pack_blocks(q, b), b), q)
 
 
@@ -113,12 +113,12 @@ def test_chunk_is_mfma_fragment():
 
 def test_offsets_are_prefix_sum_over_packed_order():
     g = np.random.default_rng(3)
-    bits = g.choice(np.array([0, 1, 2, 3, 4, 8], np.uint8), size=(7, 9))
+    bits = g.choice(np.array([0, 1, 2, 3, 4, 8, 16], np.uint8), size=(7, 9))
     off, code_bytes = oracle.block_offsets(bits)
     assert code_bytes == 1024 * int(bits.astype(np.int64).sum())
     # brute force: walk the packed order explicitly
     acc = 0
-    for b in (1, 2, 3, 4, 8):
+    for b in (1, 2, 3, 4, 8, 16):
         for r in range(7):
             for c in range(9):
                 if bits[r, c] == b:
@@ -150,3 +150,17 @@ def test_empty_segments_and_all_zero_bits():
     bits = np.full((2, 3), 8, np.uint8)
     off, cb = oracle.block_offsets(bits)
     assert cb == 6 * 8192 and list(off.ravel()) == [0, 8, 16, 24, 32, 40]
+
+
+def test_passthrough_chunk_is_the_bf16_fragment():
+    """16-bit blocks: chunk F holds, at lane l's 16 bytes, the eight bf16 values of row
+    16 (F >> 2) + (l & 15), columns 32 (F & 3) + 8 (l >> 4) .. + 7, little-endian,
+    i.e. the matrix-core B operand of that fragment with no unpacking."""
+    g = np.random.default_rng(77)
+    q = g.integers(0, 1 << 16, size=(1, 64, 128)).astype(np.uint16)
+    raw = oracle.pack_blocks(q, 16)[0].view("<u2").reshape(16, 64, 8)
+    for F in range(16):
+        for l in range(64):
+            row = 16 * (F >> 2) + (l & 15)
+            col = 32 * (F & 3) + 8 * (l >> 4)
+            assert np.array_equal(raw[F, l], q[0, row, col:col + 8])
