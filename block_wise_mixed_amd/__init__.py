@@ -27,7 +27,7 @@ __all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspa
            "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M",
            "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS", "reorder_channels"]
 
-FORMAT_VERSION = 1
+FORMAT_VERSION = 2
 GEMV_MAX_M = 64
 KERNELS = {"auto": 0, "gemv": 1, "gemm": 2}
 
@@ -50,7 +50,7 @@ class MsqError(RuntimeError):
 class _Sizes(ctypes.Structure):
     _fields_ = [("code_bytes", ctypes.c_int64), ("scale_bytes", ctypes.c_int64),
                 ("zero_bytes", ctypes.c_int64), ("offset_bytes", ctypes.c_int64),
-                ("blocks_per_bits", ctypes.c_int64 * 9), ("mean_bits", ctypes.c_double)]
+                ("blocks_per_bits", ctypes.c_int64 * 17), ("mean_bits", ctypes.c_double)]
 
 
 class _Weight(ctypes.Structure):
@@ -58,7 +58,8 @@ class _Weight(ctypes.Structure):
                 ("bits", ctypes.c_void_p), ("perm_row", ctypes.c_void_p),
                 ("perm_col", ctypes.c_void_p), ("block_offset", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("zero", ctypes.c_void_p), ("code_bytes", ctypes.c_int64)]
+                ("zero", ctypes.c_void_p), ("code_bytes", ctypes.c_int64),
+                ("tile16_blocks", ctypes.c_int64)]
 
 
 def load_library():
@@ -158,7 +159,7 @@ def _as_bf16_cuda(a, device):
 
 @dataclass
 class PackedWeight:
-    """Device buffers of one packed weight (format version 1).  Holds the tensors
+    """Device buffers of one packed weight (format version 2).  Holds the tensors
     so their memory outlives every call that uses the descriptor."""
     N: int
     K: int
@@ -171,6 +172,7 @@ class PackedWeight:
     zero: "object"          # uint8 [N/64][K/128][64]
     code_bytes: int
     mean_bits: float = 0.0
+    tile16_blocks: int = 0
 
     def descriptor(self) -> _Weight:
         w = _Weight()
@@ -183,6 +185,7 @@ class PackedWeight:
         w.scale = self.scale.data_ptr()
         w.zero = self.zero.data_ptr()
         w.code_bytes = self.code_bytes
+        w.tile16_blocks = self.tile16_blocks
         return w
 
     def to_numpy(self) -> dict:
@@ -196,7 +199,8 @@ class PackedWeight:
         """Independent copy of every buffer (used to defeat caches in benchmarks)."""
         return PackedWeight(self.N, self.K, self.bits.clone(), self.perm_row.clone(),
                             self.perm_col.clone(), self.block_offset.clone(), self.codes.clone(),
-                            self.scale.clone(), self.zero.clone(), self.code_bytes, self.mean_bits)
+                            self.scale.clone(), self.zero.clone(), self.code_bytes, self.mean_bits,
+                            self.tile16_blocks)
 
     @property
     def packed_bytes(self) -> int:
@@ -230,7 +234,8 @@ def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> Pa
         codes=torch.empty(max(code_bytes, 256), dtype=torch.uint8, device=dev),
         scale=torch.empty((N // 64, K // 128, 64), dtype=torch.float32, device=dev),
         zero=torch.empty((N // 64, K // 128, 64), dtype=torch.uint8, device=dev),
-        code_bytes=code_bytes, mean_bits=float(sizes["mean_bits"]))
+        code_bytes=code_bytes, mean_bits=float(sizes["mean_bits"]),
+        tile16_blocks=int(sizes["blocks_per_bits"][16]))
     w = pw.descriptor()
     _check(lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), _stream_handle(stream)),
            "msq_quantize_pack")

@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libmsq.so")
 ARCH = "gfx950"
 
 SOURCES = ["msq_host.cpp", "msq_pack.hip", "msq_gemv.hip", "msq_gemm.hip", "msq_alloc.hip",
-           "msq_reorder.hip"]
+           "msq_reorder.hip", "msq_tile16.hip"]
 
 # Device code: O3, no fast-math (correctly rounded division, denormals kept),
 # no packed-fp32 instructions.

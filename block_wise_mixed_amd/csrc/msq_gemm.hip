@@ -297,6 +297,11 @@ constexpr int kTUnits = 4;  // units of 4 rows per thread: BR * 32 * 16 / (128 *
 // Workgroup barrier that waits for the wavefront's LDS operations only (loads
 // from global memory stay in flight); the empty asm statements keep the
 // compiler from moving memory operations across it.
+// Bitwidth as the quantized products see it: 16-bit (passthrough) blocks
+// count as pruned here (their scale is 0, so the correction skips them too);
+// k_tile16 adds their products afterwards.
+__device__ __forceinline__ int quantized_bits(int b) { return b == 16 ? 0 : b; }
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
@@ -347,7 +352,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     }
     const int64_t blk = (int64_t)(rb + q) * w.NBc + c;
     off = __builtin_amdgcn_readfirstlane(w.block_offset[blk]);
-    return __builtin_amdgcn_readfirstlane(w.bits[blk]);
+    return quantized_bits(__builtin_amdgcn_readfirstlane(w.bits[blk]));
   };
 
   // Direct-to-LDS copies of group c into stage st: wavefront w copies rows
@@ -381,7 +386,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     const int q = i / tabG, c = i - (i / tabG) * tabG;
     const int rr = rb + q;
     const int64_t blk = (int64_t)(rr < w.NBr ? rr : 0) * w.NBc + g0 + c;
-    tbits[q][c] = rr < w.NBr ? w.bits[blk] : 0;
+    tbits[q][c] = rr < w.NBr ? quantized_bits(w.bits[blk]) : 0;
     toff[q][c] = rr < w.NBr ? w.block_offset[blk] : 0u;
   }
   __syncthreads();
@@ -504,7 +509,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       const int rr = rb + q;
       const bool live = rr < w.NBr && c >= g0 && c < g1;
       const int64_t blk = live ? (int64_t)rr * w.NBc + c : 0;
-      lb[k] = !live ? 0 : (c - g0 < kTabG ? (int)tbits[q][c - g0] : (int)w.bits[blk]);
+      lb[k] = !live ? 0 : (c - g0 < kTabG ? (int)tbits[q][c - g0] : quantized_bits(w.bits[blk]));
       ls[k] = *reinterpret_cast<const float4*>(w.scale + blk * kBlockRows + n4);
       lz[k] = *reinterpret_cast<const uint32_t*>(w.zero + blk * kBlockRows + n4);
     }

@@ -18,7 +18,9 @@ using msq::kBlockRows;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool bits_ok(uint8_t b) { return b == 0 || b == 1 || b == 2 || b == 3 || b == 4 || b == 8; }
+bool bits_ok(uint8_t b) {
+  return b == 0 || b == 1 || b == 2 || b == 3 || b == 4 || b == 8 || b == 16;
+}
 
 msq_status check_shape(int64_t N, int64_t K) {
   if (N <= 0 || K <= 0 || N % kBlockRows != 0 || K % kBlockCols != 0) return MSQ_ERR_SHAPE;
@@ -67,6 +69,7 @@ msq_status weight_ptrs_ok(const msq_weight* w) {
   if (!w->bits || !w->perm_row || !w->perm_col || !w->block_offset || !w->scale || !w->zero)
     return MSQ_ERR_INVALID_ARG;
   if (!w->codes && w->code_bytes > 0) return MSQ_ERR_INVALID_ARG;
+  if (w->tile16_blocks < 0) return MSQ_ERR_INVALID_ARG;
   if (w->codes && !aligned(w->codes, 256)) return MSQ_ERR_INVALID_ARG;
   if (!aligned(w->perm_row, 4) || !aligned(w->perm_col, 16) || !aligned(w->block_offset, 4) ||
       !aligned(w->scale, 16) || !aligned(w->zero, 16))
@@ -130,6 +133,7 @@ msq_status msq_quantize_pack(const uint16_t* W_bf16, const msq_weight* w, hipStr
   st = plan_impl(N, K, bits.data(), prow.data(), pcol.data(), &sz);
   if (st != MSQ_OK) return st;
   if (w->code_bytes < sz.code_bytes) return MSQ_ERR_BUFFER_TOO_SMALL;
+  if (w->tile16_blocks != sz.blocks_per_bits[16]) return MSQ_ERR_INVALID_ARG;
   if (hipError_t e = msq::launch_block_offsets(w->bits, nblk, w->block_offset, stream); e != hipSuccess)
     return MSQ_ERR_HIP;
   if (hipError_t e = msq::launch_pack(W_bf16, N, K, w->bits, w->perm_row, w->perm_col,
@@ -171,6 +175,7 @@ msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, f
   } else {
     e = msq::launch_gemm(x_bf16, M, v, y, workspace, stream);
   }
+  if (e == hipSuccess && w->tile16_blocks > 0) e = msq::launch_tile16(x_bf16, M, v, y, stream);
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
@@ -224,8 +229,10 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
   if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
   msq::WeightView v[MSQ_GROUP_MAX];
   for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
-  const hipError_t e = M == 1 ? msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream)
-                              : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
+  hipError_t e = M == 1 ? msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream)
+                        : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
+  for (int i = 0; i < count && e == hipSuccess; ++i)
+    if (w[i]->tile16_blocks > 0) e = msq::launch_tile16(x_bf16[i], M, v[i], y[i], stream);
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
@@ -234,7 +241,7 @@ const char* msq_status_string(msq_status s) {
     case MSQ_OK: return "success";
     case MSQ_ERR_INVALID_ARG: return "invalid argument (null, misaligned pointer or bad enum)";
     case MSQ_ERR_SHAPE: return "bad shape (N % 64, K % 128, sizes out of range or M < 0)";
-    case MSQ_ERR_BITS: return "bit map entry outside {0,1,2,3,4,8}";
+    case MSQ_ERR_BITS: return "bit map entry outside {0,1,2,3,4,8,16}";
     case MSQ_ERR_PERM: return "perm_row or perm_col is not a permutation";
     case MSQ_ERR_BUFFER_TOO_SMALL: return "buffer too small";
     case MSQ_ERR_HIP: return "HIP runtime or launch error";

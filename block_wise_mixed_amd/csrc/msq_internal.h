@@ -50,6 +50,11 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows = 0);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 
+// y[m][perm_row[n]] += the exact bf16 product of the 16-bit (passthrough)
+// blocks of every block row: one launch after the quantized kernels.
+hipError_t launch_tile16(const uint16_t* x, int64_t M, const WeightView& w, float* y,
+                         hipStream_t stream);
+
 // Grouped M == 1 decode of count (1 .. 8) matrices in one decode launch (and
 // one prep launch for those with several K ranges); the workspace holds each
 // matrix's single-call workspace in turn.

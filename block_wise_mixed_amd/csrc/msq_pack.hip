@@ -32,12 +32,14 @@ __device__ __forceinline__ int segment_of(int b) {
     case 3: return 2;
     case 4: return 3;
     case 8: return 4;
+    case 16: return 5;
     default: return -1;
   }
 }
 
 constexpr int kScanThreads = 1024;
-__constant__ int kSegBits[5] = {1, 2, 3, 4, 8};
+constexpr int kSegs = 6;
+__constant__ int kSegBits[kSegs] = {1, 2, 3, 4, 8, 16};
 
 // One workgroup.  Thread t owns a contiguous run of the row-major block list,
 // counts the blocks of each bitwidth in it, and after a workgroup-wide
@@ -45,23 +47,23 @@ __constant__ int kSegBits[5] = {1, 2, 3, 4, 8};
 __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* __restrict__ bits,
                                                                 int64_t nblk,
                                                                 uint32_t* __restrict__ off) {
-  __shared__ uint32_t wave_tot[5][kScanThreads / 64];
-  __shared__ uint32_t seg_base[5];
+  __shared__ uint32_t wave_tot[kSegs][kScanThreads / 64];
+  __shared__ uint32_t seg_base[kSegs];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t per = (nblk + kScanThreads - 1) / kScanThreads;
   const int64_t beg = (int64_t)tid * per;
   const int64_t end = beg + per < nblk ? beg + per : nblk;
 
-  uint32_t cnt[5] = {0, 0, 0, 0, 0};
+  uint32_t cnt[kSegs] = {0, 0, 0, 0, 0, 0};
   for (int64_t i = beg; i < end; ++i) {
     int k = segment_of(bits[i]);
     if (k >= 0) cnt[k]++;
   }
   // inclusive scan inside the wave, per segment
-  uint32_t incl[5];
+  uint32_t incl[kSegs];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
+  for (int k = 0; k < kSegs; ++k) {
     uint32_t v = cnt[k];
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* _
     if (lane == 63) wave_tot[k][wave] = v;
   }
   __syncthreads();
-  if (tid < 5) {
+  if (tid < kSegs) {
     // scan of wave totals for segment tid, kept in place as exclusive prefixes
     uint32_t run = 0;
     for (int w = 0; w < kScanThreads / 64; ++w) {
@@ -85,16 +87,16 @@ __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* _
   __syncthreads();
   if (tid == 0) {
     uint32_t acc = 0;
-    for (int k = 0; k < 5; ++k) {
+    for (int k = 0; k < kSegs; ++k) {
       uint32_t total = seg_base[k];
       seg_base[k] = acc;
       acc += (uint32_t)kSegBits[k] * total;
     }
   }
   __syncthreads();
-  uint32_t rank[5];
+  uint32_t rank[kSegs];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
+  for (int k = 0; k < kSegs; ++k) rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
   for (int64_t i = beg; i < end; ++i) {
     const int b = bits[i];
     const int k = segment_of(b);
@@ -167,6 +169,24 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(
     tile[ib][jb] = bf16_to_f32(W[rows[ib] + cols[jb]]);
   }
   __syncthreads();
+
+  // 16-bit block: the bf16 bit patterns themselves (the tile holds them
+  // exactly as fp32), one fragment per chunk: word w is chunk F = w >> 8,
+  // lane l, dword d, halves h = 0, 1; scale and zero point 0.
+  if (b == 16) {
+    if (tid < kBlockRows) {
+      scale[blk * kBlockRows + tid] = 0.0f;
+      zero[blk * kBlockRows + tid] = 0;
+    }
+    uint32_t* out = reinterpret_cast<uint32_t*>(codes + (int64_t)offsets[blk] * 1024);
+    for (int w = tid; w < 256 * 16; w += kPackThreads) {
+      const int F = w >> 8, l = (w >> 2) & 63, d = w & 3;
+      const int ib = 16 * (F >> 2) + (l & 15);
+      const int jb = 32 * (F & 3) + 8 * (l >> 4) + 2 * d;
+      out[w] = (__float_as_uint(tile[ib][jb]) >> 16) | (__float_as_uint(tile[ib][jb + 1]) & 0xFFFF0000u);
+    }
+    return;
+  }
 
   // Scale and zero point: four threads per row, 32 values each, combined by shuffles.
   const float qmax = (float)((1 << b) - 1);

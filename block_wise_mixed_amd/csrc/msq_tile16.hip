@@ -1,0 +1,99 @@
+// 16-bit (passthrough) blocks: tiles kept at bf16 beside quantized ones
+// ("TileQuant" abstract, fugumt.com page: the highest-scoring tiles stay at
+// 16 bits, the kernel computes natively on 16-bit values).  The quantized
+// kernels treat these blocks as pruned (scale 0); this pass adds their exact
+// products afterwards:
+//     y[m][perm_row[n]] += sum over 16-bit blocks (r, c) of row n of
+//                          sum_k x[m][perm_col[128 c + k]] W[n][k].
+// The packed block is the bf16 weight in the v1 layout with one fragment per
+// chunk, so chunk F = 4 rt + kt at lane l is already the matrix instruction's
+// B operand for row tile rt, k-step kt: no unpacking.
+//
+// Workgroup (block row r, 64 rows of M); wavefront rt owns rows 16 rt ..
+// 16 rt + 15 of the block row.  Per 16-bit block: x's 64 x 128 slice is
+// gathered through perm_col into LDS, each wavefront loads its four chunks
+// and issues 4 (m tiles) x 4 (k-steps) matrix instructions.  Every output is
+// owned by one thread, which adds its sum to y once (no atomics; the pass
+// runs after the quantized kernels on the same stream).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "msq_dequant.h"
+#include "msq_internal.h"
+
+namespace msq {
+namespace {
+
+constexpr int kT16Threads = 256;
+constexpr int kT16M = 64;                   // rows of M per workgroup
+constexpr int kT16Stride = kBlockCols + 8;  // LDS row of x, bf16 (+16 bytes against conflicts)
+
+__global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restrict__ x, int M,
+                                                        WeightView w, float* __restrict__ y) {
+  __shared__ __align__(16) uint16_t xs[kT16M * kT16Stride];
+  __shared__ int pc[kBlockCols];
+  const int r = blockIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * kT16M;
+  const int t = threadIdx.x, lane = t & 63;
+  const int rt = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int kk = (int)w.K - 1;
+  f32x4 acc[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  bool any = false;
+  for (int c = 0; c < w.NBc; ++c) {
+    const int64_t blk = (int64_t)r * w.NBc + c;
+    if (w.bits[blk] != 16) continue;
+    any = true;
+    __syncthreads();  // the previous block's readers of xs and pc are done
+    if (t < kBlockCols) {
+      const int p = w.perm_col[(int64_t)c * kBlockCols + t];
+      pc[t] = p < 0 ? 0 : (p > kk ? kk : p);
+    }
+    __syncthreads();
+    for (int e = t; e < kT16M * kBlockCols; e += kT16Threads) {
+      const int mm = e >> 7, k = e & (kBlockCols - 1);
+      const int64_t m = m0 + mm;
+      xs[mm * kT16Stride + k] = m < M ? x[m * w.K + pc[k]] : (uint16_t)0;
+    }
+    const uint8_t* cb = w.codes + (int64_t)w.block_offset[blk] * 1024 + 16 * lane;
+    uint4 b[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) b[kt] = *reinterpret_cast<const uint4*>(cb + 1024 * (4 * rt + kt));
+    __syncthreads();
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        // A fragment: row 16 mt + (lane & 15), columns 32 kt + 8 (lane >> 4) .. + 7
+        const uint4 a = *reinterpret_cast<const uint4*>(
+            xs + (16 * mt + (lane & 15)) * kT16Stride + 32 * kt + 8 * (lane >> 4));
+        acc[mt] = mfma_bf16(as_bf16x8(a), as_bf16x8(b[kt]), acc[mt]);
+      }
+  }
+  if (!any) return;
+  // output (m, n): m = m0 + 16 mt + 4 (lane >> 4) + i, n = 64 r + 16 rt + (lane & 15)
+  const int64_t n = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
+  int64_t on = w.perm_row[n];
+  on = on < 0 ? 0 : (on >= w.N ? w.N - 1 : on);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + 16 * mt + 4 * (lane >> 4) + i;
+      if (m < M) y[m * w.N + on] += acc[mt][i];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_tile16(const uint16_t* x, int64_t M, const WeightView& w, float* y,
+                         hipStream_t stream) {
+  if (M <= 0) return hipSuccess;
+  const dim3 grid((unsigned)w.NBr, (unsigned)((M + kT16M - 1) / kT16M));
+  hipLaunchKernelGGL(k_tile16, grid, dim3(kT16Threads), 0, stream, x, (int)M, w, y);
+  return hipGetLastError();
+}
+
+}  // namespace msq

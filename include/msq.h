@@ -7,7 +7,9 @@
  * (rows by perm_row, columns by perm_col), cut into blocks of 64 rows x 128
  * columns, and every block is round-to-nearest quantized at its own bitwidth
  * b in {0,1,2,3,4,8}: asymmetric, one group of 128 along K per row per block,
- * so each (row, block) has one scale and one integer zero point.  The codes
+ * so each (row, block) has one scale and one integer zero point; or kept at
+ * b == 16, a bf16 passthrough ("TileQuant" abstract, fugumt.com page: tiles
+ * kept at 16 bits beside 8-bit ones).  The codes
  * are packed into one compact buffer, segment by segment in ascending
  * bitwidth, located through a prefix-summed block-offset table.  Inference
  * then computes y = x . W^T by dequantizing every block on the fly.
@@ -42,7 +44,7 @@
  *     perm_row[i]; reordered column j is original column perm_col[j].
  *   - y comes back in the ORIGINAL row order, in fp32.
  *
- * Packed format, version 1 (MSQ_FORMAT_VERSION)
+ * Packed format, version 2 (MSQ_FORMAT_VERSION): version 1 plus b == 16
  * ---------------------------------------------
  * Block (r, c) covers reordered rows 64r..64r+63 and reordered columns
  * 128c..128c+127.  For element (ib, jb) of the block (0 <= ib < 64,
@@ -54,6 +56,11 @@
  * chunk t = F / phi, slot s = F % phi.  The b-bit code sits at bit
  * 16*h + b*s of the little-endian uint32 at byte 1024*t + 16*l + 4*d of the
  * block.  A b-bit block therefore occupies 1024*b bytes.
+ * For b == 16 (phi = 1, chunk t = F) the same rule places the bf16 bit
+ * pattern of the reordered weight: chunk F holds, at lane l, the eight bf16
+ * values of fragment F, ready as the matrix instruction's B operand; such a
+ * block occupies 16384 bytes and stores s = 0, z = 0 (the quantized kernels
+ * treat it as pruned; one more pass adds its exact bf16 product).
  * For b == 3 the code q = q_lo + 4*q_hi is split into planes: q_lo (2 bits)
  * follows the b == 2 rule in chunks 0..1 and q_hi (1 bit) follows the
  * b == 1 rule in chunk 2; the block occupies 3072 bytes.
@@ -63,7 +70,7 @@
  * instruction (row 16*rt + n, columns 32*kt + 8*kg .. +7).
  *
  * Buffer: block (r, c) starts at byte 1024 * block_offset[r][c] of codes.
- * Blocks are laid out segment by segment for b = 1, 2, 3, 4, 8; inside a
+ * Blocks are laid out segment by segment for b = 1, 2, 3, 4, 8, 16; inside a
  * segment in row-major (r, c) order; block_offset is the exclusive prefix
  * sum of bits over that order, in KiB.  0-bit blocks own no bytes and have
  * block_offset == MSQ_NO_BLOCK.  code_bytes = 1024 * sum(bits).
@@ -95,7 +102,7 @@
 extern "C" {
 #endif
 
-#define MSQ_FORMAT_VERSION 1
+#define MSQ_FORMAT_VERSION 2
 #define MSQ_BLOCK_ROWS 64
 #define MSQ_BLOCK_COLS 128
 #define MSQ_NO_BLOCK 0xFFFFFFFFu
@@ -109,7 +116,7 @@ typedef enum {
   MSQ_OK = 0,
   MSQ_ERR_INVALID_ARG = 1,      /* null pointer, misaligned pointer, bad enum */
   MSQ_ERR_SHAPE = 2,            /* N or K not a positive multiple of 64 / 128, M < 0 */
-  MSQ_ERR_BITS = 3,             /* a bits entry outside {0,1,2,3,4,8} */
+  MSQ_ERR_BITS = 3,             /* a bits entry outside {0,1,2,3,4,8,16} */
   MSQ_ERR_PERM = 4,             /* perm_row or perm_col is not a permutation */
   MSQ_ERR_BUFFER_TOO_SMALL = 5, /* code_bytes or workspace smaller than needed */
   MSQ_ERR_HIP = 6,              /* a HIP launch or runtime call failed */
@@ -128,7 +135,7 @@ typedef struct {
   int64_t scale_bytes;         /* 4 * N * K / 128 */
   int64_t zero_bytes;          /* N * K / 128 */
   int64_t offset_bytes;        /* 4 * (N/64) * (K/128) */
-  int64_t blocks_per_bits[9];  /* histogram of bits; index = bitwidth */
+  int64_t blocks_per_bits[17]; /* histogram of bits; index = bitwidth */
   double mean_bits;            /* sum(bits) / number of blocks */
 } msq_sizes;
 
@@ -136,7 +143,7 @@ typedef struct {
  * the pointers and never frees them. */
 typedef struct {
   int64_t N, K;               /* N % 64 == 0, K % 128 == 0, both > 0 */
-  const uint8_t *bits;        /* [N/64][K/128], values in {0,1,2,3,4,8} */
+  const uint8_t *bits;        /* [N/64][K/128], values in {0,1,2,3,4,8,16} */
   const int32_t *perm_row;    /* [N]: reordered row i <- original row perm_row[i] */
   const int32_t *perm_col;    /* [K]: reordered col j <- original col perm_col[j]; 16-byte aligned */
   uint32_t *block_offset;     /* [N/64][K/128] in KiB; MSQ_NO_BLOCK for 0-bit */
@@ -144,6 +151,9 @@ typedef struct {
   float *scale;               /* [N/64][K/128][64], 16-byte aligned */
   uint8_t *zero;              /* [N/64][K/128][64], 16-byte aligned */
   int64_t code_bytes;         /* size of the codes buffer in bytes */
+  int64_t tile16_blocks;      /* number of 16-bit blocks (blocks_per_bits[16] of msq_plan);
+                                 msq_quantize_pack refuses a mismatch, msq_gemm skips the
+                                 16-bit pass when 0 */
 } msq_weight;
 
 /* Host only; needs no GPU.  Validates N, K, the bit map and both

@@ -43,7 +43,7 @@ def test_status_strings(lib):
     for s in range(8):
         assert lib.msq_status_string(s)
     assert lib.msq_status_string(99) == b"unknown status"
-    assert lib.msq_format_version() == 1
+    assert lib.msq_format_version() == 2 == msq.FORMAT_VERSION
 
 
 def _plan_raw(lib, N, K, bits, pr, pc):
@@ -62,7 +62,7 @@ def test_plan_sizes(lib):
     total = int(c.bits.astype(np.int64).sum())
     assert out.code_bytes == 1024 * total
     assert out.scale_bytes == 4 * 256 * 4 and out.zero_bytes == 256 * 4 and out.offset_bytes == 4 * 16
-    hist = np.bincount(c.bits.ravel(), minlength=9)
+    hist = np.bincount(c.bits.ravel(), minlength=17)
     assert list(out.blocks_per_bits) == list(hist)
     assert out.mean_bits == pytest.approx(total / 16)
 
@@ -238,3 +238,22 @@ def test_reorder_host_checks(lib):
     assert f(264, 64, 128, 1, 256, 256, 256, 1 << 20, None) == 1   # saliency not 16-byte aligned
     assert f(256, 65, 128, 1, 256, 256, 256, 1 << 20, None) == 2
     assert f(256, 64, 128, 1, 256, 256, 256, 16, None) == 5
+
+
+def test_plan_counts_passthrough_blocks(lib):
+    """16-bit blocks are accepted, counted and sized at 16 KiB each; other values are not."""
+    c = synth.random_case(128, 256, 4, dist={16: .5, 2: .5})
+    st, out = _plan_raw(lib, 128, 256, c.bits, c.perm_row, c.perm_col)
+    assert st == OK
+    assert out.blocks_per_bits[16] == int((c.bits == 16).sum()) > 0
+    assert out.code_bytes == 1024 * int(c.bits.astype(np.int64).sum())
+    for bad in (5, 6, 7, 9, 15, 17, 32):
+        st, _ = _plan_raw(lib, 128, 256, np.full_like(c.bits, bad), c.perm_row, c.perm_col)
+        assert st == 3
+
+
+def test_negative_passthrough_count_rejected(lib):
+    w = _fake_weight()
+    w.tile16_blocks = -1
+    x = 1 << 41
+    assert lib.msq_gemm(x, 1, ctypes.byref(w), x, x, 1 << 30, None) == INVALID

@@ -1,0 +1,75 @@
+"""GPU parity with 16-bit (bf16 passthrough) blocks beside quantized ones: packing
+bit-exact, y against the oracle within tolerance through every kernel path, exact on
+the integer lattice, and bitwise identical between the single and grouped calls."""
+import numpy as np
+import pytest
+
+import oracle
+from block_wise_mixed_amd import synth
+
+from test_gpu_parity import TOL, check_pack, check_y, _bf16_cuda
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+MIX16 = {0: .05, 1: .1, 2: .3, 3: .15, 4: .1, 8: .15, 16: .15}
+TQ = {8: .7, 16: .3}  # tiles at 8 or 16 bits only, as the pages' 16/8 variant
+
+
+@pytest.fixture(scope="module")
+def msq():
+    import block_wise_mixed_amd as m
+    m.load_library()
+    assert torch.cuda.is_available()
+    return m
+
+
+@pytest.mark.parametrize("N,K,dist,seed", [(256, 1024, MIX16, 80), (192, 384, TQ, 81),
+                                           (64, 128, {16: 1.0}, 82), (512, 8192, MIX16, 83)])
+def test_pack_and_products(msq, monkeypatch, N, K, dist, seed):
+    c = synth.random_case(N, K, seed, dist=dist)
+    pw, ref = check_pack(msq, c)
+    assert pw.tile16_blocks == int((c.bits == 16).sum())
+    for M, kernel in ((1, "auto"), (4, "auto"), (4, "gemm"), (64, "gemv"), (130, "auto")):
+        check_y(msq, pw, c, ref, M, kernel=kernel)
+    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")  # M = 1 with the workgroups reordering x
+    check_y(msq, pw, c, ref, 1)
+
+
+def test_integer_lattice_exact(msq):
+    """Integer x and small integer W (bf16-exact in the 16-bit blocks): every product
+    and sum is exact, so y must equal the oracle exactly."""
+    c, _ = synth.lattice_case(192, 512, 84, dist={16: .5, 1: .25, 4: .25})
+    W = oracle.bf16_to_f32(c.W).copy()
+    Wr = W[np.ix_(c.perm_row, c.perm_col)]
+    pt = np.repeat(np.repeat(c.bits == 16, 64, axis=0), 128, axis=1)
+    Wr[pt] = np.random.default_rng(84).integers(-8, 8, int(pt.sum())).astype(np.float32)
+    W[np.ix_(c.perm_row, c.perm_col)] = Wr
+    c.W = synth.f32_to_bf16_bits(W)
+    pw, ref = check_pack(msq, c)
+    g = np.random.default_rng(5)
+    for M in (1, 3, 70):
+        x = synth.f32_to_bf16_bits(g.integers(-8, 9, (M, 512)).astype(np.float32))
+        check_y(msq, pw, c, ref, M, exact=True, x=x)
+
+
+def test_group_matches_single(msq):
+    cases = [synth.random_case(256, 2048, 85 + i, dist=d) for i, d in enumerate((MIX16, TQ))]
+    packed = [check_pack(msq, c)[0] for c in cases]
+    for M in (1, 200):
+        xs = [_bf16_cuda(cases[0].x(M))] * 2
+        outs = msq.gemm_group(xs, packed)
+        for x, pw, y in zip(xs, packed, outs):
+            assert torch.equal(y, msq.gemm(x, pw))
+
+
+def test_descriptor_count_must_match(msq):
+    """msq_quantize_pack refuses a descriptor whose 16-bit block count is wrong."""
+    import ctypes
+    c = synth.random_case(128, 256, 86, dist=MIX16)
+    pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
+    w = pw.descriptor()
+    w.tile16_blocks = pw.tile16_blocks + 1
+    Wd = _bf16_cuda(c.W)
+    lib = msq.load_library()
+    assert lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), None) == 1
