@@ -247,6 +247,56 @@ def alloc_leg(msq, synth, torch, log):
             "note": "batched greedy over a 70B model's blocks, synthetic utilities; median of 3"}
 
 
+def tile16_leg(msq, synth, torch, np, log):
+    """A TileQuant-style weight (tiles at 8 or 16 bits, 70/30) of the Llama-3-8B gate_proj
+    shape (14336 x 4096): M = 1 decode in a HIP graph over rotating copies, and M = 2048
+    prefill; the quantized kernels plus the k_tile16 pass for the bf16 tiles."""
+    c = synth.random_case(14336, 4096, 90, dist={8: 0.7, 16: 0.3})
+    pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
+    dev = pw.bits.device
+    out = {"N": c.N, "K": c.K, "mix": "8-bit 0.7, 16-bit 0.3", "tile16_blocks": pw.tile16_blocks,
+           "mean_bits": round(float(c.bits.astype(np.float64).mean()), 4)}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    x = torch.from_numpy(c.x(1).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((1, c.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(msq.workspace_bytes(1, c.N, c.K), 256), dtype=torch.uint8, device=dev)
+    R = max(2, min(64, int(np.ceil((1 << 30) / pw.packed_bytes))))
+    cps = [pw] + [pw.clone() for _ in range(R - 1)]
+    msq.gemm(x, pw, out=y, workspace=ws)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for cp in cps:
+            msq.gemm(x, cp, out=y, workspace=ws)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (3 * R)
+    out.update({"decode_us": round(us, 3), "decode_gbps": round(decode_bytes(pw, 1) / (us * 1e-6) / 1e9, 1)})
+    del g, cps
+    M = 2048
+    x = torch.from_numpy(c.x(M).view(np.int16)).view(torch.bfloat16).to(dev)
+    y = torch.empty((M, c.N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(msq.workspace_bytes(M, c.N, c.K), 256), dtype=torch.uint8, device=dev)
+    msq.gemm(x, pw, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(3):
+        msq.gemm(x, pw, out=y, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 3
+    flops = 2.0 * M * c.N * c.K * float((c.bits != 0).mean())
+    out.update({"prefill_M": M, "prefill_us": round(us, 1),
+                "prefill_tflops": round(flops / (us * 1e-6) / 1e12, 1)})
+    log(f"tile16 (8/16 mix): decode {out['decode_us']} us ({out['decode_gbps']} GB/s), "
+        f"prefill M=2048 {out['prefill_us']} us ({out['prefill_tflops']} TFLOP/s)")
+    return out
+
+
 def reorder_leg(msq, torch, log):
     """Channel reordering for one gate_proj-shaped saliency map (28672 x 8192 fp32,
     940 MB, read once): time per call over 5 calls bracketed by events."""
@@ -571,6 +621,7 @@ def main() -> int:
 
     alloc = alloc_leg(msq, synth, torch, log)
     reorder = reorder_leg(msq, torch, log)
+    tile16 = tile16_leg(msq, synth, torch, np, log)
 
     configs, context = None, None
     if not args.no_configs:
@@ -601,6 +652,7 @@ def main() -> int:
         "pack": pack,
         "alloc": alloc,
         "reorder": reorder,
+        "tile16": tile16,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "configs": configs,

@@ -1069,6 +1069,12 @@ int env_int(const char* name, int dflt) {
 // wavefronts (two per CU) and at most 8 splits.  M > 1: about 512
 // workgroups.  MSQ_GEMV_SPLIT and MSQ_GEMV_WAVES override the split count
 // and, for M == 1, the wavefronts per workgroup (tuning only).
+const uint16_t* gemv_reordered_x(void* workspace, const GemvPlan& p, int64_t M, int64_t N) {
+  if (M <= 1) return nullptr;
+  return reinterpret_cast<const uint16_t*>(reinterpret_cast<uint8_t*>(workspace) +
+                                           part_bytes(p, M, N));
+}
+
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   GemvPlan p{};
   const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);

@@ -169,13 +169,17 @@ msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, f
   if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
   const msq::WeightView v = view_of(w);
   hipError_t e;
+  const uint16_t* xr = nullptr;  // reordered x left in the workspace (M > 1)
   if (kernel == MSQ_KERNEL_GEMV) {
     const msq::GemvPlan p = msq::plan_gemv(M, w->N, w->K);
     e = msq::launch_gemv(x_bf16, M, v, y, workspace, p, stream);
+    xr = msq::gemv_reordered_x(workspace, p, M, w->N);
   } else {
     e = msq::launch_gemm(x_bf16, M, v, y, workspace, stream);
+    xr = reinterpret_cast<const uint16_t*>(workspace);
   }
-  if (e == hipSuccess && w->tile16_blocks > 0) e = msq::launch_tile16(x_bf16, M, v, y, stream);
+  if (e == hipSuccess && w->tile16_blocks > 0)
+    e = msq::launch_tile16(x_bf16, xr, M, v, y, stream);
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
@@ -231,8 +235,13 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
   for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
   hipError_t e = M == 1 ? msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream)
                         : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
-  for (int i = 0; i < count && e == hipSuccess; ++i)
-    if (w[i]->tile16_blocks > 0) e = msq::launch_tile16(x_bf16[i], M, v[i], y[i], stream);
+  // M > 16: job i's reordered x starts its workspace share
+  const uint8_t* share = reinterpret_cast<const uint8_t*>(workspace);
+  for (int i = 0; i < count && e == hipSuccess; ++i) {
+    const uint16_t* xr = M == 1 ? nullptr : reinterpret_cast<const uint16_t*>(share);
+    if (w[i]->tile16_blocks > 0) e = msq::launch_tile16(x_bf16[i], xr, M, v[i], y[i], stream);
+    share += (msq::gemm_workspace_bytes(M, w[i]->N, w[i]->K) + 255) & ~(size_t)255;
+  }
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 

@@ -51,9 +51,12 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 
 // y[m][perm_row[n]] += the exact bf16 product of the 16-bit (passthrough)
-// blocks of every block row: one launch after the quantized kernels.
-hipError_t launch_tile16(const uint16_t* x, int64_t M, const WeightView& w, float* y,
-                         hipStream_t stream);
+// blocks of every block row: one launch after the quantized kernels.  xr:
+// the reordered x [M][K] those kernels left in the workspace, or null.
+hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const WeightView& w,
+                         float* y, hipStream_t stream);
+// The reordered x [M][K] that launch_gemv (M > 1) leaves in its workspace.
+const uint16_t* gemv_reordered_x(void* workspace, const GemvPlan& p, int64_t M, int64_t N);
 
 // Grouped M == 1 decode of count (1 .. 8) matrices in one decode launch (and
 // one prep launch for those with several K ranges); the workspace holds each

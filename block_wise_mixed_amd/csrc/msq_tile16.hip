@@ -9,10 +9,11 @@
 // chunk, so chunk F = 4 rt + kt at lane l is already the matrix instruction's
 // B operand for row tile rt, k-step kt: no unpacking.
 //
-// Workgroup (block row r, 64 rows of M); wavefront rt owns rows 16 rt ..
-// 16 rt + 15 of the block row.  Per 16-bit block: x's 64 x 128 slice is
-// gathered through perm_col into LDS, each wavefront loads its four chunks
-// and issues 4 (m tiles) x 4 (k-steps) matrix instructions.  Every output is
+// Workgroup (block row r, 16 or 64 rows of M); wavefront rt owns rows
+// 16 rt .. 16 rt + 15 of the block row.  Per 16-bit block: x's slice is
+// staged in LDS (from the reordered x the gather kernel left in the
+// workspace, or gathered through perm_col at M == 1), each wavefront loads
+// its four chunks and issues (m tiles) x 4 (k-steps) matrix instructions.  Every output is
 // owned by one thread, which adds its sum to y once (no atomics; the pass
 // runs after the quantized kernels on the same stream).
 #include <hip/hip_runtime.h>
@@ -26,36 +27,52 @@ namespace msq {
 namespace {
 
 constexpr int kT16Threads = 256;
-constexpr int kT16M = 64;                   // rows of M per workgroup
 constexpr int kT16Stride = kBlockCols + 8;  // LDS row of x, bf16 (+16 bytes against conflicts)
 
-__global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restrict__ x, int M,
+// kMT m tiles of 16 rows per workgroup (1 for small M, 4 otherwise).  xr: x
+// already reordered along K ([M][K], the gather kernel's output in the
+// caller's workspace), read with 16-byte loads; null: x gathered through
+// perm_col here.
+template <int kMT>
+__global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restrict__ x,
+                                                        const uint16_t* __restrict__ xr, int M,
                                                         WeightView w, float* __restrict__ y) {
-  __shared__ __align__(16) uint16_t xs[kT16M * kT16Stride];
+  constexpr int kRows = 16 * kMT;
+  __shared__ __align__(16) uint16_t xs[kRows * kT16Stride];
   __shared__ int pc[kBlockCols];
   const int r = blockIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.y * kT16M;
+  const int64_t m0 = (int64_t)blockIdx.y * kRows;
   const int t = threadIdx.x, lane = t & 63;
   const int rt = __builtin_amdgcn_readfirstlane(t >> 6);
   const int kk = (int)w.K - 1;
-  f32x4 acc[4];
+  f32x4 acc[kMT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < kMT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   bool any = false;
   for (int c = 0; c < w.NBc; ++c) {
     const int64_t blk = (int64_t)r * w.NBc + c;
     if (w.bits[blk] != 16) continue;
     any = true;
     __syncthreads();  // the previous block's readers of xs and pc are done
-    if (t < kBlockCols) {
-      const int p = w.perm_col[(int64_t)c * kBlockCols + t];
-      pc[t] = p < 0 ? 0 : (p > kk ? kk : p);
-    }
-    __syncthreads();
-    for (int e = t; e < kT16M * kBlockCols; e += kT16Threads) {
-      const int mm = e >> 7, k = e & (kBlockCols - 1);
-      const int64_t m = m0 + mm;
-      xs[mm * kT16Stride + k] = m < M ? x[m * w.K + pc[k]] : (uint16_t)0;
+    if (xr) {
+      // rows past M repeat row M - 1 (their outputs are never stored)
+      for (int e = t; e < kRows * 16; e += kT16Threads) {
+        const int mm = e >> 4, q = e & 15;
+        const int64_t m = min(m0 + mm, (int64_t)M - 1);
+        *reinterpret_cast<uint4*>(xs + mm * kT16Stride + 8 * q) =
+            *reinterpret_cast<const uint4*>(xr + m * w.K + (int64_t)c * kBlockCols + 8 * q);
+      }
+    } else {
+      if (t < kBlockCols) {
+        const int p = w.perm_col[(int64_t)c * kBlockCols + t];
+        pc[t] = p < 0 ? 0 : (p > kk ? kk : p);
+      }
+      __syncthreads();
+      for (int e = t; e < kRows * kBlockCols; e += kT16Threads) {
+        const int mm = e >> 7, k = e & (kBlockCols - 1);
+        const int64_t m = min(m0 + mm, (int64_t)M - 1);
+        xs[mm * kT16Stride + k] = x[m * w.K + pc[k]];
+      }
     }
     const uint8_t* cb = w.codes + (int64_t)w.block_offset[blk] * 1024 + 16 * lane;
     uint4 b[4];
@@ -63,7 +80,7 @@ __global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restri
     for (int kt = 0; kt < 4; ++kt) b[kt] = *reinterpret_cast<const uint4*>(cb + 1024 * (4 * rt + kt));
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+    for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         // A fragment: row 16 mt + (lane & 15), columns 32 kt + 8 (lane >> 4) .. + 7
@@ -78,7 +95,7 @@ __global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restri
   int64_t on = w.perm_row[n];
   on = on < 0 ? 0 : (on >= w.N ? w.N - 1 : on);
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < kMT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = m0 + 16 * mt + 4 * (lane >> 4) + i;
@@ -88,11 +105,16 @@ __global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restri
 
 }  // namespace
 
-hipError_t launch_tile16(const uint16_t* x, int64_t M, const WeightView& w, float* y,
-                         hipStream_t stream) {
+hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const WeightView& w,
+                         float* y, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  const dim3 grid((unsigned)w.NBr, (unsigned)((M + kT16M - 1) / kT16M));
-  hipLaunchKernelGGL(k_tile16, grid, dim3(kT16Threads), 0, stream, x, (int)M, w, y);
+  if (M <= 16) {
+    hipLaunchKernelGGL(k_tile16<1>, dim3((unsigned)w.NBr, 1u), dim3(kT16Threads), 0, stream, x, xr,
+                       (int)M, w, y);
+  } else {
+    const dim3 grid((unsigned)w.NBr, (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL(k_tile16<4>, grid, dim3(kT16Threads), 0, stream, x, xr, (int)M, w, y);
+  }
   return hipGetLastError();
 }
 
