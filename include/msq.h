@@ -175,9 +175,10 @@ msq_status msq_plan(int64_t N, int64_t K, const uint8_t *bits_host,
  * before launching it copies bits, perm_row and perm_col back to the host
  * (ordered on stream, then waited for) and validates them exactly as
  * msq_plan does, so a bad descriptor is refused instead of read out of
- * bounds.  Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer),
- * MSQ_ERR_SHAPE, MSQ_ERR_BITS, MSQ_ERR_PERM, MSQ_ERR_BUFFER_TOO_SMALL
- * (w->code_bytes below 1024 * sum(bits)), MSQ_ERR_HIP. */
+ * bounds.  Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer, or
+ * w->tile16_blocks not the bit map's count of 16-bit blocks), MSQ_ERR_SHAPE,
+ * MSQ_ERR_BITS, MSQ_ERR_PERM, MSQ_ERR_BUFFER_TOO_SMALL (w->code_bytes below
+ * 1024 * sum(bits)), MSQ_ERR_HIP. */
 msq_status msq_quantize_pack(const uint16_t *W_bf16, const msq_weight *w,
                              hipStream_t stream);
 
