@@ -26,10 +26,12 @@
 namespace msq {
 namespace {
 
+extern __shared__ __align__(16) unsigned char smem_t16[];
+
 constexpr int kT16Threads = 256;
 constexpr int kT16Stride = kBlockCols + 8;  // LDS row of x, bf16 (+16 bytes against conflicts)
 
-// kMT m tiles of 16 rows per workgroup (1 for small M, 4 otherwise).  xr: x
+// kMT m tiles of 16 rows per workgroup (4: M > 16).  xr: x
 // already reordered along K ([M][K], the gather kernel's output in the
 // caller's workspace), read with 16-byte loads; null: x gathered through
 // perm_col here.
@@ -103,13 +105,104 @@ __global__ __launch_bounds__(kT16Threads) void k_tile16(const uint16_t* __restri
     }
 }
 
+// M <= 16: the four wavefronts of a workgroup (one block row) take the
+// row's 16-bit blocks c with c % 4 == wave independently, each computing
+// all 64 rows of its blocks (16 chunks, 16 matrix instructions per block),
+// with no barrier per block; their sums are added through LDS in wavefront
+// order at the end.  A operands straight from the reordered x (M > 1) or,
+// at M == 1, from x gathered once per workgroup into LDS (row 0 of the
+// operand; the other rows zero).
+__global__ __launch_bounds__(kT16Threads) void k_tile16_small(const uint16_t* __restrict__ x,
+                                                              const uint16_t* __restrict__ xr,
+                                                              int M, WeightView w,
+                                                              float* __restrict__ y) {
+  __shared__ f32x4 red[4][4][64];
+  uint16_t* xg = reinterpret_cast<uint16_t*>(smem_t16);  // M == 1: x reordered, [K]
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kk = (int)w.K - 1;
+  if (!xr) {
+    for (int64_t j = threadIdx.x; j < w.K; j += kT16Threads) {
+      const int p = w.perm_col[j];
+      xg[j] = x[p < 0 ? 0 : (p > kk ? kk : p)];
+    }
+    __syncthreads();
+  }
+  const int arow = lane & 15, acol = 8 * (lane >> 4);  // A fragment: row, first column
+  f32x4 acc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the row's bit map and offsets 64 columns at a time (lane = column); this
+  // wavefront's 16-bit blocks are the set bits of a ballot
+  for (int c0 = 0; c0 < w.NBc; c0 += 64) {
+    const int64_t rb = (int64_t)r * w.NBc + c0;
+    const bool in = c0 + lane < w.NBc;
+    const int bl = in ? w.bits[rb + lane] : 0;
+    const uint32_t ol = in ? w.block_offset[rb + lane] : 0u;
+    uint64_t todo = __ballot(bl == 16) & (0x1111111111111111ull << wave);
+    while (todo) {
+      const int p = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int c = c0 + p;
+      const uint32_t off = __builtin_amdgcn_readlane(ol, p);
+      const uint8_t* cb = w.codes + (int64_t)off * 1024 + 16 * lane;
+      uint4 b[16];
+#pragma unroll
+      for (int f = 0; f < 16; ++f) b[f] = *reinterpret_cast<const uint4*>(cb + 1024 * f);
+      uint4 a[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int64_t col = (int64_t)c * kBlockCols + 32 * kt + acol;
+        if (xr) {
+          const int64_t m = min(arow, M - 1);  // rows past M are never stored
+          a[kt] = *reinterpret_cast<const uint4*>(xr + m * w.K + col);
+        } else {
+          // row 0 from the LDS copy; the other rows of the operand are zero
+          const uint4 v = *reinterpret_cast<const uint4*>(xg + col);
+          a[kt] = arow == 0 ? v : uint4{0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          acc[rt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(b[4 * rt + kt]), acc[rt]);
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) red[wave][rt][lane] = acc[rt];
+  __syncthreads();
+  if (wave != 0) return;
+  // output (m, n): m = 4 (lane >> 4) + i, n = 64 r + 16 rt + (lane & 15)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    f32x4 s = red[0][rt][lane];
+#pragma unroll
+    for (int k = 1; k < 4; ++k) {
+      const f32x4 t = red[k][rt][lane];
+      s = f32x4{s[0] + t[0], s[1] + t[1], s[2] + t[2], s[3] + t[3]};
+    }
+    const int64_t n = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
+    int64_t on = w.perm_row[n];
+    on = on < 0 ? 0 : (on >= w.N ? w.N - 1 : on);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * (lane >> 4) + i;
+      if (m < M) y[(int64_t)m * w.N + on] += s[i];
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const WeightView& w,
                          float* y, hipStream_t stream) {
   if (M <= 0) return hipSuccess;
-  if (M <= 16) {
-    hipLaunchKernelGGL(k_tile16<1>, dim3((unsigned)w.NBr, 1u), dim3(kT16Threads), 0, stream, x, xr,
+  // the small-M kernel keeps x's reordered row in LDS when it has no xr
+  if (M <= 16 && (xr || w.K <= 32768)) {
+    const size_t lds = xr ? 0 : (size_t)w.K * 2;  // M == 1: the reordered x row
+    hipLaunchKernelGGL(k_tile16_small, dim3((unsigned)w.NBr), dim3(kT16Threads), lds, stream, x, xr,
                        (int)M, w, y);
   } else {
     const dim3 grid((unsigned)w.NBr, (unsigned)((M + 63) / 64));
