@@ -194,6 +194,88 @@ __global__ __launch_bounds__(kT16Threads) void k_tile16_small(const uint16_t* __
   }
 }
 
+// M > 16: workgroup (block row r, 64 rows of M); as the small-M kernel, each
+// wavefront takes the 16-bit blocks c = wave (mod 4) of the row from a
+// ballot, with no barrier per block, and computes all 64 x 64 outputs of its
+// blocks: A fragments (4 m tiles x 4 k-steps) straight from the reordered x
+// in the workspace, B = the block's 16 chunks, 64 matrix instructions.  The
+// four wavefronts' sums are added through LDS in wavefront order at the end.
+__global__ __launch_bounds__(kT16Threads) void k_tile16_large(const uint16_t* __restrict__ xr,
+                                                              int M, WeightView w,
+                                                              float* __restrict__ y) {
+  f32x4* red = reinterpret_cast<f32x4*>(smem_t16);  // [3][16][64]: wavefronts 1..3
+  const int r = blockIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.y * 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int arow = lane & 15, acol = 8 * (lane >> 4);
+  f32x4 acc[4][4];  // [mt][rt]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < w.NBc; c0 += 64) {
+    const int64_t rb = (int64_t)r * w.NBc + c0;
+    const bool in = c0 + lane < w.NBc;
+    const int bl = in ? w.bits[rb + lane] : 0;
+    const uint32_t ol = in ? w.block_offset[rb + lane] : 0u;
+    uint64_t todo = __ballot(bl == 16) & (0x1111111111111111ull << wave);
+    while (todo) {
+      const int p = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int c = c0 + p;
+      const uint32_t off = __builtin_amdgcn_readlane(ol, p);
+      const uint8_t* cb = w.codes + (int64_t)off * 1024 + 16 * lane;
+      uint4 b[16];
+#pragma unroll
+      for (int f = 0; f < 16; ++f) b[f] = *reinterpret_cast<const uint4*>(cb + 1024 * f);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        // rows past M repeat row M - 1 (their outputs are never stored)
+        const int64_t m = min(m0 + 16 * mt + arow, (int64_t)M - 1);
+        const uint16_t* src = xr + m * w.K + (int64_t)c * kBlockCols + acol;
+        uint4 a[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) a[kt] = *reinterpret_cast<const uint4*>(src + 32 * kt);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+            acc[mt][rt] = mfma_bf16(as_bf16x8(a[kt]), as_bf16x8(b[4 * rt + kt]), acc[mt][rt]);
+      }
+    }
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) red[((wave - 1) * 16 + 4 * mt + rt) * 64 + lane] = acc[mt][rt];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // output (m, n): m = m0 + 16 mt + 4 (lane >> 4) + i, n = 64 r + 16 rt + (lane & 15)
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int64_t n = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
+    int64_t on = w.perm_row[n];
+    on = on < 0 ? 0 : (on >= w.N ? w.N - 1 : on);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 s = acc[mt][rt];
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        const f32x4 t = red[(k * 16 + 4 * mt + rt) * 64 + lane];
+        s = f32x4{s[0] + t[0], s[1] + t[1], s[2] + t[2], s[3] + t[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 16 * mt + 4 * (lane >> 4) + i;
+        if (m < M) y[m * w.N + on] += s[i];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const WeightView& w,
@@ -204,6 +286,10 @@ hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const
     const size_t lds = xr ? 0 : (size_t)w.K * 2;  // M == 1: the reordered x row
     hipLaunchKernelGGL(k_tile16_small, dim3((unsigned)w.NBr), dim3(kT16Threads), lds, stream, x, xr,
                        (int)M, w, y);
+  } else if (xr) {
+    const dim3 grid((unsigned)w.NBr, (unsigned)((M + 63) / 64));
+    hipLaunchKernelGGL(k_tile16_large, grid, dim3(kT16Threads), (size_t)3 * 16 * 64 * 16, stream,
+                       xr, (int)M, w, y);
   } else {
     const dim3 grid((unsigned)w.NBr, (unsigned)((M + 63) / 64));
     hipLaunchKernelGGL(k_tile16<4>, grid, dim3(kT16Threads), 0, stream, x, xr, (int)M, w, y);
