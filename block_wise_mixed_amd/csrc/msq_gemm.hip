@@ -190,7 +190,7 @@ __host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 1
 // One stage of the pipeline in LDS.
 struct Stage {
   uint4* a;      // x_r tile [kBM][16 chunks], swizzled
-  uint4* codes;  // [BR][8 chunks][64 lanes]
+  uint4* codes;  // [BR][CH chunks][64 lanes]; CH = 8, or 16 when 16-bit blocks occur
 };
 
 // Chunk of a B-bit block holding (the low plane of) fragment F.
@@ -229,11 +229,28 @@ __device__ __forceinline__ void read_a(const Stage& st, const uint32_t (&apk)[4]
       A[kt][mt] = as_bf16x8(*reinterpret_cast<const uint4*>(abase + apk[kt] + 4096 * mt));
 }
 
-template <int B>
+// 16-bit block: chunk F is the B operand of fragment F as it is (bf16
+// weights, no unpack, no scale), so the products go straight into acc.
+template <int CH>
+__device__ __forceinline__ void group_mfma16(const Stage& st, int q, const bf16x8 (&A)[4][4],
+                                             f32x4 (&acc)[4][4]) {
+  static_assert(CH == 16, "16-bit blocks need 16 chunks per block in LDS");
+  const uint4* cb = st.codes + q * CH * 64 + (threadIdx.x & 63);
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bf16x8 bop = as_bf16x8(cb[64 * (4 * rt + kt)]);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][rt] = mfma_bf16(A[kt][mt], bop, acc[mt][rt]);
+    }
+}
+
+template <int B, int CH>
 __device__ __forceinline__ void group_mfma(const Stage& st, int q, const bf16x8 (&A)[4][4],
                                            const float (&sc)[4], f32x4 (&acc)[4][4]) {
   const int lane = threadIdx.x & 63;
-  const uint4* cb = st.codes + q * 8 * 64 + lane;
+  const uint4* cb = st.codes + q * CH * 64 + lane;
   auto rstep = [&](auto RTc) __attribute__((always_inline)) {
     constexpr int rt = decltype(RTc)::value;
     constexpr int k0 = lo_chunk<B, 4 * rt>(), k1 = lo_chunk<B, 4 * rt + 3>();
@@ -297,10 +314,11 @@ constexpr int kTUnits = 4;  // units of 4 rows per thread: BR * 32 * 16 / (128 *
 // Workgroup barrier that waits for the wavefront's LDS operations only (loads
 // from global memory stay in flight); the empty asm statements keep the
 // compiler from moving memory operations across it.
-// Bitwidth as the quantized products see it: 16-bit (passthrough) blocks
-// count as pruned here (their scale is 0, so the correction skips them too);
-// k_tile16 adds their products afterwards.
-__device__ __forceinline__ int quantized_bits(int b) { return b == 16 ? 0 : b; }
+// Bitwidth as the products see it.  CH == 8 (weights without 16-bit
+// blocks, or kernels that leave them to k_tile16): 16-bit blocks count as
+// pruned (their scale is 0, so the correction skips them too).
+template <int CH>
+__device__ __forceinline__ int tile_bits(int b) { return CH == 16 || b != 16 ? b : 0; }
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
@@ -314,7 +332,7 @@ __device__ __forceinline__ void lds_barrier() {
 // and y is written (scattered through perm_row); otherwise the tile's share
 // of a K split goes to part[m][reordered row] (summed over the splits, in
 // split order, by the split-reduce kernel).
-template <int BR>
+template <int BR, int CH>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                           const uint16_t* __restrict__ sxs, int M,
                                           const WeightView& w, float* __restrict__ y, int mtile,
@@ -324,7 +342,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   constexpr bool kSingleA = TileCfg<BR>::kSingleA;
   static_assert(kTUnits * kThreads == kBR * 32 * 16, "T units per thread");
   __shared__ __align__(16) uint4 a0[kBM * 16], a1[kSingleA ? 16 : kBM * 16];
-  __shared__ __align__(16) uint4 c0s[kBR * 8 * 64], c1s[kBR * 8 * 64];
+  __shared__ __align__(16) uint4 c0s[kBR * CH * 64], c1s[kBR * CH * 64];
   __shared__ uint32_t toff[kBR][kTabG];
   __shared__ uint8_t tbits[kBR][kTabG];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -352,7 +370,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     }
     const int64_t blk = (int64_t)(rb + q) * w.NBc + c;
     off = __builtin_amdgcn_readfirstlane(w.block_offset[blk]);
-    return quantized_bits(__builtin_amdgcn_readfirstlane(w.bits[blk]));
+    return tile_bits<CH>(__builtin_amdgcn_readfirstlane(w.bits[blk]));
   };
 
   // Direct-to-LDS copies of group c into stage st: wavefront w copies rows
@@ -375,10 +393,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     const int b = block_at(q, c, off);
     const uint8_t* cb = w.codes + (int64_t)off * 1024 + 16 * lane;
 #pragma unroll
-    for (int t = 0; t < 8; t += 2)
+    for (int t = 0; t < CH; t += 2)
       if (t + half < b)
         __builtin_amdgcn_global_load_lds(cb + 1024 * (t + half),
-                                         (lds_void*)(st.codes + (q * 8 + t + half) * 64), 16, 0, 0);
+                                         (lds_void*)(st.codes + (q * CH + t + half) * 64), 16, 0, 0);
   };
 
   // the workgroup's bit map and offsets for the first tabG groups of its range
@@ -386,7 +404,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     const int q = i / tabG, c = i - (i / tabG) * tabG;
     const int rr = rb + q;
     const int64_t blk = (int64_t)(rr < w.NBr ? rr : 0) * w.NBc + g0 + c;
-    tbits[q][c] = rr < w.NBr ? quantized_bits(w.bits[blk]) : 0;
+    tbits[q][c] = rr < w.NBr ? tile_bits<CH>(w.bits[blk]) : 0;
     toff[q][c] = rr < w.NBr ? w.block_offset[blk] : 0u;
   }
   __syncthreads();
@@ -414,11 +432,14 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     const int b = block_at(wn, c, unused_off);
     switch (b) {
       case 0: break;
-      case 1: group_mfma<1>(st, wn, A, sc, acc); break;
-      case 2: group_mfma<2>(st, wn, A, sc, acc); break;
-      case 3: group_mfma<3>(st, wn, A, sc, acc); break;
-      case 4: group_mfma<4>(st, wn, A, sc, acc); break;
-      default: group_mfma<8>(st, wn, A, sc, acc); break;
+      case 1: group_mfma<1, CH>(st, wn, A, sc, acc); break;
+      case 2: group_mfma<2, CH>(st, wn, A, sc, acc); break;
+      case 3: group_mfma<3, CH>(st, wn, A, sc, acc); break;
+      case 4: group_mfma<4, CH>(st, wn, A, sc, acc); break;
+      case 16:
+        if constexpr (CH == 16) group_mfma16<CH>(st, wn, A, acc);
+        break;
+      default: group_mfma<8, CH>(st, wn, A, sc, acc); break;
     }
   };
   auto compute = [&](const Stage& st, int c, const float (&sc)[4]) __attribute__((always_inline)) {
@@ -509,7 +530,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       const int rr = rb + q;
       const bool live = rr < w.NBr && c >= g0 && c < g1;
       const int64_t blk = live ? (int64_t)rr * w.NBc + c : 0;
-      lb[k] = !live ? 0 : (c - g0 < kTabG ? (int)tbits[q][c - g0] : quantized_bits(w.bits[blk]));
+      lb[k] = !live ? 0 : (c - g0 < kTabG ? (int)tbits[q][c - g0] : tile_bits<CH>(w.bits[blk]));
       ls[k] = *reinterpret_cast<const float4*>(w.scale + blk * kBlockRows + n4);
       lz[k] = *reinterpret_cast<const uint32_t*>(w.zero + blk * kBlockRows + n4);
     }
@@ -593,13 +614,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   }
 }
 
-template <int BR>
+template <int BR, int CH>
 __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
     float* __restrict__ y, float* __restrict__ part, int gper) {
   // K split blockIdx.z: groups gper z .. ; partials plane z of part
   const int g0 = blockIdx.z * gper, g1 = min(w.NBc, g0 + gper);
-  gemm_tile<BR>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
+  gemm_tile<BR, CH>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
                 part ? part + (int64_t)blockIdx.z * M * w.N : nullptr);
 }
 
@@ -643,12 +664,12 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) 
              padded_groups(q.w.K / kBlockCols) * 16);
 }
 
-template <int BR>
+template <int BR, int CH>
 __global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
     GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
   const int t = blockIdx.x - q.tile_begin;
-  gemm_tile<BR>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, q.yr);
+  gemm_tile<BR, CH>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, q.yr);
 }
 
 // ---- row un-permutation ------------------------------------------------------------
@@ -795,11 +816,16 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
                      stream, g);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (br == 2)
-    hipLaunchKernelGGL(k_gemm_group<2>, dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
+  bool any16 = false;
+  for (int i = 0; i < count; ++i) any16 = any16 || w[i].has16;
+  if (br == 2 && any16)
+    hipLaunchKernelGGL((k_gemm_group<2, 16>), dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
+                       stream, g);
+  else if (br == 2)
+    hipLaunchKernelGGL((k_gemm_group<2, 8>), dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
                        stream, g);
   else
-    hipLaunchKernelGGL(k_gemm_group<4>, dim3((unsigned)tiles), dim3(TileCfg<4>::kThreads), 0,
+    hipLaunchKernelGGL((k_gemm_group<4, 8>), dim3((unsigned)tiles), dim3(TileCfg<4>::kThreads), 0,
                        stream, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -839,6 +865,8 @@ size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return gather + (p.split > 1 ? (size_t)p.split * M * N * 4 : 0);
 }
 
+bool gemm_handles_tile16() { return gemm_br() == 2; }
+
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, hipStream_t stream) {
   const int64_t K = w.K;
@@ -857,12 +885,15 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
   // one K range: the tiles write y in reordered order (into y), un-permuted after
   const bool unpermute = p.split == 1 && w.N <= kUnpermuteMaxN;
   float* out = p.split > 1 ? part : (unpermute ? y : nullptr);
-  if (p.br == 2)
-    hipLaunchKernelGGL(k_gemm<2>, grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y, out, p.gper);
+  if (p.br == 2 && w.has16)
+    hipLaunchKernelGGL((k_gemm<2, 16>), grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs,
+                       (int)M, w, y, out, p.gper);
+  else if (p.br == 2)
+    hipLaunchKernelGGL((k_gemm<2, 8>), grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs,
+                       (int)M, w, y, out, p.gper);
   else
-    hipLaunchKernelGGL(k_gemm<4>, grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs, (int)M, w,
-                       y, out, p.gper);
+    hipLaunchKernelGGL((k_gemm<4, 8>), grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs,
+                       (int)M, w, y, out, p.gper);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.split > 1) return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);

@@ -90,6 +90,7 @@ msq::WeightView view_of(const msq_weight* w) {
   v.codes = w->codes;
   v.scale = w->scale;
   v.zero = w->zero;
+  v.has16 = w->tile16_blocks > 0 ? 1 : 0;
   return v;
 }
 
@@ -170,6 +171,7 @@ msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, f
   const msq::WeightView v = view_of(w);
   hipError_t e;
   const uint16_t* xr = nullptr;  // reordered x left in the workspace (M > 1)
+  bool pass16 = w->tile16_blocks > 0;  // 16-bit blocks left to k_tile16
   if (kernel == MSQ_KERNEL_GEMV) {
     const msq::GemvPlan p = msq::plan_gemv(M, w->N, w->K);
     e = msq::launch_gemv(x_bf16, M, v, y, workspace, p, stream);
@@ -177,9 +179,9 @@ msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, f
   } else {
     e = msq::launch_gemm(x_bf16, M, v, y, workspace, stream);
     xr = reinterpret_cast<const uint16_t*>(workspace);
+    pass16 = pass16 && !msq::gemm_handles_tile16();
   }
-  if (e == hipSuccess && w->tile16_blocks > 0)
-    e = msq::launch_tile16(x_bf16, xr, M, v, y, stream);
+  if (e == hipSuccess && pass16) e = msq::launch_tile16(x_bf16, xr, M, v, y, stream);
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
@@ -237,9 +239,11 @@ msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_we
                         : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
   // M > 16: job i's reordered x starts its workspace share
   const uint8_t* share = reinterpret_cast<const uint8_t*>(workspace);
+  const bool gemm16 = M > 1 && msq::gemm_handles_tile16();
   for (int i = 0; i < count && e == hipSuccess; ++i) {
     const uint16_t* xr = M == 1 ? nullptr : reinterpret_cast<const uint16_t*>(share);
-    if (w[i]->tile16_blocks > 0) e = msq::launch_tile16(x_bf16[i], xr, M, v[i], y[i], stream);
+    if (w[i]->tile16_blocks > 0 && !gemm16)
+      e = msq::launch_tile16(x_bf16[i], xr, M, v[i], y[i], stream);
     share += (msq::gemm_workspace_bytes(M, w[i]->N, w[i]->K) + 255) & ~(size_t)255;
   }
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;

@@ -23,6 +23,7 @@ struct WeightView {
   const uint8_t* codes;
   const float* scale;          // [NBr][NBc][64]
   const uint8_t* zero;         // [NBr][NBc][64]
+  int has16;                   // the bit map holds 16-bit (passthrough) blocks
 };
 
 // ---- pack (msq_pack.hip)
@@ -49,6 +50,11 @@ struct GemvPlan {
 GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows = 0);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
+
+// The prefill GEMM multiplies 16-bit blocks itself (16 chunks per block in
+// LDS, two block rows per workgroup); false only under the four-block-row
+// tuning override, where k_tile16 adds them instead.
+bool gemm_handles_tile16();
 
 // y[m][perm_row[n]] += the exact bf16 product of the 16-bit (passthrough)
 // blocks of every block row: one launch after the quantized kernels.  xr:
