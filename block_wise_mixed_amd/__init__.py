@@ -22,7 +22,9 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "gemm", "workspace_bytes",
+__all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "allocate_packed", "pack_into",
+           "pack_bytes", "gemm", "workspace_bytes",
+           "OPTION_FIELDS",
            "gemm_group", "group_workspace_bytes", "GROUP_MAX",
            "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M",
            "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS", "reorder_channels"]
@@ -53,6 +55,28 @@ class _Sizes(ctypes.Structure):
                 ("blocks_per_bits", ctypes.c_int64 * 17), ("mean_bits", ctypes.c_double)]
 
 
+class _Options(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("gemv_split", ctypes.c_int32),
+                ("gemv_waves", ctypes.c_int32), ("m1_prep", ctypes.c_int32),
+                ("gemm_split", ctypes.c_int32)]
+
+
+OPTION_FIELDS = ("gemv_split", "gemv_waves", "m1_prep", "gemm_split")
+
+
+def _options(kernel: str = "auto", options: Optional[dict] = None) -> Optional[_Options]:
+    """msq_options for a kernel name and a dict of launch choices (None: automatic)."""
+    if kernel == "auto" and not options:
+        return None
+    o = _Options()
+    o.kernel = KERNELS[kernel]
+    for k, v in (options or {}).items():
+        if k not in OPTION_FIELDS:
+            raise ValueError(f"unknown option {k!r}; known: {OPTION_FIELDS}")
+        setattr(o, k, int(v))
+    return o
+
+
 class _Weight(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("bits", ctypes.c_void_p), ("perm_row", ctypes.c_void_p),
@@ -80,14 +104,24 @@ def load_library():
     lib.msq_gemm_workspace_bytes.restype = sz
     lib.msq_gemm.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz, vp]
     lib.msq_gemm.restype = ctypes.c_int
-    lib.msq_gemm_ex.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz, ctypes.c_int, vp]
+    lib.msq_gemm_ex.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp, sz,
+                                ctypes.POINTER(_Options), vp]
     lib.msq_gemm_ex.restype = ctypes.c_int
+    lib.msq_gemm_workspace_bytes_ex.argtypes = [i64, i64, i64, ctypes.POINTER(_Options)]
+    lib.msq_gemm_workspace_bytes_ex.restype = sz
     lib.msq_gemm_group_workspace_bytes.argtypes = [i64, ctypes.POINTER(ctypes.POINTER(_Weight)),
                                                    ctypes.c_int]
     lib.msq_gemm_group_workspace_bytes.restype = sz
     lib.msq_gemm_group.argtypes = [ctypes.POINTER(vp), i64, ctypes.POINTER(ctypes.POINTER(_Weight)),
                                    ctypes.POINTER(vp), ctypes.c_int, vp, sz, vp]
     lib.msq_gemm_group.restype = ctypes.c_int
+    lib.msq_gemm_group_workspace_bytes_ex.argtypes = [
+        i64, ctypes.POINTER(ctypes.POINTER(_Weight)), ctypes.c_int, ctypes.POINTER(_Options)]
+    lib.msq_gemm_group_workspace_bytes_ex.restype = sz
+    lib.msq_gemm_group_ex.argtypes = [ctypes.POINTER(vp), i64,
+                                      ctypes.POINTER(ctypes.POINTER(_Weight)), ctypes.POINTER(vp),
+                                      ctypes.c_int, vp, sz, ctypes.POINTER(_Options), vp]
+    lib.msq_gemm_group_ex.restype = ctypes.c_int
     lib.msq_alloc_workspace_bytes.argtypes = [i64]
     lib.msq_alloc_workspace_bytes.restype = sz
     lib.msq_allocate_bits.argtypes = [vp, i64, i64, vp, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
@@ -211,21 +245,19 @@ class PackedWeight:
         return self.code_bytes + 320 * live + 5 * nb + 4 * (self.N + self.K)
 
 
-def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> PackedWeight:
-    """Quantize and pack W (bf16 [N][K], original order) on the GPU."""
+def allocate_packed(N: int, K: int, bits, perm_row, perm_col, device="cuda") -> PackedWeight:
+    """Validate the problem on the host (msq_plan, the one validation) and allocate the
+    device buffers of its packed weight; the bit map and permutations are copied in."""
     torch = _torch()
-    lib = load_library()
-    Wd = _as_bf16_cuda(W, device)
-    N, K = int(Wd.shape[0]), int(Wd.shape[1])
     bh = _host(bits, np.uint8)
     if N % 64 == 0 and K % 128 == 0 and N > 0 and K > 0:
         bh = bh.reshape(N // 64, K // 128)
     ph = _host(perm_row, np.int32)
     qh = _host(perm_col, np.int32)
     sizes = plan(N, K, bh, ph, qh)
-    dev = Wd.device
+    dev = torch.device(device)
     code_bytes = int(sizes["code_bytes"])
-    pw = PackedWeight(
+    return PackedWeight(
         N, K,
         bits=torch.from_numpy(bh.copy()).to(dev),
         perm_row=torch.from_numpy(ph.copy()).to(dev),
@@ -236,14 +268,45 @@ def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> Pa
         zero=torch.empty((N // 64, K // 128, 64), dtype=torch.uint8, device=dev),
         code_bytes=code_bytes, mean_bits=float(sizes["mean_bits"]),
         tile16_blocks=int(sizes["blocks_per_bits"][16]))
+
+
+def pack_into(W, pw: PackedWeight, stream=None) -> PackedWeight:
+    """msq_quantize_pack of W (bf16 [N][K] on the weight's device) into the buffers of
+    pw (from allocate_packed); asynchronous on the stream."""
+    lib = load_library()
+    Wd = _as_bf16_cuda(W, pw.bits.device)
+    if tuple(Wd.shape) != (pw.N, pw.K):
+        raise ValueError(f"W must be [{pw.N}][{pw.K}]")
     w = pw.descriptor()
     _check(lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), _stream_handle(stream)),
            "msq_quantize_pack")
     return pw
 
 
-def workspace_bytes(M: int, N: int, K: int) -> int:
-    return int(load_library().msq_gemm_workspace_bytes(M, N, K))
+def quantize_pack(W, bits, perm_row, perm_col, device="cuda", stream=None) -> PackedWeight:
+    """Quantize and pack W (bf16 [N][K], original order) on the GPU."""
+    Wd = _as_bf16_cuda(W, device)
+    N, K = int(Wd.shape[0]), int(Wd.shape[1])
+    pw = allocate_packed(N, K, bits, perm_row, perm_col, device=Wd.device)
+    return pack_into(Wd, pw, stream=stream)
+
+
+def pack_bytes(pw: PackedWeight) -> int:
+    """HBM bytes the pack must move: W read (2 N K), permutations and bit map read,
+    offsets, codes, scales and zero points written."""
+    nb = int(pw.bits.numel())
+    return (2 * pw.N * pw.K + 4 * (pw.N + pw.K) + nb + 4 * nb + pw.code_bytes
+            + 4 * pw.N * (pw.K // 128) + pw.N * (pw.K // 128))
+
+
+def workspace_bytes(M: int, N: int, K: int, kernel: str = "auto",
+                    options: Optional[dict] = None) -> int:
+    """Workspace of msq_gemm (automatic choices) or of msq_gemm_ex with these choices."""
+    o = _options(kernel, options)
+    lib = load_library()
+    if o is None:
+        return int(lib.msq_gemm_workspace_bytes(M, N, K))
+    return int(lib.msq_gemm_workspace_bytes_ex(M, N, K, ctypes.byref(o)))
 
 
 GROUP_MAX = 8
@@ -255,12 +318,16 @@ def _descriptor_array(pws):
     return descs, arr
 
 
-def group_workspace_bytes(M: int, pws) -> int:
+def group_workspace_bytes(M: int, pws, options: Optional[dict] = None) -> int:
     descs, arr = _descriptor_array(pws)
-    return int(load_library().msq_gemm_group_workspace_bytes(M, arr, len(descs)))
+    o = _options("auto", options)
+    lib = load_library()
+    if o is None:
+        return int(lib.msq_gemm_group_workspace_bytes(M, arr, len(descs)))
+    return int(lib.msq_gemm_group_workspace_bytes_ex(M, arr, len(descs), ctypes.byref(o)))
 
 
-def gemm_group(xs, pws, outs=None, workspace=None, stream=None):
+def gemm_group(xs, pws, outs=None, workspace=None, stream=None, options: Optional[dict] = None):
     """[x_i . W_i^T] for up to GROUP_MAX packed weights in one call (M == 1: one decode
     launch for all of them, plus one prep launch if some have several K ranges; large M:
     one gather and one GEMM launch).  xs: one activation per weight (the same tensor may
@@ -278,20 +345,29 @@ def gemm_group(xs, pws, outs=None, workspace=None, stream=None):
     if outs is None:
         outs = [torch.empty((M, pw.N), dtype=torch.float32, device=xds[0].device) for pw in pws]
     descs, arr = _descriptor_array(pws)
-    need = int(lib.msq_gemm_group_workspace_bytes(M, arr, len(descs)))
+    need = group_workspace_bytes(M, pws, options)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xds[0].device)
     xa = (ctypes.c_void_p * len(xds))(*[xd.data_ptr() for xd in xds])
-    ya = (ctypes.c_void_p * len(outs))(*[o.data_ptr() for o in outs])
+    ya = (ctypes.c_void_p * len(outs))(*[y.data_ptr() for y in outs])
+    o = _options("auto", options)
     if M > 0:
-        _check(lib.msq_gemm_group(xa, M, arr, ya, len(descs),
-                                  workspace.data_ptr() if need > 0 else None, workspace.numel(),
-                                  _stream_handle(stream)), "msq_gemm_group")
+        ws_ptr = workspace.data_ptr() if need > 0 else None
+        if o is None:
+            st = lib.msq_gemm_group(xa, M, arr, ya, len(descs), ws_ptr, workspace.numel(),
+                                    _stream_handle(stream))
+        else:
+            st = lib.msq_gemm_group_ex(xa, M, arr, ya, len(descs), ws_ptr, workspace.numel(),
+                                       ctypes.byref(o), _stream_handle(stream))
+        _check(st, "msq_gemm_group")
     return outs
 
 
-def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, stream=None):
-    """y = x . W^T (fp32 [M][N], original row order) from packed weights."""
+def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, stream=None,
+         options: Optional[dict] = None):
+    """y = x . W^T (fp32 [M][N], original row order) from packed weights.  kernel and
+    options (keys gemv_split, gemv_waves, m1_prep, gemm_split) select the launch
+    (msq_gemm_ex); the defaults are msq_gemm's automatic choices."""
     torch = _torch()
     lib = load_library()
     xd = _as_bf16_cuda(x, pw.bits.device)
@@ -300,14 +376,21 @@ def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, st
     M = int(xd.shape[0])
     if out is None:
         out = torch.empty((M, pw.N), dtype=torch.float32, device=xd.device)
-    need = workspace_bytes(M, pw.N, pw.K)
+    need = workspace_bytes(M, pw.N, pw.K, kernel, options)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=xd.device)
     w = pw.descriptor()
     ws_ptr = workspace.data_ptr() if need > 0 else None
-    _check(lib.msq_gemm_ex(xd.data_ptr() if M > 0 else None, M, ctypes.byref(w),
-                           out.data_ptr() if M > 0 else None, ws_ptr, workspace.numel(),
-                           KERNELS[kernel], _stream_handle(stream)), "msq_gemm")
+    o = _options(kernel, options)
+    xp = xd.data_ptr() if M > 0 else None
+    yp = out.data_ptr() if M > 0 else None
+    if o is None:
+        st = lib.msq_gemm(xp, M, ctypes.byref(w), yp, ws_ptr, workspace.numel(),
+                          _stream_handle(stream))
+    else:
+        st = lib.msq_gemm_ex(xp, M, ctypes.byref(w), yp, ws_ptr, workspace.numel(),
+                             ctypes.byref(o), _stream_handle(stream))
+    _check(st, "msq_gemm")
     return out
 
 

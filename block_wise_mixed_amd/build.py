@@ -16,6 +16,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmsq.so")
+# read-bandwidth probe used by bench.py for context (not part of the library's ABI)
+PROBE_LIB = os.path.join(HERE, "libmsq_probe.so")
+PROBE_SOURCES = ["msq_probe.hip"]
 ARCH = "gfx950"
 
 SOURCES = ["msq_host.cpp", "msq_pack.hip", "msq_gemv.hip", "msq_gemm.hip", "msq_alloc.hip",
@@ -37,6 +40,31 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmsq.so)")
 
 
+def _compile(cc: str, src: str, obj: str, extra=(), verbose: bool = False) -> None:
+    cmd = [cc, *HIP_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd.insert(1, "-x")
+        cmd.insert(2, "hip")
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def _link(cc: str, objs, out: str, extra=()) -> None:
+    tmp = out + ".tmp"
+    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
 def build(verbose: bool = False) -> str:
     cc = hipcc()
     objdir = os.path.join(HERE, "_build")
@@ -44,26 +72,15 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
-               os.path.join(CSRC, src), "-o", obj]
-        if src.endswith(".cpp"):
-            cmd.insert(1, "-x")
-            cmd.insert(2, "hip")
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
-        if verbose and err.strip():
-            print(err, file=sys.stderr)
+        _compile(cc, src, obj, verbose=verbose)
         objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    _link(cc, objs, LIB)
+    pobjs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        _compile(cc, src, obj, verbose=verbose)
+        pobjs.append(obj)
+    _link(cc, pobjs, PROBE_LIB)
     return LIB
 
 

@@ -7,9 +7,9 @@
 //                sum_j x_r[m][j] over each 128-column group (fp32), written to
 //                the workspace once per call (the activation reordering of the
 //                "SFMP" abstract).
-//   k_gemm     : workgroup tile 128 (M) x 256 (N = four block rows), eight
-//                wavefronts of 64 x 64, one K group ahead in flight; details
-//                above the kernel.
+//   k_gemm     : workgroup tile 128 (M) x 128 (N = two block rows), four
+//                wavefronts of 64 x 64, the next K group's copies in flight
+//                while the current one is multiplied; details above the kernel.
 //
 // Keeping the matrix-core operands exact integers and applying the fp32 scale
 // per (row, group) keeps y within fp32 accumulation error of the exact
@@ -136,61 +136,49 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 
 // ---- GEMM ------------------------------------------------------------------------------
 //
-// Workgroup tile: kBM rows of x_r x kBR block rows (64 outputs each); eight
-// wavefronts (wm, wn) = (wave & 1, wave >> 1), each 64 rows x one block row,
-// two wavefronts per SIMD (one workgroup per CU: the LDS holds two stages).
-// Per 128-wide K group c:
-//   - the next group's x_r tile (kBM x 128 bf16) and the workgroup's kBR
-//     blocks of codes are copied global -> LDS by the direct-to-LDS loads
-//     (global_load_lds_dwordx4) into the other stage, and each wavefront
+// Workgroup tile: kBM = 128 rows of x_r x kBR = 2 block rows (64 outputs
+// each); four wavefronts (wm, wn) = (wave & 1, wave >> 1), each 64 rows x one
+// block row.  LDS holds ONE x_r tile and two code buffers (69 KiB), so two
+// workgroups share a CU and one's barrier waits and fragment-read bursts
+// overlap the other's products.  Per 128-wide K group c:
+//   - every wavefront reads its 16 A fragments (4 k-steps x 4 m tiles) of
+//     group c from the x_r tile into registers; workgroup barrier;
+//   - the next group's x_r tile (kBM x 128 bf16) goes into that same buffer
+//     and the workgroup's kBR blocks of codes into the other code buffer, by
+//     the direct-to-LDS loads (global_load_lds_dwordx4), and each wavefront
 //     loads its block's next scales;
-//   - the wavefront reads its 16 A fragments (4 k-steps x 4 m tiles) from
-//     LDS and, row tile by row tile, the code chunks that tile needs,
-//     unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: both planes
-//     merged into one operand; 8-bit: low 7 bits and top bit, two operands,
-//     bias 384), issues 16 v_mfma_f32_16x16x32_bf16 (32 for 8 bits) into a
-//     group accumulator
-//     and folds it, acc += s_n * acc_g, while the next row tile's products
-//     run;
+//   - row tile by row tile, the wavefront reads the code chunks that tile
+//     needs, unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: both
+//     planes merged into one operand; 8-bit: low 7 bits and top bit, two
+//     operands, bias 384), issues 16 v_mfma_f32_16x16x32_bf16 (32 for 8
+//     bits) into a group accumulator and folds it, acc += s_n * acc_g, while
+//     the next row tile's products run;
 //   - wait for its own copies, one barrier.
 // acc_g carries the unpack bias and the zero point: acc_g = sum_k (bias +
 // q_k) x_k = sum_k (q_k - z) x_k + (bias + z) S_c with S_c the group's sum
 // of x_r.  The term sum_c s_c (bias + z_c) S_c of every output is removed at
 // the end by one more matrix product over the groups (see below), so the
 // fold is a single FMA per output and group.
-// The two stages are distinct LDS objects and the loop is unrolled by two,
-// so the compiler sees that the copies in flight never alias what the
+// The two code buffers are distinct LDS objects and the loop is unrolled by
+// two, so the compiler sees that the copies in flight never alias what the
 // products read and adds no wait for them before those reads.  The x_r tile
 // is stored without padding, 16-byte chunk p of row r holding column chunk
 // p ^ (r & 15) (the direct-to-LDS copies write each 1 KiB contiguously; the
 // swizzle keeps the fragment reads free of bank conflicts).  0-bit blocks
 // skip the copies and the products.  y is scattered to original rows
 // through perm_row.
-//
-// Two tile shapes share this code (template parameter BR, block rows per
-// workgroup): BR = 4 as above; BR = 2, four wavefronts, with ONE x_r buffer:
-// every wavefront reads its A fragments of group c into registers first, a
-// barrier, then the copies of group c + 1 go into that same buffer (and the
-// other code buffer) while the products of group c run, and a second barrier
-// ends the group.  Its LDS (69 KiB) lets two workgroups share a CU, so one
-// workgroup's barrier waits and fragment-read bursts overlap the other's
-// products.
 constexpr int kBM = 128;
+constexpr int kBR = 2;                 // block rows per workgroup
+constexpr int kWaves = 2 * kBR;
+constexpr int kThreads = kWaves * 64;
 constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
-template <int BR>
-struct TileCfg {
-  static constexpr int kWaves = 2 * BR;
-  static constexpr int kThreads = kWaves * 64;
-  static constexpr bool kSingleA = BR == 2;  // one x_r buffer, two barriers per group
-};
-
 
 __host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 128.f; }
 
 // One stage of the pipeline in LDS.
 struct Stage {
   uint4* a;      // x_r tile [kBM][16 chunks], swizzled
-  uint4* codes;  // [BR][CH chunks][64 lanes]; CH = 8, or 16 when 16-bit blocks occur
+  uint4* codes;  // [kBR][CH chunks][64 lanes]; CH = 8, or 16 when 16-bit blocks occur
 };
 
 // Chunk of a B-bit block holding (the low plane of) fragment F.
@@ -309,7 +297,7 @@ __device__ __forceinline__ void load_scales(const WeightView& w, int r, int c, f
 // scales, zero points and S terms of the next batch are loaded while the
 // current one is built and multiplied.
 constexpr int kTermBytes = 4 * 64 * 16;  // one term of one block row: 4 row tiles x 1 KiB
-constexpr int kTUnits = 4;  // units of 4 rows per thread: BR * 32 * 16 / (128 * BR)
+constexpr int kTUnits = 4;  // units of 4 rows per thread: kBR * 32 * 16 / (4 kThreads)
 
 // Workgroup barrier that waits for the wavefront's LDS operations only (loads
 // from global memory stay in flight); the empty asm statements keep the
@@ -328,20 +316,17 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Tile (mtile, ntile) of one matrix over groups g0 .. g1 - 1: rows kBM mtile
-// .., block rows BR ntile ...  part == nullptr: the tile holds all groups
+// .., block rows kBR ntile ...  part == nullptr: the tile holds all groups
 // and y is written (scattered through perm_row); otherwise the tile's share
 // of a K split goes to part[m][reordered row] (summed over the splits, in
 // split order, by the split-reduce kernel).
-template <int BR, int CH>
+template <int CH>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                           const uint16_t* __restrict__ sxs, int M,
                                           const WeightView& w, float* __restrict__ y, int mtile,
                                           int ntile, int g0, int g1, float* __restrict__ part) {
-  constexpr int kBR = BR;
-  constexpr int kWaves = TileCfg<BR>::kWaves, kThreads = TileCfg<BR>::kThreads;
-  constexpr bool kSingleA = TileCfg<BR>::kSingleA;
   static_assert(kTUnits * kThreads == kBR * 32 * 16, "T units per thread");
-  __shared__ __align__(16) uint4 a0[kBM * 16], a1[kSingleA ? 16 : kBM * 16];
+  __shared__ __align__(16) uint4 a0[kBM * 16];
   __shared__ __align__(16) uint4 c0s[kBR * CH * 64], c1s[kBR * CH * 64];
   __shared__ uint32_t toff[kBR][kTabG];
   __shared__ uint8_t tbits[kBR][kTabG];
@@ -355,7 +340,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   const int64_t K = w.K;
   const int G = w.NBc;
   const int tabG = min(g1 - g0, kTabG);
-  const Stage st0{a0, c0s}, st1{kSingleA ? a0 : a1, c1s};
+  const Stage st0{a0, c0s}, st1{a0, c1s};
 
   // bitwidth and KiB offset of block (rb + q, c): LDS table (groups g0 ..
   // g0 + kTabG - 1), or global past it
@@ -442,13 +427,6 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       default: group_mfma<8, CH>(st, wn, A, sc, acc); break;
     }
   };
-  auto compute = [&](const Stage& st, int c, const float (&sc)[4]) __attribute__((always_inline)) {
-    uint32_t unused_off;
-    if (block_at(wn, c, unused_off) == 0) return;
-    bf16x8 A[4][4];
-    read_a(st, apk, A);
-    products(st, c, A, sc);
-  };
   // own copies done, then the workgroup barrier (no memory fence: the copies
   // are the only producer and their completion is what is waited for)
   auto stage_barrier = [&]() __attribute__((always_inline)) {
@@ -463,59 +441,35 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   load_scales(w, r, g0, cur);
   stage_barrier();
 
-  if constexpr (kSingleA) {
-    // group c: A fragments from the one x_r buffer into registers, barrier,
-    // copies of group c + 1 (x_r into that buffer, codes into the other code
-    // buffer), products of group c, barrier
-    auto group = [&](const Stage& st, const Stage& nx, int c) __attribute__((always_inline)) {
-      uint32_t unused_off;
-      bf16x8 A[4][4];
-      if (block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
-      lds_barrier();
-      if (c + 1 < g1) {
-        copy_group(nx, c + 1);
-        load_scales(w, r, c + 1, nxt);
-      }
-      products(st, c, A, cur);
-      stage_barrier();
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
-    };
-    for (int c = g0; c < g1; c += 2) {
-      group(st0, st1, c);
-      if (c + 1 >= g1) break;
-      group(st1, st0, c + 1);
-    }
-  } else
-  for (int c = g0; c < g1; c += 2) {
-    // group c from stage 0, group c + 1 arriving in stage 1
+  // group c: A fragments from the one x_r buffer into registers, barrier,
+  // copies of group c + 1 (x_r into that buffer, codes into the other code
+  // buffer), products of group c, barrier
+  auto group = [&](const Stage& st, const Stage& nx, int c) __attribute__((always_inline)) {
+    uint32_t unused_off;
+    bf16x8 A[4][4];
+    if (block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
+    lds_barrier();
     if (c + 1 < g1) {
-      copy_group(st1, c + 1);
+      copy_group(nx, c + 1);
       load_scales(w, r, c + 1, nxt);
     }
-    compute(st0, c, cur);
+    products(st, c, A, cur);
     stage_barrier();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
+  };
+  for (int c = g0; c < g1; c += 2) {
+    group(st0, st1, c);
     if (c + 1 >= g1) break;
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
-    // group c + 1 from stage 1, group c + 2 arriving in stage 0
-    if (c + 2 < g1) {
-      copy_group(st0, c + 2);
-      load_scales(w, r, c + 2, nxt);
-    }
-    compute(st1, c + 1, cur);
-    stage_barrier();
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
+    group(st1, st0, c + 1);
   }
 
-  // ---- correction product (the stages are free now; T of block rows 0, 1
-  // goes to a0, of block rows 2, 3 to a1)
+  // ---- correction product (the x_r buffer is free now: T of both block rows goes there)
   const int64_t Gp = padded_groups(G);
   auto tq = [&](int q) __attribute__((always_inline)) -> unsigned char* {
-    return reinterpret_cast<unsigned char*>(q < 2 ? a0 : a1) + (q & 1) * 3 * kTermBytes;
+    return reinterpret_cast<unsigned char*>(a0) + q * 3 * kTermBytes;
   };
-  static_assert(6 * kTermBytes <= (int)sizeof(a0), "two block rows of T terms per stage buffer");
+  static_assert(kBR * 3 * kTermBytes <= (int)sizeof(a0), "T terms of the block rows in the x_r buffer");
   const int64_t plane = (int64_t)M * Gp;
   // unit u = (q, gl, 4 rows n4 .. n4 + 3) for u = tid + kThreads * k
   float4 ls[kTUnits];
@@ -614,13 +568,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   }
 }
 
-template <int BR, int CH>
-__global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
+template <int CH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
     float* __restrict__ y, float* __restrict__ part, int gper) {
   // K split blockIdx.z: groups gper z .. ; partials plane z of part
   const int g0 = blockIdx.z * gper, g1 = min(w.NBc, g0 + gper);
-  gemm_tile<BR, CH>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
+  gemm_tile<CH>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
                 part ? part + (int64_t)blockIdx.z * M * w.N : nullptr);
 }
 
@@ -664,12 +618,12 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) 
              padded_groups(q.w.K / kBlockCols) * 16);
 }
 
-template <int BR, int CH>
-__global__ __launch_bounds__(TileCfg<BR>::kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
+template <int CH>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
     GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, false);
   const int t = blockIdx.x - q.tile_begin;
-  gemm_tile<BR, CH>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, q.yr);
+  gemm_tile<CH>(q.xr, q.sxs, g.M, q.w, q.y, t % q.mtiles, t / q.mtiles, 0, q.w.NBc, q.yr);
 }
 
 // ---- row un-permutation ------------------------------------------------------------
@@ -723,33 +677,22 @@ __global__ __launch_bounds__(kUnpermuteThreads) void k_unpermute_rows(UnpermuteG
   for (int n = t; n < N; n += kUnpermuteThreads) row[n] = lrow[n];
 }
 
-// Block rows per workgroup of the prefill GEMM (MSQ_GEMM_BR=2 or 4 overrides).
-int gemm_br() {
-  static const int br = [] {
-    const char* e = std::getenv("MSQ_GEMM_BR");
-    const int v = e ? std::atoi(e) : 0;
-    return v == 2 || v == 4 ? v : 2;
-  }();
-  return br;
-}
-
 // Launch shape of one GEMM call.  Fewer tiles than kFillTiles (two per CU)
 // split K into ranges of at least kMinSplitGroups groups (the correction
 // product works on batches of 32 groups, so shorter ranges waste it), the
-// ranges' partials summed by the split reduction.  MSQ_GEMM_SPLIT overrides
+// ranges' partials summed by the split reduction.  opt.gemm_split overrides
 // the split count.
 constexpr int64_t kFillTiles = 512;
 constexpr int64_t kMinSplitGroups = 8;
 struct GemmPlan {
-  int br, split, gper;
+  int split, gper;
 };
-GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, const Options& opt) {
   GemmPlan p{};
-  p.br = gemm_br();
   const int64_t G = K / kBlockCols;
-  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N / kBlockRows + p.br - 1) / p.br);
-  const char* e = std::getenv("MSQ_GEMM_SPLIT");
-  int64_t split = e && *e ? std::atoi(e) : (tiles >= kFillTiles ? 1 : (kFillTiles + tiles - 1) / tiles);
+  const int64_t tiles = ((M + kBM - 1) / kBM) * ((N / kBlockRows + kBR - 1) / kBR);
+  int64_t split = opt.gemm_split > 0 ? opt.gemm_split
+                                     : (tiles >= kFillTiles ? 1 : (kFillTiles + tiles - 1) / tiles);
   split = std::min<int64_t>(split, std::max<int64_t>(1, G / kMinSplitGroups));
   if (split < 1) split = 1;
   p.gper = (int)((G + split - 1) / split);
@@ -765,32 +708,32 @@ size_t gather_workspace_bytes(int64_t M, int64_t K) {
   return xr_al + 3 * (size_t)M * (size_t)padded_groups(K / kBlockCols) * 2;
 }
 
-size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count) {
+size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count, const Options& opt) {
   size_t total = 0;
   for (int i = 0; i < count; ++i)
-    total += (gemm_workspace_bytes(M, w[i].N, w[i].K) + 255) & ~(size_t)255;
+    total += (gemm_workspace_bytes(M, w[i].N, w[i].K, opt) + 255) & ~(size_t)255;
   return total;
 }
 
 hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightView* w,
-                             float* const* y, int count, void* workspace, hipStream_t stream) {
+                             float* const* y, int count, void* workspace, const Options& opt,
+                             hipStream_t stream) {
   if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
   GemmGroup g{};
   g.count = count;
   g.M = (int)M;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   size_t lds = 0;
-  const int br = gemm_br();
   int64_t tiles = 0;
   for (int i = 0; i < count; ++i)
-    tiles += (M + kBM - 1) / kBM * ((w[i].NBr + br - 1) / br);
+    tiles += (M + kBM - 1) / kBM * ((w[i].NBr + kBR - 1) / kBR);
   if (tiles < kFillTiles || tiles > 0x7FFFFFFF || M * count > 0x7FFFFFFF) {
     // too few tiles to fill the GPU (each call then splits K), or beyond one
     // launch's grid: each matrix on its own, in its own workspace
     for (int i = 0; i < count; ++i) {
-      const hipError_t e = launch_gemm(x[i], M, w[i], y[i], ws, stream);
+      const hipError_t e = launch_gemm(x[i], M, w[i], y[i], ws, opt, stream);
       if (e != hipSuccess) return e;
-      ws += (gemm_workspace_bytes(M, w[i].N, w[i].K) + 255) & ~(size_t)255;
+      ws += (gemm_workspace_bytes(M, w[i].N, w[i].K, opt) + 255) & ~(size_t)255;
     }
     return hipSuccess;
   }
@@ -803,14 +746,14 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
     q.xr = reinterpret_cast<uint16_t*>(ws);
     const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
     q.sxs = reinterpret_cast<uint16_t*>(ws + xr_bytes);
-    ws += (gemm_workspace_bytes(M, w[i].N, K) + 255) & ~(size_t)255;
+    ws += (gemm_workspace_bytes(M, w[i].N, K, opt) + 255) & ~(size_t)255;
     q.y = y[i];
     q.yr = w[i].N <= kUnpermuteMaxN ? y[i] : nullptr;
     q.staged = (size_t)K * 2 <= kGatherMaxLds;
     if (q.staged) lds = std::max(lds, (size_t)K * 2);
     q.mtiles = (int)((M + kBM - 1) / kBM);
     q.tile_begin = (int)tiles;
-    tiles += (int64_t)q.mtiles * ((w[i].NBr + br - 1) / br);
+    tiles += (int64_t)q.mtiles * ((w[i].NBr + kBR - 1) / kBR);
   }
   hipLaunchKernelGGL(k_gather_x_group, dim3((unsigned)(M * count)), dim3(kGatherThreads), lds,
                      stream, g);
@@ -818,15 +761,10 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   if (e != hipSuccess) return e;
   bool any16 = false;
   for (int i = 0; i < count; ++i) any16 = any16 || w[i].has16;
-  if (br == 2 && any16)
-    hipLaunchKernelGGL((k_gemm_group<2, 16>), dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
-                       stream, g);
-  else if (br == 2)
-    hipLaunchKernelGGL((k_gemm_group<2, 8>), dim3((unsigned)tiles), dim3(TileCfg<2>::kThreads), 0,
-                       stream, g);
+  if (any16)
+    hipLaunchKernelGGL((k_gemm_group<16>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
   else
-    hipLaunchKernelGGL((k_gemm_group<4, 8>), dim3((unsigned)tiles), dim3(TileCfg<4>::kThreads), 0,
-                       stream, g);
+    hipLaunchKernelGGL((k_gemm_group<8>), dim3((unsigned)tiles), dim3(kThreads), 0, stream, g);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   UnpermuteGroup u{};
@@ -859,18 +797,16 @@ hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, vo
   return hipGetLastError();
 }
 
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  const GemmPlan p = plan_gemm(M, N, K);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const Options& opt) {
+  const GemmPlan p = plan_gemm(M, N, K, opt);
   const size_t gather = (gather_workspace_bytes(M, K) + 255) & ~(size_t)255;
   return gather + (p.split > 1 ? (size_t)p.split * M * N * 4 : 0);
 }
 
-bool gemm_handles_tile16() { return gemm_br() == 2; }
-
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
-                       void* workspace, hipStream_t stream) {
+                       void* workspace, const Options& opt, hipStream_t stream) {
   const int64_t K = w.K;
-  const GemmPlan p = plan_gemm(M, w.N, K);
+  const GemmPlan p = plan_gemm(M, w.N, K, opt);
   uint16_t* xr = reinterpret_cast<uint16_t*>(workspace);
   const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
   uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(workspace) + xr_bytes);
@@ -880,20 +816,17 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
                     : nullptr;
   hipError_t e = launch_gather_x(x, M, w, workspace, stream);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + p.br - 1) / p.br),
+  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + kBR - 1) / kBR),
                   (unsigned)p.split);
   // one K range: the tiles write y in reordered order (into y), un-permuted after
   const bool unpermute = p.split == 1 && w.N <= kUnpermuteMaxN;
   float* out = p.split > 1 ? part : (unpermute ? y : nullptr);
-  if (p.br == 2 && w.has16)
-    hipLaunchKernelGGL((k_gemm<2, 16>), grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs,
-                       (int)M, w, y, out, p.gper);
-  else if (p.br == 2)
-    hipLaunchKernelGGL((k_gemm<2, 8>), grid, dim3(TileCfg<2>::kThreads), 0, stream, xr, sxs,
-                       (int)M, w, y, out, p.gper);
+  if (w.has16)
+    hipLaunchKernelGGL((k_gemm<16>), grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y, out,
+                       p.gper);
   else
-    hipLaunchKernelGGL((k_gemm<4, 8>), grid, dim3(TileCfg<4>::kThreads), 0, stream, xr, sxs,
-                       (int)M, w, y, out, p.gper);
+    hipLaunchKernelGGL((k_gemm<8>), grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y, out,
+                       p.gper);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.split > 1) return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);

@@ -1018,16 +1018,6 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
   return g;
 }
 
-// M == 1 calls without a K split reorder x inside the decode workgroups
-// (no prep launch) when the wavefront count allows it; the boundary has
-// checked that x and perm_col are 16-byte aligned, as the gathering
-// workgroups read them.  MSQ_M1_GATHER=0 turns it off (tuning).
-bool m1_gathers(const GemvPlan& p) {
-  const char* v = std::getenv("MSQ_M1_GATHER");
-  const bool enabled = !(v && *v && std::atoi(v) == 0);
-  return enabled && p.split == 1 && p.nw >= 8;
-}
-
 size_t m1_launch_lds(const GemvPlan& p, bool gather) {
   return gather ? m1_lds_bytes_gather(p.kr) : p.lds_bytes;
 }
@@ -1057,35 +1047,27 @@ hipError_t launch_cfg(const uint16_t* xr, const uint16_t* sxs, int M, const Weig
   return hipGetLastError();
 }
 
-int env_int(const char* name, int dflt) {
-  const char* v = std::getenv(name);
-  return (v && *v) ? std::atoi(v) : dflt;
-}
-
 }  // namespace
 
 // Launch shape.  The block columns of a block row are split into `split`
 // ranges of at most 64 columns.  M == 1: at most 512 workgroups of 8
 // wavefronts (two per CU) and at most 8 splits.  M > 1: about 512
-// workgroups.  MSQ_GEMV_SPLIT and MSQ_GEMV_WAVES override the split count
-// and, for M == 1, the wavefronts per workgroup (tuning only).
+// workgroups.  opt.gemv_split and opt.gemv_waves override the split count
+// and, for M == 1, the wavefronts per workgroup.
 const uint16_t* gemv_reordered_x(void* workspace, const GemvPlan& p, int64_t M, int64_t N) {
   if (M <= 1) return nullptr;
   return reinterpret_cast<const uint16_t*>(reinterpret_cast<uint8_t*>(workspace) +
                                            part_bytes(p, M, N));
 }
 
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t group_rows) {
   GemvPlan p{};
   const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);
   // the split heuristic counts the block rows of every matrix in the launch
   const int rows = group_rows > 0 ? (int)(group_rows / kBlockRows) : NBr;
   p.mt = (int)((M + 15) / 16);
   p.nw = M > 16 ? 4 : 8;
-  if (M == 1) {
-    const int nw = env_int("MSQ_GEMV_WAVES", 8);
-    p.nw = (nw == 4 || nw == 16) ? nw : 8;
-  }
+  if (M == 1) p.nw = (opt.gemv_waves == 4 || opt.gemv_waves == 16) ? opt.gemv_waves : 8;
   int kr_max = kMaxCols;
   if (M > 1) {
     // LDS per block column: x slice (2 bytes x 128 per row) + one group sum per row
@@ -1094,7 +1076,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
     if (kr_max > kMaxCols) kr_max = kMaxCols;
     if (kr_max < 1) kr_max = 1;
   }
-  int split = env_int("MSQ_GEMV_SPLIT", 0);
+  int split = opt.gemv_split;
   if (split <= 0) {
     if (M == 1) {
       // about one workgroup of 8 wavefronts per CU: more K splits add start-ups
@@ -1115,6 +1097,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows) {
   split = (NBc + kr - 1) / kr;
   p.split = split;
   p.kr = kr;
+  // M == 1 with one K range reorders x inside the decode workgroups (no prep
+  // launch) when the wavefront count allows it; the boundary has checked
+  // that x and perm_col are 16-byte aligned, as those workgroups read them.
+  p.gather = M == 1 && split == 1 && p.nw >= 8 && !opt.m1_prep ? 1 : 0;
   size_t x_bytes;
   if (M == 1) {
     p.xs_stride = kr * kBlockCols;
@@ -1136,15 +1122,16 @@ int64_t group_rows(const WeightView* w, int count) {
   return rows;
 }
 
-size_t gemv_group_workspace_m1(const WeightView* w, int count) {
+size_t gemv_group_workspace_m1(const WeightView* w, int count, const Options& opt) {
   size_t total = 0;
   const int64_t rows = group_rows(w, count);
-  for (int i = 0; i < count; ++i) total += align256(plan_gemv(1, w[i].N, w[i].K, rows).workspace);
+  for (int i = 0; i < count; ++i) total += align256(plan_gemv(1, w[i].N, w[i].K, opt, rows).workspace);
   return total;
 }
 
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
-                                int count, void* workspace, hipStream_t stream) {
+                                int count, void* workspace, const Options& opt,
+                                hipStream_t stream) {
   if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
   M1Group g{};
   g.count = count;
@@ -1153,7 +1140,7 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
   size_t lds = 0;
   const int64_t rows = group_rows(w, count);
   for (int i = 0; i < count; ++i) {
-    const GemvPlan p = plan_gemv(1, w[i].N, w[i].K, rows);
+    const GemvPlan p = plan_gemv(1, w[i].N, w[i].K, opt, rows);
     if (nw == 0) nw = p.nw;
     if (p.nw != nw) return hipErrorInvalidValue;
     const GemvWorkspace gw = carve(ws, p, 1, w[i].N, w[i].K);
@@ -1169,7 +1156,7 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
     q.split = p.split;
     q.kr = p.kr;
     q.ncounters = p.split > 1 ? (int)w[i].NBr : 0;
-    q.gather = m1_gathers(p) ? 1 : 0;
+    q.gather = p.gather;
     q.prep_begin = prep_total;
     q.wg_begin = wg_total;
     const int64_t nbc = w[i].K / kBlockCols;
@@ -1200,7 +1187,7 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
   float* dst = direct ? y : g.part;
   hipError_t e;
   if (M == 1) {
-    const bool gather = m1_gathers(p);
+    const bool gather = p.gather != 0;
     if (!gather) {
       // x reordered once for all workgroups; the split counters are cleared
       // here, only needed with several splits

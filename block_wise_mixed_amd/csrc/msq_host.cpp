@@ -94,15 +94,118 @@ msq::WeightView view_of(const msq_weight* w) {
   return v;
 }
 
-size_t workspace_for(int64_t M, int64_t N, int64_t K, msq_kernel kernel) {
+// Options of the public struct (NULL = automatic); false for bad values.
+bool options_of(const msq_options* o, msq::Options& out) {
+  out = msq::Options{};
+  if (!o) return true;
+  if (o->kernel != MSQ_KERNEL_AUTO && o->kernel != MSQ_KERNEL_GEMV && o->kernel != MSQ_KERNEL_GEMM)
+    return false;
+  if (o->gemv_split < 0 || o->gemm_split < 0) return false;
+  if (o->gemv_waves != 0 && o->gemv_waves != 4 && o->gemv_waves != 8 && o->gemv_waves != 16)
+    return false;
+  out.kernel = o->kernel;
+  out.gemv_split = o->gemv_split;
+  out.gemv_waves = o->gemv_waves;
+  out.m1_prep = o->m1_prep != 0;
+  out.gemm_split = o->gemm_split;
+  return true;
+}
+
+// The kernel a call runs.
+int kernel_for(int64_t M, const msq::Options& o) {
+  if (o.kernel != MSQ_KERNEL_AUTO) return o.kernel;
+  return M <= MSQ_AUTO_GEMV_MAX_M ? MSQ_KERNEL_GEMV : MSQ_KERNEL_GEMM;
+}
+
+size_t workspace_for(int64_t M, int64_t N, int64_t K, const msq::Options& o) {
   if (M <= 0) return 0;
-  const size_t gemv = M <= MSQ_GEMV_MAX_M ? msq::plan_gemv(M, N, K).workspace : 0;
-  const size_t gemm = msq::gemm_workspace_bytes(M, N, K);
-  switch (kernel) {
-    case MSQ_KERNEL_GEMV: return gemv;
-    case MSQ_KERNEL_GEMM: return gemm;
-    default: return M <= MSQ_AUTO_GEMV_MAX_M ? gemv : gemm;
+  if (kernel_for(M, o) == MSQ_KERNEL_GEMV)
+    return M <= MSQ_GEMV_MAX_M ? msq::plan_gemv(M, N, K, o).workspace : 0;
+  return msq::gemm_workspace_bytes(M, N, K, o);
+}
+
+msq_status gemm_impl(const uint16_t* x_bf16, int64_t M, const msq_weight* w, float* y,
+                     void* workspace, size_t workspace_bytes, const msq::Options& o,
+                     hipStream_t stream) {
+  msq_status st = weight_ptrs_ok(w);
+  if (st != MSQ_OK) return st;
+  if (M < 0) return MSQ_ERR_SHAPE;
+  if (M == 0) return MSQ_OK;
+  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
+  if (!x_bf16 || !y || !aligned(x_bf16, 16) || !aligned(y, 4)) return MSQ_ERR_INVALID_ARG;
+  const int kernel = kernel_for(M, o);
+  if (kernel == MSQ_KERNEL_GEMV && M > MSQ_GEMV_MAX_M) return MSQ_ERR_UNSUPPORTED;
+  const size_t need = workspace_for(M, w->N, w->K, o);
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
+  const msq::WeightView v = view_of(w);
+  hipError_t e;
+  if (kernel == MSQ_KERNEL_GEMV) {
+    const msq::GemvPlan p = msq::plan_gemv(M, w->N, w->K, o);
+    e = msq::launch_gemv(x_bf16, M, v, y, workspace, p, stream);
+    // the decode kernel leaves 16-bit blocks to one more pass
+    if (e == hipSuccess && w->tile16_blocks > 0)
+      e = msq::launch_tile16(x_bf16, msq::gemv_reordered_x(workspace, p, M, w->N), M, v, y, stream);
+  } else {
+    e = msq::launch_gemm(x_bf16, M, v, y, workspace, o, stream);
   }
+  return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
+}
+
+size_t group_workspace_impl(int64_t M, const msq_weight* const* w, int count, const msq::Options& o) {
+  if (!w || count < 1 || count > MSQ_GROUP_MAX || M <= 0) return 0;
+  msq::WeightView v[MSQ_GROUP_MAX];
+  size_t most = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!w[i] || check_shape(w[i]->N, w[i]->K) != MSQ_OK) return 0;
+    v[i] = view_of(w[i]);
+    const size_t one = workspace_for(M, w[i]->N, w[i]->K, o);
+    most = one > most ? one : most;
+  }
+  // M == 1 and M > MSQ_AUTO_GEMV_MAX_M: every matrix keeps its own workspace
+  // (one launch for all, or split-K single calls); 2 .. MSQ_AUTO_GEMV_MAX_M:
+  // the matrices run one after the other
+  if (M == 1) return msq::gemv_group_workspace_m1(v, count, o);
+  if (M > MSQ_AUTO_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count, o);
+  return most;
+}
+
+msq_status group_impl(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
+                      float* const* y, int count, void* workspace, size_t workspace_bytes,
+                      const msq::Options& o, hipStream_t stream) {
+  static_assert(MSQ_GROUP_MAX == msq::kGemvGroupMax, "group size of the header and the kernels");
+  if (!x_bf16 || !w || !y || count < 1 || count > MSQ_GROUP_MAX) return MSQ_ERR_INVALID_ARG;
+  if (o.kernel != MSQ_KERNEL_AUTO) return MSQ_ERR_INVALID_ARG;
+  for (int i = 0; i < count; ++i) {
+    const msq_status st = weight_ptrs_ok(w[i]);
+    if (st != MSQ_OK) return st;
+    if (!x_bf16[i] || !y[i] || !aligned(x_bf16[i], 16) || !aligned(y[i], 4))
+      return MSQ_ERR_INVALID_ARG;
+  }
+  if (M < 0) return MSQ_ERR_SHAPE;
+  if (M == 0) return MSQ_OK;
+  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
+  const size_t need = group_workspace_impl(M, w, count, o);
+  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
+  if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
+  if (M != 1 && M <= MSQ_AUTO_GEMV_MAX_M) {
+    // one matrix after the other, sharing the workspace (ordered on stream)
+    for (int i = 0; i < count; ++i) {
+      const msq_status st = gemm_impl(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, o, stream);
+      if (st != MSQ_OK) return st;
+    }
+    return MSQ_OK;
+  }
+  msq::WeightView v[MSQ_GROUP_MAX];
+  for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
+  if (M > 1)  // the prefill GEMM multiplies 16-bit blocks itself
+    return msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, o, stream) == hipSuccess
+               ? MSQ_OK
+               : MSQ_ERR_HIP;
+  hipError_t e = msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, o, stream);
+  for (int i = 0; i < count && e == hipSuccess; ++i)
+    if (w[i]->tile16_blocks > 0) e = msq::launch_tile16(x_bf16[i], nullptr, 1, v[i], y[i], stream);
+  return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
 }  // namespace
@@ -119,26 +222,17 @@ msq_status msq_quantize_pack(const uint16_t* W_bf16, const msq_weight* w, hipStr
   if (!W_bf16 || !aligned(W_bf16, 16)) return MSQ_ERR_INVALID_ARG;
   msq_status st = weight_ptrs_ok(w);
   if (st != MSQ_OK) return st;
+  if (w->code_bytes < 0) return MSQ_ERR_INVALID_ARG;
+  // The descriptor is trusted (its bits and permutations passed msq_plan):
+  // nothing is read back, so the call stays asynchronous.  The kernels clamp
+  // every index and skip blocks that would end past code_bytes.
   const int64_t N = w->N, K = w->K;
   const int64_t nblk = (N / kBlockRows) * (K / kBlockCols);
-  // Read the descriptor's bit map and permutations back and validate them as
-  // msq_plan does, so the kernels below can never index out of bounds.
-  std::vector<uint8_t> bits((size_t)nblk);
-  std::vector<int32_t> prow((size_t)N), pcol((size_t)K);
-  if (hipMemcpyAsync(bits.data(), w->bits, (size_t)nblk, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      hipMemcpyAsync(prow.data(), w->perm_row, (size_t)N * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      hipMemcpyAsync(pcol.data(), w->perm_col, (size_t)K * 4, hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return MSQ_ERR_HIP;
-  msq_sizes sz;
-  st = plan_impl(N, K, bits.data(), prow.data(), pcol.data(), &sz);
-  if (st != MSQ_OK) return st;
-  if (w->code_bytes < sz.code_bytes) return MSQ_ERR_BUFFER_TOO_SMALL;
-  if (w->tile16_blocks != sz.blocks_per_bits[16]) return MSQ_ERR_INVALID_ARG;
   if (hipError_t e = msq::launch_block_offsets(w->bits, nblk, w->block_offset, stream); e != hipSuccess)
     return MSQ_ERR_HIP;
   if (hipError_t e = msq::launch_pack(W_bf16, N, K, w->bits, w->perm_row, w->perm_col,
-                                      w->block_offset, w->codes, w->scale, w->zero, stream);
+                                      w->block_offset, w->codes, w->code_bytes, w->scale, w->zero,
+                                      stream);
       e != hipSuccess)
     return MSQ_ERR_HIP;
   return MSQ_OK;
@@ -146,107 +240,58 @@ msq_status msq_quantize_pack(const uint16_t* W_bf16, const msq_weight* w, hipStr
 
 size_t msq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (check_shape(N, K) != MSQ_OK || M <= 0) return 0;
-  // enough for either kernel, so msq_gemm_ex may pick any of them
-  const size_t a = workspace_for(M, N, K, MSQ_KERNEL_GEMV);
-  const size_t b = workspace_for(M, N, K, MSQ_KERNEL_GEMM);
+  // enough for either kernel, so msq_gemm_ex with only a kernel choice fits too
+  msq::Options o;
+  o.kernel = MSQ_KERNEL_GEMV;
+  const size_t a = M <= MSQ_GEMV_MAX_M ? workspace_for(M, N, K, o) : 0;
+  o.kernel = MSQ_KERNEL_GEMM;
+  const size_t b = workspace_for(M, N, K, o);
   return a > b ? a : b;
 }
 
+size_t msq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, const msq_options* opt) {
+  msq::Options o;
+  if (!options_of(opt, o) || check_shape(N, K) != MSQ_OK || M <= 0) return 0;
+  if (!opt) return msq_gemm_workspace_bytes(M, N, K);
+  return workspace_for(M, N, K, o);
+}
+
 msq_status msq_gemm_ex(const uint16_t* x_bf16, int64_t M, const msq_weight* w, float* y,
-                       void* workspace, size_t workspace_bytes, msq_kernel kernel,
+                       void* workspace, size_t workspace_bytes, const msq_options* opt,
                        hipStream_t stream) {
-  if (kernel != MSQ_KERNEL_AUTO && kernel != MSQ_KERNEL_GEMV && kernel != MSQ_KERNEL_GEMM)
-    return MSQ_ERR_INVALID_ARG;
-  msq_status st = weight_ptrs_ok(w);
-  if (st != MSQ_OK) return st;
-  if (M < 0) return MSQ_ERR_SHAPE;
-  if (M == 0) return MSQ_OK;
-  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
-  if (!x_bf16 || !y || !aligned(x_bf16, 16) || !aligned(y, 4)) return MSQ_ERR_INVALID_ARG;
-  if (kernel == MSQ_KERNEL_AUTO) kernel = M <= MSQ_AUTO_GEMV_MAX_M ? MSQ_KERNEL_GEMV : MSQ_KERNEL_GEMM;
-  if (kernel == MSQ_KERNEL_GEMV && M > MSQ_GEMV_MAX_M) return MSQ_ERR_UNSUPPORTED;
-  const size_t need = workspace_for(M, w->N, w->K, kernel);
-  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
-  if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
-  const msq::WeightView v = view_of(w);
-  hipError_t e;
-  const uint16_t* xr = nullptr;  // reordered x left in the workspace (M > 1)
-  bool pass16 = w->tile16_blocks > 0;  // 16-bit blocks left to k_tile16
-  if (kernel == MSQ_KERNEL_GEMV) {
-    const msq::GemvPlan p = msq::plan_gemv(M, w->N, w->K);
-    e = msq::launch_gemv(x_bf16, M, v, y, workspace, p, stream);
-    xr = msq::gemv_reordered_x(workspace, p, M, w->N);
-  } else {
-    e = msq::launch_gemm(x_bf16, M, v, y, workspace, stream);
-    xr = reinterpret_cast<const uint16_t*>(workspace);
-    pass16 = pass16 && !msq::gemm_handles_tile16();
-  }
-  if (e == hipSuccess && pass16) e = msq::launch_tile16(x_bf16, xr, M, v, y, stream);
-  return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
+  msq::Options o;
+  if (!options_of(opt, o)) return MSQ_ERR_INVALID_ARG;
+  return gemm_impl(x_bf16, M, w, y, workspace, workspace_bytes, o, stream);
 }
 
 msq_status msq_gemm(const uint16_t* x_bf16, int64_t M, const msq_weight* w, float* y,
                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return msq_gemm_ex(x_bf16, M, w, y, workspace, workspace_bytes, MSQ_KERNEL_AUTO, stream);
+  return gemm_impl(x_bf16, M, w, y, workspace, workspace_bytes, msq::Options{}, stream);
 }
 
 size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight* const* w, int count) {
-  if (!w || count < 1 || count > MSQ_GROUP_MAX || M <= 0) return 0;
-  msq::WeightView v[MSQ_GROUP_MAX];
-  size_t most = 0;
-  for (int i = 0; i < count; ++i) {
-    if (!w[i] || check_shape(w[i]->N, w[i]->K) != MSQ_OK) return 0;
-    v[i] = view_of(w[i]);
-    const size_t one = msq_gemm_workspace_bytes(M, w[i]->N, w[i]->K);
-    most = one > most ? one : most;
-  }
-  // M == 1 and M > 16: every matrix keeps its own workspace (one launch for
-  // all, or split-K single calls); 2 .. 16: the matrices run one after the
-  // other
-  if (M == 1) return msq::gemv_group_workspace_m1(v, count);
-  if (M > MSQ_AUTO_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count);
-  return most;
+  return group_workspace_impl(M, w, count, msq::Options{});
+}
+
+size_t msq_gemm_group_workspace_bytes_ex(int64_t M, const msq_weight* const* w, int count,
+                                         const msq_options* opt) {
+  msq::Options o;
+  if (!options_of(opt, o) || o.kernel != MSQ_KERNEL_AUTO) return 0;
+  return group_workspace_impl(M, w, count, o);
 }
 
 msq_status msq_gemm_group(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
                           float* const* y, int count, void* workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  static_assert(MSQ_GROUP_MAX == msq::kGemvGroupMax, "group size of the header and the kernels");
-  if (!x_bf16 || !w || !y || count < 1 || count > MSQ_GROUP_MAX) return MSQ_ERR_INVALID_ARG;
-  for (int i = 0; i < count; ++i) {
-    const msq_status st = weight_ptrs_ok(w[i]);
-    if (st != MSQ_OK) return st;
-    if (!x_bf16[i] || !y[i] || !aligned(x_bf16[i], 16) || !aligned(y[i], 4))
-      return MSQ_ERR_INVALID_ARG;
-  }
-  if (M < 0) return MSQ_ERR_SHAPE;
-  if (M == 0) return MSQ_OK;
-  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
-  if (M != 1 && M <= MSQ_AUTO_GEMV_MAX_M) {
-    // one matrix after the other, sharing the workspace (ordered on stream)
-    for (int i = 0; i < count; ++i) {
-      const msq_status st = msq_gemm(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, stream);
-      if (st != MSQ_OK) return st;
-    }
-    return MSQ_OK;
-  }
-  const size_t need = msq_gemm_group_workspace_bytes(M, w, count);
-  if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
-  if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
-  msq::WeightView v[MSQ_GROUP_MAX];
-  for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
-  hipError_t e = M == 1 ? msq::launch_gemv_group_m1(x_bf16, v, y, count, workspace, stream)
-                        : msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, stream);
-  // M > 16: job i's reordered x starts its workspace share
-  const uint8_t* share = reinterpret_cast<const uint8_t*>(workspace);
-  const bool gemm16 = M > 1 && msq::gemm_handles_tile16();
-  for (int i = 0; i < count && e == hipSuccess; ++i) {
-    const uint16_t* xr = M == 1 ? nullptr : reinterpret_cast<const uint16_t*>(share);
-    if (w[i]->tile16_blocks > 0 && !gemm16)
-      e = msq::launch_tile16(x_bf16[i], xr, M, v[i], y[i], stream);
-    share += (msq::gemm_workspace_bytes(M, w[i]->N, w[i]->K) + 255) & ~(size_t)255;
-  }
-  return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
+  return group_impl(x_bf16, M, w, y, count, workspace, workspace_bytes, msq::Options{}, stream);
+}
+
+msq_status msq_gemm_group_ex(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
+                             float* const* y, int count, void* workspace, size_t workspace_bytes,
+                             const msq_options* opt, hipStream_t stream) {
+  msq::Options o;
+  if (!options_of(opt, o)) return MSQ_ERR_INVALID_ARG;
+  return group_impl(x_bf16, M, w, y, count, workspace, workspace_bytes, o, stream);
 }
 
 const char* msq_status_string(msq_status s) {

@@ -26,13 +26,22 @@ struct WeightView {
   int has16;                   // the bit map holds 16-bit (passthrough) blocks
 };
 
+// Launch choices (the public msq_options, validated by the C-ABI layer).
+struct Options {
+  int kernel = 0;      // 0 auto, 1 GEMV, 2 GEMM
+  int gemv_split = 0;  // 0 automatic
+  int gemv_waves = 0;  // 0 automatic, else 4, 8, 16 (M == 1)
+  int m1_prep = 0;     // nonzero: M == 1 always reorders x in the prep launch
+  int gemm_split = 0;  // 0 automatic
+};
+
 // ---- pack (msq_pack.hip)
 hipError_t launch_block_offsets(const uint8_t* bits, int64_t nblocks, uint32_t* offsets,
                                 hipStream_t stream);
 hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* bits,
                        const int32_t* perm_row, const int32_t* perm_col,
-                       const uint32_t* offsets, uint8_t* codes, float* scale, uint8_t* zero,
-                       hipStream_t stream);
+                       const uint32_t* offsets, uint8_t* codes, int64_t code_bytes, float* scale,
+                       uint8_t* zero, hipStream_t stream);
 
 // ---- decode GEMV, M <= 64 (msq_gemv.hip)
 struct GemvPlan {
@@ -41,23 +50,21 @@ struct GemvPlan {
   int mt;           // 16-row tiles of M
   int nw;           // wavefronts per workgroup
   int xs_stride;    // bf16 elements per LDS row of the activation slice
+  int gather;       // M == 1: the workgroups reorder x themselves (no prep launch)
   size_t lds_bytes; // dynamic LDS per workgroup
   size_t workspace; // bytes: fp32 partials (split > 1), then M == 1 prep or M > 1 gather buffers
 };
 // group_rows > 0: the plan of one matrix of a grouped launch whose matrices
 // have group_rows output rows in total (the K split then fills the GPU with
 // the whole group's workgroups).
-GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, int64_t group_rows = 0);
+GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt,
+                   int64_t group_rows = 0);
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,
                        void* workspace, const GemvPlan& plan, hipStream_t stream);
 
-// The prefill GEMM multiplies 16-bit blocks itself (16 chunks per block in
-// LDS, two block rows per workgroup); false only under the four-block-row
-// tuning override, where k_tile16 adds them instead.
-bool gemm_handles_tile16();
-
 // y[m][perm_row[n]] += the exact bf16 product of the 16-bit (passthrough)
-// blocks of every block row: one launch after the quantized kernels.  xr:
+// blocks of every block row: one launch after the decode kernel (the
+// prefill GEMM multiplies 16-bit blocks itself).  xr:
 // the reordered x [M][K] those kernels left in the workspace, or null.
 hipError_t launch_tile16(const uint16_t* x, const uint16_t* xr, int64_t M, const WeightView& w,
                          float* y, hipStream_t stream);
@@ -68,9 +75,10 @@ const uint16_t* gemv_reordered_x(void* workspace, const GemvPlan& p, int64_t M, 
 // one prep launch for those with several K ranges); the workspace holds each
 // matrix's single-call workspace in turn.
 constexpr int kGemvGroupMax = 8;
-size_t gemv_group_workspace_m1(const WeightView* w, int count);
+size_t gemv_group_workspace_m1(const WeightView* w, int count, const Options& opt);
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
-                                int count, void* workspace, hipStream_t stream);
+                                int count, void* workspace, const Options& opt,
+                                hipStream_t stream);
 
 // ---- activation gather for M > 1 (msq_gemm.hip): x_r[m][j] = x[m][perm_col[j]]
 // and the group sums of x_r split into three bf16 terms S0 + S1 + S2 (exact
@@ -89,13 +97,14 @@ hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t 
 
 // ---- prefill GEMM, any M (msq_gemm.hip).  Workspace: the gather buffers,
 // then (when the call splits K to fill the GPU) fp32 partials.
-size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, const Options& opt);
 hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float* y,
-                       void* workspace, hipStream_t stream);
+                       void* workspace, const Options& opt, hipStream_t stream);
 // Grouped prefill of count (1 .. 8) matrices at one M: one gather and one GEMM
 // launch; the workspace holds each matrix's single-call workspace in turn.
-size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count);
+size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count, const Options& opt);
 hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightView* w,
-                             float* const* y, int count, void* workspace, hipStream_t stream);
+                             float* const* y, int count, void* workspace, const Options& opt,
+                             hipStream_t stream);
 
 }  // namespace msq

@@ -131,8 +131,8 @@ constexpr int kPackThreads = 256;
 __global__ __launch_bounds__(kPackThreads) void k_pack(
     const uint16_t* __restrict__ W, int64_t N, int64_t K, const uint8_t* __restrict__ bits,
     const int32_t* __restrict__ perm_row, const int32_t* __restrict__ perm_col,
-    const uint32_t* __restrict__ offsets, uint8_t* __restrict__ codes, float* __restrict__ scale,
-    uint8_t* __restrict__ zero) {
+    const uint32_t* __restrict__ offsets, uint8_t* __restrict__ codes, int64_t code_bytes,
+    float* __restrict__ scale, uint8_t* __restrict__ zero) {
   __shared__ float tile[kBlockRows][kBlockCols + 1];
   __shared__ int cols[kBlockCols];
   __shared__ int64_t rows[kBlockRows];
@@ -142,8 +142,12 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(
   const int NBc = (int)(K / kBlockCols);
   const int64_t blk = blockIdx.x;
   const int r = (int)(blk / NBc), c = (int)(blk % NBc);
-  const int b = bits[blk];
+  int b = bits[blk];
   const int tid = threadIdx.x;
+  // a bitwidth outside the format, or a block that would end past the codes
+  // buffer (a descriptor msq_plan did not size), is written as pruned
+  const uint32_t off = offsets[blk];
+  if (segment_of(b) < 0 || off == kNoBlock || ((int64_t)off + b) * 1024 > code_bytes) b = 0;
 
   if (b == 0) {
     if (tid < kBlockRows) {
@@ -178,7 +182,7 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(
       scale[blk * kBlockRows + tid] = 0.0f;
       zero[blk * kBlockRows + tid] = 0;
     }
-    uint32_t* out = reinterpret_cast<uint32_t*>(codes + (int64_t)offsets[blk] * 1024);
+    uint32_t* out = reinterpret_cast<uint32_t*>(codes + (int64_t)off * 1024);
     for (int w = tid; w < 256 * 16; w += kPackThreads) {
       const int F = w >> 8, l = (w >> 2) & 63, d = w & 3;
       const int ib = 16 * (F >> 2) + (l & 15);
@@ -219,7 +223,7 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(
   // Word assembly.  Word index w of the block (byte 4*w): chunk t = w >> 8,
   // lane l = (w >> 2) & 63, dword d = w & 3.  For b == 3 words 0..511 hold the
   // low 2 bits (b == 2 rule) and words 512..767 the high bit (b == 1 rule).
-  uint32_t* out = reinterpret_cast<uint32_t*>(codes + (int64_t)offsets[blk] * 1024);
+  uint32_t* out = reinterpret_cast<uint32_t*>(codes + (int64_t)off * 1024);
   const int nwords = 256 * b;
   for (int w = tid; w < nwords; w += kPackThreads) {
     int width = b, plane_shift = 0, t = w >> 8;
@@ -261,12 +265,12 @@ hipError_t launch_block_offsets(const uint8_t* bits, int64_t nblocks, uint32_t* 
 
 hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* bits,
                        const int32_t* perm_row, const int32_t* perm_col,
-                       const uint32_t* offsets, uint8_t* codes, float* scale, uint8_t* zero,
-                       hipStream_t stream) {
+                       const uint32_t* offsets, uint8_t* codes, int64_t code_bytes, float* scale,
+                       uint8_t* zero, hipStream_t stream) {
   const int64_t nblk = (N / kBlockRows) * (K / kBlockCols);
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL(k_pack, dim3((unsigned)nblk), dim3(kPackThreads), 0, stream, W, N, K, bits,
-                     perm_row, perm_col, offsets, codes, scale, zero);
+                     perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
   return hipGetLastError();
 }
 

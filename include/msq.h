@@ -152,8 +152,7 @@ typedef struct {
   uint8_t *zero;              /* [N/64][K/128][64], 16-byte aligned */
   int64_t code_bytes;         /* size of the codes buffer in bytes */
   int64_t tile16_blocks;      /* number of 16-bit blocks (blocks_per_bits[16] of msq_plan);
-                                 msq_quantize_pack refuses a mismatch, msq_gemm skips the
-                                 16-bit pass when 0 */
+                                 trusted: msq_gemm skips the 16-bit pass when it is 0 */
 } msq_weight;
 
 /* Host only; needs no GPU.  Validates N, K, the bit map and both
@@ -167,18 +166,18 @@ msq_status msq_plan(int64_t N, int64_t K, const uint8_t *bits_host,
 
 /* Quantizes and packs W (bf16 bit patterns, [N][K] row-major, original
  * order, 16-byte aligned) into w->block_offset, w->codes, w->scale and
- * w->zero, asynchronously on stream.  RTN-g128 per block at the block's
- * bitwidth ("ScaleBITS" summary page, sections Approach and Limitations);
- * compact per-bitwidth buffers ("TileQuant" abstract).  Results are
- * bit-exact against the quantizer and format stated at the top of this
- * header.  This offline call is the one exception to "never synchronizes":
- * before launching it copies bits, perm_row and perm_col back to the host
- * (ordered on stream, then waited for) and validates them exactly as
- * msq_plan does, so a bad descriptor is refused instead of read out of
- * bounds.  Errors: MSQ_ERR_INVALID_ARG (null or misaligned pointer, or
- * w->tile16_blocks not the bit map's count of 16-bit blocks), MSQ_ERR_SHAPE,
- * MSQ_ERR_BITS, MSQ_ERR_PERM, MSQ_ERR_BUFFER_TOO_SMALL (w->code_bytes below
- * 1024 * sum(bits)), MSQ_ERR_HIP. */
+ * w->zero, asynchronously on stream (no host synchronization).  RTN-g128 per
+ * block at the block's bitwidth ("ScaleBITS" summary page, sections Approach
+ * and Limitations); compact per-bitwidth buffers ("TileQuant" abstract).
+ * Results are bit-exact against the quantizer and format stated at the top
+ * of this header.  Like every device call it trusts the descriptor: w->bits,
+ * w->perm_row and w->perm_col must be what msq_plan accepted, w->code_bytes
+ * at least msq_plan's code_bytes and w->tile16_blocks its
+ * blocks_per_bits[16].  The kernels never read outside W or the permutations
+ * and never write outside the buffers the descriptor sizes, even for a bad
+ * descriptor (indices are clamped, blocks past code_bytes are skipped), but
+ * the results are then unspecified.  Errors: MSQ_ERR_INVALID_ARG (null or
+ * misaligned pointer, negative tile16_blocks), MSQ_ERR_SHAPE, MSQ_ERR_HIP. */
 msq_status msq_quantize_pack(const uint16_t *W_bf16, const msq_weight *w,
                              hipStream_t stream);
 
@@ -199,20 +198,45 @@ msq_status msq_gemm(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
                     float *y, void *workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
-/* As msq_gemm, with the kernel chosen by the caller (testing and
- * benchmarking).  MSQ_ERR_UNSUPPORTED for MSQ_KERNEL_GEMV with M > 64;
- * MSQ_ERR_INVALID_ARG for an unknown kernel value. */
+/* Launch choices for msq_gemm_ex and msq_gemm_group_ex (testing and
+ * benchmarking).  A zeroed struct, or a NULL pointer, gives exactly the
+ * automatic choices of msq_gemm and msq_gemm_group; results never depend on
+ * these fields beyond fp32 summation order.  The library reads no
+ * environment variables. */
+typedef struct {
+  int32_t kernel;      /* msq_kernel: MSQ_KERNEL_AUTO (0), MSQ_KERNEL_GEMV or MSQ_KERNEL_GEMM */
+  int32_t gemv_split;  /* decode kernel: K ranges per block row; 0 = automatic, else >= 1
+                          (capped at K / 128; ranges hold at most 64 block columns) */
+  int32_t gemv_waves;  /* decode kernel at M == 1: wavefronts per workgroup; 0 = automatic,
+                          else 4, 8 or 16 */
+  int32_t m1_prep;     /* decode kernel at M == 1: nonzero = reorder x in the separate
+                          activation-prep launch even where the workgroups could do it */
+  int32_t gemm_split;  /* prefill kernel: K ranges; 0 = automatic, else >= 1 (capped at
+                          K / 1024) */
+} msq_options;
+
+/* Workspace bytes of msq_gemm_ex with these options (NULL = automatic, the
+ * same as msq_gemm_workspace_bytes).  Zero for M <= 0, a bad shape or bad
+ * options. */
+size_t msq_gemm_workspace_bytes_ex(int64_t M, int64_t N, int64_t K, const msq_options *opt);
+
+/* As msq_gemm, with the launch choices of *opt (NULL = automatic).  The
+ * workspace must hold msq_gemm_workspace_bytes_ex(M, N, K, opt) bytes.
+ * MSQ_ERR_UNSUPPORTED for MSQ_KERNEL_GEMV with M > 64; MSQ_ERR_INVALID_ARG
+ * for an unknown kernel value, a negative split or a wavefront count other
+ * than 0, 4, 8, 16. */
 msq_status msq_gemm_ex(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
                        float *y, void *workspace, size_t workspace_bytes,
-                       msq_kernel kernel, hipStream_t stream);
+                       const msq_options *opt, hipStream_t stream);
 
 /* Most matrices one msq_gemm_group call takes. */
 #define MSQ_GROUP_MAX 8
 
 /* Bytes of device workspace msq_gemm_group needs for these count matrices
- * at M rows (M == 1 and M > 64: about the sum of the single-call
- * workspaces, since all matrices are in flight together; 2 .. 64 their
- * maximum).  Zero for M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad
+ * at M rows: for M == 1 and M > MSQ_AUTO_GEMV_MAX_M about the sum of the
+ * single-call workspaces (all matrices are in flight together); for
+ * 2 .. MSQ_AUTO_GEMV_MAX_M their maximum (the matrices run one after the
+ * other).  Zero for M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad
  * shape. */
 size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int count);
 
@@ -236,6 +260,17 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int
 msq_status msq_gemm_group(const uint16_t *const *x_bf16, int64_t M,
                           const msq_weight *const *w, float *const *y, int count,
                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* msq_gemm_group_workspace_bytes and msq_gemm_group with the launch choices
+ * of *opt (NULL = automatic; kernel must be MSQ_KERNEL_AUTO, since the
+ * grouping follows the automatic kernel choice).  Errors as msq_gemm_group,
+ * plus MSQ_ERR_INVALID_ARG for bad options. */
+size_t msq_gemm_group_workspace_bytes_ex(int64_t M, const msq_weight *const *w, int count,
+                                         const msq_options *opt);
+msq_status msq_gemm_group_ex(const uint16_t *const *x_bf16, int64_t M,
+                             const msq_weight *const *w, float *const *y, int count,
+                             void *workspace, size_t workspace_bytes, const msq_options *opt,
+                             hipStream_t stream);
 
 /* ---- bitwidth allocation under a memory budget ---------------------------
  * Chooses a bitwidth per 64x128 block, from {0, 1, 2, 3, 4, 8}, so as to

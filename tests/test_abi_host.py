@@ -34,7 +34,9 @@ def declared_functions():
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert {"msq_plan", "msq_quantize_pack", "msq_gemm", "msq_gemm_ex",
-            "msq_gemm_workspace_bytes", "msq_status_string", "msq_format_version"} <= set(names)
+            "msq_gemm_workspace_bytes", "msq_gemm_workspace_bytes_ex", "msq_gemm_group",
+            "msq_gemm_group_ex", "msq_gemm_group_workspace_bytes_ex",
+            "msq_status_string", "msq_format_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -113,27 +115,55 @@ def _fake_weight(N=128, K=256, code_bytes=1 << 20):
     return w
 
 
+def _opt(kernel=0, **kw):
+    o = msq._Options()
+    o.kernel = kernel
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return ctypes.byref(o)
+
+
 def test_gemm_argument_errors_before_any_launch(lib):
     w = _fake_weight()
     x, y, ws = 1 << 41, 1 << 42, 1 << 43
     g = lib.msq_gemm_ex
-    assert g(x, 1, ctypes.byref(w), y, ws, 1 << 30, 7, None) == INVALID        # bad kernel enum
-    assert g(x, 1, None, y, ws, 1 << 30, 0, None) == INVALID                   # null weight
-    assert g(x, -1, ctypes.byref(w), y, ws, 1 << 30, 0, None) == SHAPE         # M < 0
-    assert g(None, 0, ctypes.byref(w), None, None, 0, 0, None) == OK          # M == 0: no-op
-    assert g(None, 4, ctypes.byref(w), y, ws, 1 << 30, 0, None) == INVALID     # null x
-    assert g(x + 2, 4, ctypes.byref(w), y, ws, 1 << 30, 0, None) == INVALID    # misaligned x
-    assert g(x, 65, ctypes.byref(w), y, ws, 1 << 30, 1, None) == UNSUP        # GEMV with M > 64
-    assert g(x, 600, ctypes.byref(w), y, ws, 1, 2, None) == SMALL              # workspace too small
-    assert g(x, 600, ctypes.byref(w), y, ws + 16, 1 << 30, 2, None) == INVALID  # misaligned workspace
+    big = 1 << 30
+    assert g(x, 1, ctypes.byref(w), y, ws, big, _opt(7), None) == INVALID          # bad kernel enum
+    assert g(x, 1, ctypes.byref(w), y, ws, big, _opt(gemv_waves=5), None) == INVALID
+    assert g(x, 1, ctypes.byref(w), y, ws, big, _opt(gemv_split=-1), None) == INVALID
+    assert g(x, 1, ctypes.byref(w), y, ws, big, _opt(gemm_split=-3), None) == INVALID
+    assert g(x, 1, None, y, ws, big, None, None) == INVALID                         # null weight
+    assert g(x, -1, ctypes.byref(w), y, ws, big, None, None) == SHAPE               # M < 0
+    assert g(None, 0, ctypes.byref(w), None, None, 0, None, None) == OK             # M == 0: no-op
+    assert g(None, 4, ctypes.byref(w), y, ws, big, None, None) == INVALID           # null x
+    assert g(x + 2, 4, ctypes.byref(w), y, ws, big, None, None) == INVALID          # misaligned x
+    assert g(x, 65, ctypes.byref(w), y, ws, big, _opt(1), None) == UNSUP            # GEMV with M > 64
+    assert g(x, 600, ctypes.byref(w), y, ws, 1, _opt(2), None) == SMALL             # workspace too small
+    assert g(x, 600, ctypes.byref(w), y, ws + 16, big, _opt(2), None) == INVALID    # misaligned workspace
     w2 = _fake_weight(N=100)
-    assert g(x, 1, ctypes.byref(w2), y, ws, 1 << 30, 0, None) == SHAPE
+    assert g(x, 1, ctypes.byref(w2), y, ws, big, None, None) == SHAPE
     w3 = _fake_weight()
     w3.codes = (1 << 40) + 16400  # not 256-aligned
-    assert g(x, 1, ctypes.byref(w3), y, ws, 1 << 30, 0, None) == INVALID
+    assert g(x, 1, ctypes.byref(w3), y, ws, big, None, None) == INVALID
     w4 = _fake_weight()
     w4.scale = None
-    assert lib.msq_gemm(x, 1, ctypes.byref(w4), y, ws, 1 << 30, None) == INVALID
+    assert lib.msq_gemm(x, 1, ctypes.byref(w4), y, ws, big, None) == INVALID
+
+
+def test_options_workspace_sizes(lib):
+    """msq_gemm_workspace_bytes_ex: NULL options = msq_gemm_workspace_bytes; forced K
+    splits add their fp32 partials; bad options size nothing."""
+    f = lib.msq_gemm_workspace_bytes_ex
+    for M in (1, 16, 64, 2048):
+        assert f(M, 4096, 14336, None) == lib.msq_gemm_workspace_bytes(M, 4096, 14336)
+    auto1 = f(1, 4096, 8192, _opt(1))
+    split8 = f(1, 4096, 8192, _opt(1, gemv_split=8))
+    assert split8 >= 8 * 4096 * 4 and split8 > auto1
+    g1 = f(130, 4096, 8192, _opt(2, gemm_split=1))
+    g4 = f(130, 4096, 8192, _opt(2, gemm_split=4))
+    assert g4 - g1 >= 4 * 130 * 4096 * 4
+    assert f(1, 4096, 8192, _opt(gemv_waves=3)) == 0
+    assert f(1, 4096, 8192, _opt(9)) == 0
 
 
 def test_quantize_pack_argument_errors_before_any_launch(lib):

@@ -5,9 +5,8 @@
   method is held to; y_ref is the oracle's fp64 product with the oracle's own
   dequantized weights.  With max|y_ref| == 0, y must be exactly 0.
 * Integer lattice (s = 1, integer x): y must equal y_ref exactly.
-* Full-size workloads run in the same launch configuration as bench.py
-  (msq_gemm's automatic kernel choice) and are compared on sampled block rows
-  that the oracle computes one by one.
+* Full-size workloads (test_gpu_wholesize.py) run in the same launch
+  configuration as bench.py and are compared whole, block row by block row.
 """
 import os
 
@@ -62,10 +61,10 @@ def check_pack(msq, case, block_rows=None):
     return pw, ref
 
 
-def check_y(msq, pw, case, ref, M, kernel="auto", exact=False, x=None):
+def check_y(msq, pw, case, ref, M, kernel="auto", exact=False, x=None, options=None):
     x = case.x(M) if x is None else x
-    _log(f"gemm {case.name} {case.N}x{case.K} M={M} kernel={kernel}")
-    y = msq.gemm(x, pw, kernel=kernel)
+    _log(f"gemm {case.name} {case.N}x{case.K} M={M} kernel={kernel} options={options}")
+    y = msq.gemm(x, pw, kernel=kernel, options=options)
     torch.cuda.synchronize()
     y = y.cpu().numpy().astype(np.float64)
     yref = oracle.reference_gemm(x, ref, case.perm_row, case.perm_col)
@@ -153,17 +152,16 @@ def shape_cases(msq):
 @pytest.mark.parametrize("split,waves", [(1, 8), (1, 4), (1, 16), (2, 8), (3, 8), (5, 4), (16, 16),
                                          (64, 8)])
 @pytest.mark.parametrize("name", ["mixed", "1bit", "8bit"])
-def test_decode_launch_shapes(msq, shape_cases, monkeypatch, name, split, waves):
-    """M = 1 decode in every launch shape the tuning knobs reach: full 64-column ranges
+def test_decode_launch_shapes(msq, shape_cases, name, split, waves):
+    """M = 1 decode in every launch shape the options reach: full 64-column ranges
     (wavefronts then stream more chunks than their ring holds), ragged last ranges, one
     column per range, 4 to 16 wavefronts per workgroup."""
     c, pw, ref = shape_cases[name]
-    monkeypatch.setenv("MSQ_GEMV_SPLIT", str(split))
-    monkeypatch.setenv("MSQ_GEMV_WAVES", str(waves))
-    check_y(msq, pw, c, ref, 1)
+    opt = {"gemv_split": split, "gemv_waves": waves}
+    check_y(msq, pw, c, ref, 1, options=opt)
     if split > 1:
         # again: the split counters of the last-workgroup reduction start from zero each call
-        check_y(msq, pw, c, ref, 1)
+        check_y(msq, pw, c, ref, 1, options=opt)
 
 
 def _bf16_cuda(a):
@@ -173,33 +171,30 @@ def _bf16_cuda(a):
 @pytest.mark.parametrize("waves", [8, 16])
 @pytest.mark.parametrize("N,K,seed", [(256, 8192, 70), (192, 1024, 71), (64, 128, 72),
                                       (320, 640, 73)])
-def test_decode_gather_matches_prep(msq, monkeypatch, N, K, seed, waves):
+def test_decode_gather_matches_prep(msq, N, K, seed, waves):
     """M = 1 without a K split: the decode workgroups reorder x themselves (no prep
     launch).  The result equals the prep-kernel path bit for bit (the reordered values
     are copies and the k-step sums use the same addition tree) and the oracle within
     tolerance; 64, 8, 1 and 5 block columns per row (ragged perm_col loads)."""
     c = synth.random_case(N, K, seed, dist=SMALL_DIST)
     pw, ref = check_pack(msq, c)
-    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")
-    monkeypatch.setenv("MSQ_GEMV_WAVES", str(waves))
+    opt = {"gemv_split": 1, "gemv_waves": waves}
     x = _bf16_cuda(c.x(1))
-    monkeypatch.setenv("MSQ_M1_GATHER", "0")
-    y_prep = msq.gemm(x, pw)
-    monkeypatch.setenv("MSQ_M1_GATHER", "1")
-    y_gather = msq.gemm(x, pw)
-    y_again = msq.gemm(x, pw)
+    y_prep = msq.gemm(x, pw, options=dict(opt, m1_prep=1))
+    y_gather = msq.gemm(x, pw, options=opt)
+    y_again = msq.gemm(x, pw, options=opt)
     torch.cuda.synchronize()
     assert torch.equal(y_gather, y_prep)
     assert torch.equal(y_again, y_prep)
-    check_y(msq, pw, c, ref, 1)
+    check_y(msq, pw, c, ref, 1, options=opt)
 
 
-def test_group_decode_gather_mixed(msq, group_cases, monkeypatch):
+def test_group_decode_gather_mixed(msq, group_cases):
     """A grouped M = 1 call whose jobs split between gathering workgroups (one K range)
     and the prep launch (a 16384-wide matrix needs two K ranges; placed first, in the
     middle and last): every output equals its single call on the prep path bit for
     bit, twice in a row, and the oracle within tolerance."""
-    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")
+    opt = {"gemv_split": 1}
     wide = synth.random_case(128, 16384, 74, dist=SMALL_DIST)
     cases = list(group_cases) + [(wide,) + check_pack(msq, wide)]
     xs_all = [_bf16_cuda(c.x(1)) for c, _, _ in cases]
@@ -209,10 +204,8 @@ def test_group_decode_gather_mixed(msq, group_cases, monkeypatch):
         pws = [pw for _, pw, _ in sel]
         _log(f"group decode, job order {order}")
         for rep in range(2):
-            monkeypatch.setenv("MSQ_M1_GATHER", "1")
-            outs = msq.gemm_group(xs, pws)
-            monkeypatch.setenv("MSQ_M1_GATHER", "0")
-            singles = [msq.gemm(x, pw) for x, pw in zip(xs, pws)]
+            outs = msq.gemm_group(xs, pws, options=opt)
+            singles = [msq.gemm(x, pw, options=dict(opt, m1_prep=1)) for x, pw in zip(xs, pws)]
             torch.cuda.synchronize()
             for (c, _, _), y, s in zip(sel, outs, singles):
                 assert torch.equal(y, s), c.name
@@ -268,61 +261,37 @@ def test_rejects_wrong_x_shape(msq):
         msq.gemm(c.x(65), pw, kernel="gemv")
 
 
-# ---- full-size workloads, sampled rows --------------------------------------------------
-
-def _sample_block_rows(NBr, seed):
-    g = np.random.default_rng(seed)
-    pick = {0, NBr - 1} | set(int(v) for v in g.choice(NBr, size=min(NBr, 3), replace=False))
-    return np.array(sorted(pick))
-
-
-FULL = [(w, m.name) for w in ("llama3-8b-q_proj", "llama3-8b-mlp", "llama3-8b-down_proj-prefill",
-                              "llama3-70b-layer")
-        for m in synth.WORKLOADS[w].matrices]
-
-
-@pytest.mark.parametrize("workload,matrix", FULL)
-def test_full_size_sampled(msq, workload, matrix):
-    c = synth.matrix_inputs(workload, matrix)
-    brs = _sample_block_rows(c.N // 64, 7)
-    pw, ref = check_pack(msq, c, block_rows=brs)
-    for M in synth.WORKLOADS[workload].ms:
-        check_y(msq, pw, c, ref, M)
-    del pw
-    torch.cuda.empty_cache()
-
-
 @pytest.mark.parametrize("split", ["auto", "1"])
-def test_graph_replay_matches_eager(msq, monkeypatch, split):
+def test_graph_replay_matches_eager(msq, split):
     """The decode and prefill calls are captured in HIP graphs by bench.py: every replay,
     with eager work in between, must equal the eager result bit for bit (at M = 1 with
     the automatic K split and with one K range, where the decode workgroups reorder x
     themselves)."""
-    if split != "auto":
-        monkeypatch.setenv("MSQ_GEMV_SPLIT", split)
+    opt = None if split == "auto" else {"gemv_split": int(split)}
     c = synth.random_case(1024, 4096, 50, dist=SMALL_DIST)
     pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
     for M in (1, 16, 200):
         x = torch.from_numpy(c.x(M).view(np.int16)).view(torch.bfloat16).cuda()
-        ws = torch.empty(max(msq.workspace_bytes(M, c.N, c.K), 256), dtype=torch.uint8, device="cuda")
-        y_eager = msq.gemm(x, pw)
+        ws = torch.empty(max(msq.workspace_bytes(M, c.N, c.K, options=opt), 256), dtype=torch.uint8,
+                         device="cuda")
+        y_eager = msq.gemm(x, pw, options=opt)
         y = torch.empty_like(y_eager)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            msq.gemm(x, pw, out=y, workspace=ws)
+            msq.gemm(x, pw, out=y, workspace=ws, options=opt)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            msq.gemm(x, pw, out=y, workspace=ws)
+            msq.gemm(x, pw, out=y, workspace=ws, options=opt)
         other = (-x).contiguous()
         for rep in range(3):
             y.fill_(float("nan"))
             g.replay()
             torch.cuda.synchronize()
             assert torch.equal(y, y_eager), f"replay {rep} differs at M={M}"
-            msq.gemm(other, pw, workspace=ws)  # eager work between replays, same workspace
+            msq.gemm(other, pw, workspace=ws, options=opt)  # eager work between replays, same workspace
             torch.cuda.synchronize()
 
 
@@ -339,24 +308,25 @@ def group_cases(msq):
 
 
 @pytest.mark.parametrize("M", [1, 3, 200])
-def test_group_matches_single_calls(msq, group_cases, monkeypatch, M):
+def test_group_matches_single_calls(msq, group_cases, M):
     """Each output of the grouped call equals the single call bit for bit (the same
     kernels, launch plan and summation order) and the oracle within tolerance; at
-    M == 1 with several K splits (the shapes here force them) as well, and at a
-    prefill M of two row tiles, the second ragged, with four matrices in one launch."""
-    monkeypatch.setenv("MSQ_GEMV_SPLIT", "3")
+    M == 1 with several K splits (forced to 3) as well, and at M = 200 (18 tiles,
+    too few for the one grouped GEMM launch: the group runs as split-K single calls;
+    the one-launch path is test_group_prefill_one_launch)."""
+    opt = {"gemv_split": 3}
     pws = [pw for _, pw, _ in group_cases]
     x_shared = group_cases[0][0].x(M)
     xs = [x_shared, x_shared, x_shared, group_cases[3][0].x(M)]
     _log(f"group of {len(pws)} M={M}")
     for rep in range(2):  # twice: the split counters start from zero every call
-        outs = msq.gemm_group(xs, pws)
+        outs = msq.gemm_group(xs, pws, options=opt)
         torch.cuda.synchronize()
         for (c, pw, ref), x, y in zip(group_cases, xs, outs):
-            single = msq.gemm(x, pw)
+            single = msq.gemm(x, pw, options=opt)
             torch.cuda.synchronize()
             assert torch.equal(y, single), c.name
-            check_y(msq, pw, c, ref, M, x=x)
+            check_y(msq, pw, c, ref, M, x=x, options=opt)
 
 
 def test_group_prefill_one_launch(msq):
@@ -379,18 +349,18 @@ def test_group_prefill_one_launch(msq):
 
 
 @pytest.mark.parametrize("split", [1, 2, 3, 5, 8])
-def test_gemm_split_k(msq, monkeypatch, split):
+def test_gemm_split_k(msq, split):
     """The GEMM with its K range cut into `split` pieces (ragged last piece for 3 and 5;
     partials summed in split order by the reduction): oracle within tolerance at a
     one-tile and a two-tile M, and reproducible."""
     c = synth.random_case(256, 8192, 66, dist=SMALL_DIST)
     pw, ref = check_pack(msq, c)
-    monkeypatch.setenv("MSQ_GEMM_SPLIT", str(split))
+    opt = {"gemm_split": split}
     for M in (16, 130):
         x = c.x(M)
-        check_y(msq, pw, c, ref, M, kernel="gemm", x=x)
-        a = msq.gemm(x, pw, kernel="gemm")
-        b = msq.gemm(x, pw, kernel="gemm")
+        check_y(msq, pw, c, ref, M, kernel="gemm", x=x, options=opt)
+        a = msq.gemm(x, pw, kernel="gemm", options=opt)
+        b = msq.gemm(x, pw, kernel="gemm", options=opt)
         torch.cuda.synchronize()
         assert torch.equal(a, b)
 
@@ -412,29 +382,29 @@ def test_group_sizes(msq, group_cases, M):
 
 
 @pytest.mark.parametrize("split", ["auto", "1"])
-def test_group_graph_replay_matches_eager(msq, group_cases, monkeypatch, split):
+def test_group_graph_replay_matches_eager(msq, group_cases, split):
     """bench.py captures grouped decode calls in HIP graphs: every replay, with eager
     work in between on the same workspace, must equal the eager result bit for bit;
     with the automatic split (prep launch, split counters) and with one K range (the
     workgroups reorder x themselves)."""
-    if split != "auto":
-        monkeypatch.setenv("MSQ_GEMV_SPLIT", split)
+    opt = None if split == "auto" else {"gemv_split": int(split)}
     pws = [pw for _, pw, _ in group_cases]
     x_shared = torch.from_numpy(group_cases[0][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
     x_last = torch.from_numpy(group_cases[3][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
     xs = [x_shared, x_shared, x_shared, x_last]
-    ws = torch.empty(max(msq.group_workspace_bytes(1, pws), 256), dtype=torch.uint8, device="cuda")
-    eager = [y.clone() for y in msq.gemm_group(xs, pws)]
+    ws = torch.empty(max(msq.group_workspace_bytes(1, pws, options=opt), 256), dtype=torch.uint8,
+                     device="cuda")
+    eager = [y.clone() for y in msq.gemm_group(xs, pws, options=opt)]
     outs = [torch.empty_like(y) for y in eager]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        msq.gemm_group(xs, pws, outs=outs, workspace=ws)
+        msq.gemm_group(xs, pws, outs=outs, workspace=ws, options=opt)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        msq.gemm_group(xs, pws, outs=outs, workspace=ws)
+        msq.gemm_group(xs, pws, outs=outs, workspace=ws, options=opt)
     others = [(-x).contiguous() for x in xs]
     for rep in range(3):
         for o in outs:
@@ -443,5 +413,110 @@ def test_group_graph_replay_matches_eager(msq, group_cases, monkeypatch, split):
         torch.cuda.synchronize()
         for o, e in zip(outs, eager):
             assert torch.equal(o, e), f"replay {rep} differs"
-        msq.gemm_group(others, pws, workspace=ws)  # eager work between replays
+        msq.gemm_group(others, pws, workspace=ws, options=opt)  # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---- shipped branches that the full-size workloads do not reach ------------------------
+
+def test_prefill_wide_n_scatters_directly(msq):
+    """N > 32768 (a vocabulary-sized output): the prefill GEMM stores y through perm_row
+    itself instead of the row un-permutation pass (whose LDS row holds at most 32768
+    floats); single call, and a group of two in one GEMM launch (1028 tiles)."""
+    c = synth.random_case(32832, 128, 90, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    M = 130
+    x = c.x(M)
+    check_y(msq, pw, c, ref, M, x=x)
+    xd = _bf16_cuda(x)
+    single = msq.gemm(xd, pw)
+    outs = msq.gemm_group([xd, xd], [pw, pw])
+    torch.cuda.synchronize()
+    for y in outs:
+        assert torch.equal(y, single)
+
+
+@pytest.mark.parametrize("M,kernel", [(1, "auto"), (2, "auto"), (2, "gemm"), (130, "auto")])
+def test_long_k_unstaged_gather(msq, M, kernel):
+    """K = 32896 (> 32768): the activation gather reads x from global memory instead of
+    an LDS copy of the row (64 KiB at most); decode at M = 1 and 2, prefill at M = 2 and
+    130."""
+    c = synth.random_case(128, 32896, 91, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    check_y(msq, pw, c, ref, M, kernel=kernel)
+
+
+@pytest.mark.parametrize("M", [1, 4])
+def test_long_k_tile16_pass(msq, M):
+    """16-bit blocks with K = 32896 after the decode kernel: at M = 1 the 16-bit pass
+    gathers x through perm_col itself in its four-block-row form (k_tile16<4>: the
+    one-row LDS copy of x holds at most 32768 columns); at M = 4 it reads the reordered
+    x the decode kernel left in the workspace."""
+    from test_gpu_tile16 import MIX16
+    c = synth.random_case(128, 32896, 92, dist=MIX16)
+    pw, ref = check_pack(msq, c)
+    assert pw.tile16_blocks > 0
+    check_y(msq, pw, c, ref, M)
+
+
+def test_pack_guard_short_codes_buffer(msq):
+    """msq_quantize_pack trusts the descriptor (no host read-back) but never writes past
+    it: with code_bytes below what the bit map needs, the blocks that would end past it
+    are written as pruned (scale and zero point 0) and the bytes after code_bytes stay
+    untouched; every other block is packed exactly as usual."""
+    import ctypes
+    c = synth.random_case(256, 1024, 93, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    full = pw.code_bytes
+    short = (full // 2048) * 1024  # about half, whole KiB
+    codes = torch.full((full + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    scale = torch.full_like(pw.scale, 7.0)
+    zero = torch.full_like(pw.zero, 9)
+    w = pw.descriptor()
+    w.codes = codes.data_ptr()
+    w.code_bytes = short
+    w.scale = scale.data_ptr()
+    w.zero = zero.data_ptr()
+    lib = msq.load_library()
+    Wd = _bf16_cuda(c.W)
+    assert lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), None) == 0
+    torch.cuda.synchronize()
+    got = codes.cpu().numpy()
+    assert (got[short:] == 0xAB).all(), "bytes past code_bytes were written"
+    off, _ = oracle.block_offsets(c.bits)
+    fits = (off != oracle.NO_BLOCK) & ((off.astype(np.int64) + c.bits) * 1024 <= short)
+    want_codes = pw.codes.cpu().numpy()[:short]
+    have_s = scale.cpu().numpy()
+    have_z = zero.cpu().numpy()
+    ref_s = pw.scale.cpu().numpy()
+    ref_z = pw.zero.cpu().numpy()
+    for r, cc in zip(*np.nonzero(fits)):
+        o, b = int(off[r, cc]) * 1024, int(c.bits[r, cc])
+        assert np.array_equal(got[o:o + 1024 * b], want_codes[o:o + 1024 * b])
+        assert np.array_equal(have_s[r, cc].view(np.uint32), ref_s[r, cc].view(np.uint32))
+        assert np.array_equal(have_z[r, cc], ref_z[r, cc])
+    skipped = ~fits & (c.bits != 0)
+    assert skipped.any()
+    assert (have_s[skipped] == 0).all() and (have_z[skipped] == 0).all()
+
+
+def test_options_rejected(msq):
+    """msq_gemm_ex refuses options outside their documented values before any launch."""
+    c = synth.random_case(64, 128, 94)
+    pw, _ = check_pack(msq, c)
+    for bad in ({"gemv_waves": 5}, {"gemv_split": -1}, {"gemm_split": -2}):
+        with pytest.raises(msq.MsqError):
+            msq.gemm(c.x(1), pw, options=bad)
+    with pytest.raises(msq.MsqError):  # the grouped call takes no kernel choice
+        import ctypes
+        lib = msq.load_library()
+        o = msq._Options()
+        o.kernel = 1
+        descs, arr = msq._descriptor_array([pw])
+        x = _bf16_cuda(c.x(1))
+        y = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+        ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+        xa = (ctypes.c_void_p * 1)(x.data_ptr())
+        ya = (ctypes.c_void_p * 1)(y.data_ptr())
+        msq._check(lib.msq_gemm_group_ex(xa, 1, arr, ya, 1, ws.data_ptr(), ws.numel(),
+                                         ctypes.byref(o), None), "msq_gemm_group_ex")

@@ -26,14 +26,13 @@ def msq():
 
 @pytest.mark.parametrize("N,K,dist,seed", [(256, 1024, MIX16, 80), (192, 384, TQ, 81),
                                            (64, 128, {16: 1.0}, 82), (512, 8192, MIX16, 83)])
-def test_pack_and_products(msq, monkeypatch, N, K, dist, seed):
+def test_pack_and_products(msq, N, K, dist, seed):
     c = synth.random_case(N, K, seed, dist=dist)
     pw, ref = check_pack(msq, c)
     assert pw.tile16_blocks == int((c.bits == 16).sum())
     for M, kernel in ((1, "auto"), (4, "auto"), (4, "gemm"), (64, "gemv"), (130, "auto")):
         check_y(msq, pw, c, ref, M, kernel=kernel)
-    monkeypatch.setenv("MSQ_GEMV_SPLIT", "1")  # M = 1 with the workgroups reordering x
-    check_y(msq, pw, c, ref, 1)
+    check_y(msq, pw, c, ref, 1, options={"gemv_split": 1})  # the workgroups reorder x
 
 
 def test_integer_lattice_exact(msq):
@@ -63,13 +62,25 @@ def test_group_matches_single(msq):
             assert torch.equal(y, msq.gemm(x, pw))
 
 
-def test_descriptor_count_must_match(msq):
-    """msq_quantize_pack refuses a descriptor whose 16-bit block count is wrong."""
-    import ctypes
-    c = synth.random_case(128, 256, 86, dist=MIX16)
-    pw = msq.quantize_pack(c.W, c.bits, c.perm_row, c.perm_col)
-    w = pw.descriptor()
-    w.tile16_blocks = pw.tile16_blocks + 1
-    Wd = _bf16_cuda(c.W)
-    lib = msq.load_library()
-    assert lib.msq_quantize_pack(Wd.data_ptr(), ctypes.byref(w), None) == 1
+def test_group_one_launch_with_16bit_blocks(msq):
+    """Groups that reach the one grouped GEMM launch (two 4096 x 1024 matrices at
+    M = 1024: 512 tiles): with 16-bit blocks in both (the 16-chunk kernel variant
+    k_gemm_group<16>), and mixing a matrix with them and one without (the whole
+    launch then takes the 16-chunk variant).  Each output equals its single call bit
+    for bit and the oracle within tolerance."""
+    M = 1024
+    plain = synth.random_case(4096, 1024, 87, dist={1: .2, 2: .5, 4: .2, 8: .1})
+    mix = synth.random_case(4096, 1024, 88, dist=MIX16)
+    tq = synth.random_case(4096, 1024, 89, dist=TQ)
+    packed = {c.name: (c,) + check_pack(msq, c) for c in (plain, mix, tq)}
+    x = _bf16_cuda(mix.x(M))
+    for names in ((mix.name, tq.name), (plain.name, mix.name)):
+        sel = [packed[n] for n in names]
+        outs = msq.gemm_group([x, x], [pw for _, pw, _ in sel])
+        torch.cuda.synchronize()
+        for (c, pw, ref), y in zip(sel, outs):
+            single = msq.gemm(x, pw)
+            torch.cuda.synchronize()
+            assert torch.equal(y, single), c.name
+            check_y(msq, pw, c, ref, M, x=mix.x(M))
+
