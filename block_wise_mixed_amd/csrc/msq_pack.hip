@@ -1,11 +1,17 @@
 // Quantize-and-pack kernels for gfx950.
 //
 //   k_block_offsets : exclusive prefix sum of the block bit map over the packed
-//                     order (segments b = 1,2,3,4,8; row-major inside), in KiB.
-//   k_pack          : one workgroup per 64x128 block: gather the reordered
-//                     block from W through perm_row / perm_col, compute one
-//                     asymmetric RTN-g128 scale and zero point per row, and
-//                     write the block's codes in packed format v1.
+//                     order (segments b = 1,2,3,4,8,16; row-major inside), in KiB.
+//   k_pack_rows     : K <= 32768.  One workgroup per (block row, row n of a
+//                     16-row tile): it streams the four original rows behind
+//                     reordered rows n, n + 16, n + 32, n + 48 of the block row
+//                     into LDS (coalesced, each W row read once), gathers
+//                     them through perm_col there, computes each (row, block)
+//                     scale and zero point and the codes, and writes the
+//                     packed words those four rows fill.
+//   k_pack_blocks   : any K (used above 32768, where a row no longer fits
+//                     the LDS): one workgroup per 64x128 block, gathering it
+//                     element by element from W.
 //
 // Precision per 64x128 block after two-way reordering: "ScaleBITS" summary
 // page, section Approach.  RTN with group size 128: same page, section
@@ -38,80 +44,119 @@ __device__ __forceinline__ int segment_of(int b) {
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 16;  // consecutive blocks per thread per pass
 constexpr int kSegs = 6;
 __constant__ int kSegBits[kSegs] = {1, 2, 3, 4, 8, 16};
 
-// One workgroup.  Thread t owns a contiguous run of the row-major block list,
-// counts the blocks of each bitwidth in it, and after a workgroup-wide
-// exclusive scan of those counts assigns offset = segment base + b * rank.
+// One workgroup, two sweeps over the bit map in passes of kScanThreads *
+// kScanPer blocks (thread t takes 16 consecutive blocks of a pass, so the
+// loads and stores of a wavefront are contiguous).  Sweep 1 counts the
+// blocks of every bitwidth: segment k starts at the sum of bits over the
+// segments before it.  Sweep 2 scans the per-thread counts of each pass
+// (wavefront prefix sums, then across wavefronts) on top of the counts of
+// the passes before, and assigns offset = segment base + b * rank.
 __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* __restrict__ bits,
                                                                 int64_t nblk,
                                                                 uint32_t* __restrict__ off) {
   __shared__ uint32_t wave_tot[kSegs][kScanThreads / 64];
   __shared__ uint32_t seg_base[kSegs];
+  __shared__ uint32_t seg_run[kSegs];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int64_t per = (nblk + kScanThreads - 1) / kScanThreads;
-  const int64_t beg = (int64_t)tid * per;
-  const int64_t end = beg + per < nblk ? beg + per : nblk;
+  const int64_t pass_blocks = (int64_t)kScanThreads * kScanPer;
 
-  uint32_t cnt[kSegs] = {0, 0, 0, 0, 0, 0};
-  for (int64_t i = beg; i < end; ++i) {
-    int k = segment_of(bits[i]);
-    if (k >= 0) cnt[k]++;
+  auto load16 = [&](int64_t i0, int (&seg)[kScanPer]) __attribute__((always_inline)) {
+    uint8_t v[kScanPer];
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) v[e] = i0 + e < nblk ? bits[i0 + e] : 0;
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) seg[e] = segment_of(v[e]);
+  };
+  // sweep 1: totals per segment
+  uint32_t tot[kSegs] = {0, 0, 0, 0, 0, 0};
+  for (int64_t p0 = 0; p0 < nblk; p0 += pass_blocks) {
+    int seg[kScanPer];
+    load16(p0 + (int64_t)tid * kScanPer, seg);
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e)
+#pragma unroll
+      for (int k = 0; k < kSegs; ++k) tot[k] += seg[e] == k ? 1u : 0u;
   }
-  // inclusive scan inside the wave, per segment
-  uint32_t incl[kSegs];
 #pragma unroll
   for (int k = 0; k < kSegs; ++k) {
-    uint32_t v = cnt[k];
+    uint32_t v = tot[k];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      uint32_t u = __shfl_up(v, d, 64);
-      if (lane >= d) v += u;
-    }
-    incl[k] = v;
-    if (lane == 63) wave_tot[k][wave] = v;
-  }
-  __syncthreads();
-  if (tid < kSegs) {
-    // scan of wave totals for segment tid, kept in place as exclusive prefixes
-    uint32_t run = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) {
-      uint32_t t = wave_tot[tid][w];
-      wave_tot[tid][w] = run;
-      run += t;
-    }
-    seg_base[tid] = run;  // total count for now
+    for (int d = 32; d > 0; d >>= 1) v += __shfl_xor(v, d, 64);
+    if (lane == 0) wave_tot[k][wave] = v;
   }
   __syncthreads();
   if (tid == 0) {
     uint32_t acc = 0;
     for (int k = 0; k < kSegs; ++k) {
-      uint32_t total = seg_base[k];
+      uint32_t total = 0;
+      for (int w = 0; w < kScanThreads / 64; ++w) total += wave_tot[k][w];
       seg_base[k] = acc;
+      seg_run[k] = 0;
       acc += (uint32_t)kSegBits[k] * total;
     }
   }
   __syncthreads();
-  uint32_t rank[kSegs];
+  // sweep 2: ranks and offsets
+  for (int64_t p0 = 0; p0 < nblk; p0 += pass_blocks) {
+    const int64_t i0 = p0 + (int64_t)tid * kScanPer;
+    int seg[kScanPer];
+    load16(i0, seg);
+    uint32_t cnt[kSegs], incl[kSegs];
 #pragma unroll
-  for (int k = 0; k < kSegs; ++k) rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
-  for (int64_t i = beg; i < end; ++i) {
-    const int b = bits[i];
-    const int k = segment_of(b);
-    if (k < 0) {
-      off[i] = kNoBlock;
-    } else {
-      off[i] = seg_base[k] + (uint32_t)b * rank[k];
-      rank[k]++;
+    for (int k = 0; k < kSegs; ++k) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e) c += seg[e] == k ? 1u : 0u;
+      cnt[k] = c;
+      uint32_t v = c;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t u = __shfl_up(v, d, 64);
+        if (lane >= d) v += u;
+      }
+      incl[k] = v;
+      if (lane == 63) wave_tot[k][wave] = v;
     }
+    __syncthreads();
+    if (tid < kSegs) {  // exclusive prefixes over the wavefronts, on top of the earlier passes
+      uint32_t run = seg_run[tid];
+      for (int w = 0; w < kScanThreads / 64; ++w) {
+        const uint32_t t = wave_tot[tid][w];
+        wave_tot[tid][w] = run;
+        run += t;
+      }
+      seg_run[tid] = run;
+    }
+    __syncthreads();
+    uint32_t rank[kSegs];
+#pragma unroll
+    for (int k = 0; k < kSegs; ++k) rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
+#pragma unroll
+    for (int e = 0; e < kScanPer; ++e) {
+      uint32_t o = kNoBlock;
+#pragma unroll
+      for (int k = 0; k < kSegs; ++k)
+        if (seg[e] == k) {
+          o = seg_base[k] + (uint32_t)kSegBits[k] * rank[k];
+          rank[k]++;
+        }
+      if (i0 + e < nblk) off[i0 + e] = o;
+    }
+    __syncthreads();  // wave_tot is rewritten by the next pass
   }
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) {
   return __uint_as_float((uint32_t)u << 16);
 }
+
+// Column index clamped into [0, K - 1] (K <= 32768, so it fits 16 bits).
+__device__ __forceinline__ int clampi_pack(int v, int hi) { return v < 0 ? 0 : (v > hi ? hi : v); }
 
 // Code of one weight: clamp(rint(w / s) + z, 0, qmax); 0 when s == 0.
 __device__ __forceinline__ uint32_t rtn_code(float w, float s, float z, float qmax) {
@@ -123,12 +168,12 @@ __device__ __forceinline__ uint32_t rtn_code(float w, float s, float z, float qm
 
 constexpr int kPackThreads = 256;
 
-// One workgroup per block.  The block's 64 x 128 reordered weights are
+// One workgroup per block (any K).  The block's 64 x 128 reordered weights are
 // gathered into LDS (perm_row picks the row, perm_col the column), each row's
 // scale and zero point are computed from that row's 128 values, then every
 // thread assembles whole 32-bit words of the packed block so the global
 // stores are coalesced.
-__global__ __launch_bounds__(kPackThreads) void k_pack(
+__global__ __launch_bounds__(kPackThreads) void k_pack_blocks(
     const uint16_t* __restrict__ W, int64_t N, int64_t K, const uint8_t* __restrict__ bits,
     const int32_t* __restrict__ perm_row, const int32_t* __restrict__ perm_col,
     const uint32_t* __restrict__ offsets, uint8_t* __restrict__ codes, int64_t code_bytes,
@@ -254,6 +299,278 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(
   }
 }
 
+// ---- row-streaming pack (K <= 32768) ----------------------------------------------------
+//
+// Which rows fill which words.  In the packed format, dword d of lane
+// l = n + 16 kg of every chunk of a block holds codes of rows 16 rt + n only
+// (rt = 0..3, the row tiles): for b = 4, 8, 16 a word holds one row's codes,
+// for b = 1, 2, 3 it mixes the four (b = 1, and the high plane of b = 3) or
+// two (b = 2, the low plane of b = 3) rows 16 apart.  So the four rows
+// n, n + 16, n + 32, n + 48 of a block row complete exactly the 16-byte lane
+// slices n + 16 kg (kg = 0..3) of every chunk, and nothing else.
+//
+// Work split inside the workgroup: 8 or 16 wavefronts x 4 groups of 16 lanes;
+// group g of wavefront w takes block columns c = (4 x wavefronts) j + 4 w + g
+// (round j), and lane
+// (kg, d) = (lane >> 2, lane & 3) of the group takes the eight columns
+// jb = 32 kt + 8 kg + 2 d + h (kt = 0..3, h = 0, 1) of that block column:
+// exactly the codes of its dword d of the lane slice n + 16 kg, for every
+// bitwidth.  The group's min / max run over its 16 lanes (one DPP row).
+//
+// Codes without a division per weight: q = rint(fl(w / s)) is taken as
+// rint(w * rcp(s)) unless w * rcp(s) lies within 2^-13 of a half-integer.
+// v_rcp_f32 is within 1 ulp, so w * rcp(s) differs from w / s by at most
+// 1.5 * 2^-23 relative, and fl(w / s) from w / s by 2^-24 relative; with
+// |w / s| <= 255 (w lies in [lo, hi], s = (hi - lo) / qmax) both stay within
+// 6.1e-5 < 2^-13 of each other, so outside that band both round to the same
+// integer.  Inside the band, and when s is not a normal number at most
+// 2^125, the correctly rounded division decides.  Bit-identical to rint of
+// the correctly rounded quotient for every input.
+constexpr int kRowMaxK = 32768;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// DPP row (16-lane) reductions: xor 1, xor 2 (quad permutes), then the
+// half-row and row mirrors pair the remaining partners.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                               0xF, 0xF, false));
+}
+__device__ __forceinline__ float row_min16(float v) {
+  v = fminf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fminf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fminf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fminf(v, dpp_f<0x140>(v));  // row_mirror
+  return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
+// clamp(rint(fl(x / s)) + z, 0, qmax) for s > 0 (see above); rs = rcp(s),
+// fast = s is a normal number <= 2^125.
+__device__ __forceinline__ uint32_t code_of(float x, float s, float rs, bool fast, float z,
+                                            float qmax) {
+  const float t = x * rs;
+  float r = __builtin_rintf(t);
+  const bool near = fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
+  if (!fast || near) r = __builtin_rintf(x / s);
+  return (uint32_t)fminf(fmaxf(r + z, 0.0f), qmax);
+}
+
+// kThreads threads (4 groups of 16 lanes per wavefront), at most kRounds
+// rounds of 4 * kThreads / 64 block columns: K <= 8192 (512 threads, 2
+// rounds), 16384 (512, 4), 32768 (1024, 4).  The per-round registers are
+// static, so fewer rounds hold fewer of them.
+template <int kThreads, int kRounds>
+__global__ __launch_bounds__(kThreads) void k_pack_rows(
+    const uint16_t* __restrict__ W, int64_t N, int64_t K, const uint8_t* __restrict__ bits,
+    const int32_t* __restrict__ perm_row, const int32_t* __restrict__ perm_col,
+    const uint32_t* __restrict__ offsets, uint8_t* __restrict__ codes, int64_t code_bytes,
+    float* __restrict__ scale, uint8_t* __restrict__ zero) {
+  constexpr int kCols = 4 * kThreads / 64;  // block columns per round
+  extern __shared__ __align__(16) uint16_t rowbuf[];  // two rows of K bf16
+  const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);
+  // The 16 workgroups of a block row run on one XCD (consecutive workgroup
+  // ids go to the XCDs in turn), so the partial lines they write of each
+  // chunk, scale and zero-point row meet in one L2.
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, j16 = bid >> 3;
+  const int r = 8 * (j16 >> 4) + xcd, n = j16 & 15;
+  if (r >= NBr) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, lam = lane & 15, kg = lam >> 2, d = lam & 3;
+  const int kk = (int)K - 1;
+
+  // rows 16 rt + n of block row r, clamped original indices
+  int orow[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int pr = perm_row[(int64_t)r * kBlockRows + 16 * rt + n];
+    orow[rt] = pr < 0 ? 0 : (pr >= N ? (int)(N - 1) : pr);
+  }
+  // Row rt of the tile into LDS buffer rt & 1: 16 bytes per lane, lane i of
+  // the wavefront landing 16 i bytes past the wavefront's base.
+  const int nchunks = (int)(K / 8);
+  auto load_row = [&](int rt) __attribute__((always_inline)) {
+    const uint16_t* src = W + (int64_t)orow[rt] * K;
+    uint16_t* dst = rowbuf + (rt & 1) * K;
+    for (int base = wave * 64; base < nchunks; base += kThreads) {
+      const int idx = base + lane;
+      if (idx < nchunks)
+        __builtin_amdgcn_global_load_lds(src + 8 * idx, (lds_void_t*)(dst + 8 * base), 16, 0, 0);
+    }
+  };
+  load_row(0);
+
+  // per round: bitwidth, offset, and this lane's eight column indices
+  // (pk[j][kt] = perm_col of jb = 32 kt + 2 lam and + 1, as two 16-bit halves)
+  int bw[kRounds];
+  uint32_t off[kRounds];
+  uint32_t pk[kRounds][4];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int c = kCols * j + 4 * wave + g;
+    bw[j] = -1;  // no column
+    off[j] = 0;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) pk[j][kt] = 0;
+    if (c < NBc) {
+      const int64_t blk = (int64_t)r * NBc + c;
+      int b = bits[blk];
+      const uint32_t o = offsets[blk];
+      // a bitwidth outside the format, or a block that would end past the
+      // codes buffer (a descriptor msq_plan did not size), is written as pruned
+      if (segment_of(b) < 0 || o == kNoBlock || ((int64_t)o + b) * 1024 > code_bytes) b = 0;
+      bw[j] = b;
+      off[j] = o;
+      const int32_t* pc = perm_col + (int64_t)c * kBlockCols + 2 * lam;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const int2 p = *reinterpret_cast<const int2*>(pc + 32 * kt);
+        pk[j][kt] = (uint32_t)clampi_pack(p.x, kk) | ((uint32_t)clampi_pack(p.y, kk) << 16);
+      }
+    }
+  }
+
+  // words of 1-, 2- and 3-bit blocks collect the four rows: [j][chunk]
+  uint32_t acc[kRounds][3];
+  // a row's other outputs are held and stored after the next row's barrier,
+  // so that the wait there never waits for stores issued just before it:
+  // scale, zero point, and the words of 4-, 8-, 16-bit blocks (row rt: 4 bits
+  // chunk rt; 8 bits chunks 2 rt, 2 rt + 1; 16 bits chunks 4 rt + kt)
+  float hs[kRounds];
+  uint32_t hz[kRounds];
+  uint32_t hw[kRounds][4];
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    acc[j][0] = acc[j][1] = acc[j][2] = 0;
+    hs[j] = 0.0f;
+    hz[j] = 0;
+    hw[j][0] = hw[j][1] = hw[j][2] = hw[j][3] = 0;
+  }
+  // this lane's byte offset inside a chunk: lane n + 16 kg, dword d
+  const uint32_t lane_off = 16 * n + 256 * kg + 4 * d;
+
+  auto flush = [&](int rt) __attribute__((always_inline)) {  // the held outputs of row rt
+    const int i = 16 * rt + n;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      const int b = bw[j];
+      if (b < 0) continue;  // uniform over the group
+      const int c = kCols * j + 4 * wave + g;
+      const int64_t blk = (int64_t)r * NBc + c;
+      if (lam == 0) {
+        scale[blk * kBlockRows + i] = hs[j];
+        zero[blk * kBlockRows + i] = (uint8_t)hz[j];
+      }
+      uint8_t* cb = codes + (int64_t)off[j] * 1024 + lane_off;
+      if (b == 4) {
+        *reinterpret_cast<uint32_t*>(cb + 1024 * rt) = hw[j][0];
+      } else if (b == 8) {
+        *reinterpret_cast<uint32_t*>(cb + 1024 * (2 * rt)) = hw[j][0];
+        *reinterpret_cast<uint32_t*>(cb + 1024 * (2 * rt + 1)) = hw[j][1];
+      } else if (b == 16) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) *reinterpret_cast<uint32_t*>(cb + 1024 * (4 * rt + kt)) = hw[j][kt];
+      }
+    }
+  };
+
+  for (int rt = 0; rt < 4; ++rt) {
+    // row rt has landed (this wavefront's copies: vmcnt; everyone's: the
+    // barrier), and every wavefront is done with buffer (rt + 1) & 1
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (rt + 1 < 4) load_row(rt + 1);
+    if (rt > 0) flush(rt - 1);
+    const uint16_t* row = rowbuf + (rt & 1) * K;
+#pragma unroll
+    for (int j = 0; j < kRounds; ++j) {
+      if (kCols * j >= NBc) break;  // uniform: no group of this round or later has a column
+      const int b = bw[j];
+      if (b < 0) continue;          // uniform over the group (one DPP row)
+      uint16_t u[4][2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        u[kt][0] = row[pk[j][kt] & 0xFFFFu];
+        u[kt][1] = row[pk[j][kt] >> 16];
+      }
+      if (b == 0 || b == 16) {
+        hs[j] = 0.0f;
+        hz[j] = 0;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)  // 16 bits: the bf16 bit patterns
+          hw[j][kt] = (uint32_t)u[kt][0] | ((uint32_t)u[kt][1] << 16);
+        continue;
+      }
+      float x[4][2];
+      float lo = 0.0f, hi = 0.0f;  // the range always contains 0
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          x[kt][h] = bf16_to_f32(u[kt][h]);
+          lo = fminf(lo, x[kt][h]);
+          hi = fmaxf(hi, x[kt][h]);
+        }
+      lo = row_min16(lo);
+      hi = row_max16(hi);
+      const float qmax = (float)((1 << b) - 1);
+      const float s = (hi - lo) / qmax;
+      float z = 0.0f;
+      if (s > 0.0f) z = fminf(fmaxf(__builtin_rintf((-lo) / s), 0.0f), qmax);
+      hs[j] = s;
+      hz[j] = (uint32_t)z;
+      uint32_t p[4];
+      if (s > 0.0f) {
+        const bool fast = s >= 0x1p-126f && s <= 0x1p125f;
+        const float rs = __builtin_amdgcn_rcpf(s);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          p[kt] = code_of(x[kt][0], s, rs, fast, z, qmax) |
+                  (code_of(x[kt][1], s, rs, fast, z, qmax) << 16);
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) p[kt] = 0;
+      }
+      if (b == 1) {  // chunk 0, slot 4 rt + kt
+        acc[j][0] |= (p[0] | (p[1] << 1) | (p[2] << 2) | (p[3] << 3)) << (4 * rt);
+      } else if (b <= 3) {  // (low plane) chunk rt >> 1, slot 4 (rt & 1) + kt
+        const uint32_t m = b == 3 ? 0x00030003u : 0xFFFFFFFFu;
+        const uint32_t v = ((p[0] & m) | ((p[1] & m) << 2) | ((p[2] & m) << 4) | ((p[3] & m) << 6))
+                           << (8 * (rt & 1));
+        if (rt < 2) acc[j][0] |= v;
+        else acc[j][1] |= v;
+        if (b == 3)  // high plane: chunk 2, slot 4 rt + kt
+          acc[j][2] |= (((p[0] >> 2) & 0x00010001u) | (((p[1] >> 2) & 0x00010001u) << 1) |
+                        (((p[2] >> 2) & 0x00010001u) << 2) | (((p[3] >> 2) & 0x00010001u) << 3))
+                       << (4 * rt);
+      } else if (b == 4) {  // chunk rt, slot kt
+        hw[j][0] = p[0] | (p[1] << 4) | (p[2] << 8) | (p[3] << 12);
+      } else {  // 8: chunks 2 rt and 2 rt + 1, slots kt & 1
+        hw[j][0] = p[0] | (p[1] << 8);
+        hw[j][1] = p[2] | (p[3] << 8);
+      }
+    }
+  }
+  flush(3);
+  // the words the four rows completed together
+#pragma unroll
+  for (int j = 0; j < kRounds; ++j) {
+    const int b = bw[j];
+    if (b < 1 || b > 3) continue;
+    uint8_t* cb = codes + (int64_t)off[j] * 1024 + lane_off;
+    *reinterpret_cast<uint32_t*>(cb) = acc[j][0];
+    if (b >= 2) *reinterpret_cast<uint32_t*>(cb + 1024) = acc[j][1];
+    if (b == 3) *reinterpret_cast<uint32_t*>(cb + 2048) = acc[j][2];
+  }
+}
+
 }  // namespace
 
 hipError_t launch_block_offsets(const uint8_t* bits, int64_t nblocks, uint32_t* offsets,
@@ -269,8 +586,23 @@ hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* b
                        uint8_t* zero, hipStream_t stream) {
   const int64_t nblk = (N / kBlockRows) * (K / kBlockCols);
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)nblk), dim3(kPackThreads), 0, stream, W, N, K, bits,
-                     perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
+  if (K <= kRowMaxK) {
+    // 16 workgroups per block row, block rows in groups of 8 (one per XCD)
+    const int64_t grid = 128 * ((N / kBlockRows + 7) / 8);
+    const size_t lds = (size_t)K * 4;
+    if (K <= 8192)
+      hipLaunchKernelGGL((k_pack_rows<512, 2>), dim3((unsigned)grid), dim3(512), lds, stream, W, N,
+                         K, bits, perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
+    else if (K <= 16384)
+      hipLaunchKernelGGL((k_pack_rows<512, 4>), dim3((unsigned)grid), dim3(512), lds, stream, W, N,
+                         K, bits, perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
+    else
+      hipLaunchKernelGGL((k_pack_rows<1024, 4>), dim3((unsigned)grid), dim3(1024), lds, stream, W,
+                         N, K, bits, perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
+  } else {
+    hipLaunchKernelGGL(k_pack_blocks, dim3((unsigned)nblk), dim3(kPackThreads), 0, stream, W, N, K,
+                       bits, perm_row, perm_col, offsets, codes, code_bytes, scale, zero);
+  }
   return hipGetLastError();
 }
 
