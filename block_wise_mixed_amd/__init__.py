@@ -24,7 +24,7 @@ import numpy as np
 
 __all__ = ["MsqError", "PackedWeight", "plan", "quantize_pack", "allocate_packed", "pack_into",
            "pack_bytes", "gemm", "workspace_bytes",
-           "OPTION_FIELDS",
+           "OPTION_FIELDS", "gemm_noalloc", "NOALLOC_SCRATCH_BYTES",
            "gemm_group", "group_workspace_bytes", "GROUP_MAX",
            "library_path", "load_library", "KERNELS", "FORMAT_VERSION", "GEMV_MAX_M",
            "allocate_bits", "alloc_workspace_bytes", "ALLOC_LEVELS", "reorder_channels"]
@@ -130,6 +130,8 @@ def load_library():
     lib.msq_reorder_workspace_bytes.restype = sz
     lib.msq_reorder_channels.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp, vp, sz, vp]
     lib.msq_reorder_channels.restype = ctypes.c_int
+    lib.msq_gemm_noalloc.argtypes = [vp, i64, ctypes.POINTER(_Weight), vp, vp]
+    lib.msq_gemm_noalloc.restype = ctypes.c_int
     lib.msq_status_string.argtypes = [ctypes.c_int]
     lib.msq_status_string.restype = ctypes.c_char_p
     lib.msq_format_version.argtypes = []
@@ -391,6 +393,27 @@ def gemm(x, pw: PackedWeight, kernel: str = "auto", out=None, workspace=None, st
         st = lib.msq_gemm_ex(xp, M, ctypes.byref(w), yp, ws_ptr, workspace.numel(),
                              ctypes.byref(o), _stream_handle(stream))
     _check(st, "msq_gemm")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def gemm_noalloc(x, pw: PackedWeight, out=None, stream=None):
+    """msq_gemm_noalloc: y = x . W^T with the library's own static device scratch as the
+    workspace (no device allocation inside the call; out is allocated here if None)."""
+    torch = _torch()
+    lib = load_library()
+    xd = _as_bf16_cuda(x, pw.bits.device)
+    if xd.dim() != 2 or xd.shape[1] != pw.K:
+        raise ValueError(f"x must be [M][{pw.K}]")
+    M = int(xd.shape[0])
+    if out is None:
+        out = torch.empty((M, pw.N), dtype=torch.float32, device=xd.device)
+    w = pw.descriptor()
+    _check(lib.msq_gemm_noalloc(xd.data_ptr() if M > 0 else None, M, ctypes.byref(w),
+                                out.data_ptr() if M > 0 else None, _stream_handle(stream)),
+           "msq_gemm_noalloc")
     return out
 
 

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "msq_internal.h"
@@ -208,6 +209,31 @@ msq_status group_impl(const uint16_t* const* x_bf16, int64_t M, const msq_weight
   return e == hipSuccess ? MSQ_OK : MSQ_ERR_HIP;
 }
 
+// ---- scratch for msq_gemm_noalloc ---------------------------------------------------------
+// The workspace of msq_gemm_noalloc: a file-scope device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code its
+// name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[MSQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, or nullptr.
+void* device_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,6 +318,24 @@ msq_status msq_gemm_group_ex(const uint16_t* const* x_bf16, int64_t M, const msq
   msq::Options o;
   if (!options_of(opt, o)) return MSQ_ERR_INVALID_ARG;
   return group_impl(x_bf16, M, w, y, count, workspace, workspace_bytes, o, stream);
+}
+
+msq_status msq_gemm_noalloc(const uint16_t* x_bf16, int64_t M, const msq_weight* w, float* y,
+                            hipStream_t stream) {
+  msq_status st = weight_ptrs_ok(w);
+  if (st != MSQ_OK) return st;
+  if (M < 0) return MSQ_ERR_SHAPE;
+  if (M == 0) return MSQ_OK;
+  if (M > (int64_t)0x7FFFFFFF / 2) return MSQ_ERR_SHAPE;
+  const msq::Options o{};
+  if (workspace_for(M, w->N, w->K, o) > (size_t)MSQ_NOALLOC_SCRATCH_BYTES)
+    return MSQ_ERR_BUFFER_TOO_SMALL;
+  // Every buffer the kernels need at zero is cleared by the kernels
+  // themselves each call (the M == 1 split counters by the activation-prep
+  // launch); everything else they read is written earlier in the same call.
+  void* ws = device_scratch();
+  if (!ws) return MSQ_ERR_HIP;
+  return gemm_impl(x_bf16, M, w, y, ws, (size_t)MSQ_NOALLOC_SCRATCH_BYTES, o, stream);
 }
 
 const char* msq_status_string(msq_status s) {

@@ -229,6 +229,26 @@ msq_status msq_gemm_ex(const uint16_t *x_bf16, int64_t M, const msq_weight *w,
                        float *y, void *workspace, size_t workspace_bytes,
                        const msq_options *opt, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): msq_gemm
+ * with the automatic launch choices, its workspace taken from a static
+ * device array of MSQ_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  No allocation, no memset and no
+ * host synchronization happen in the call; the caller still passes x and y.
+ * The first call on a device looks up that device's array (the device must
+ * be current, as for every call).  All calls on one GPU share its array:
+ * calls that may overlap on one GPU (different streams, or threads without
+ * ordering) race and give undefined results; order them on one stream.  The
+ * kernels clear what they need cleared each call, so consecutive calls of
+ * any shapes are independent.  Returns MSQ_ERR_BUFFER_TOO_SMALL when
+ * msq_gemm_workspace_bytes(M, N, K) for the automatic kernel exceeds the
+ * array (decode up to M = 64 fits every Llama-3-70B linear; prefill fits
+ * while M * K * 2 plus the K-split partials stay below it), MSQ_ERR_HIP if
+ * the array cannot be located, otherwise as msq_gemm. */
+#define MSQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+msq_status msq_gemm_noalloc(const uint16_t *x_bf16, int64_t M, const msq_weight *w, float *y,
+                            hipStream_t stream);
+
 /* Most matrices one msq_gemm_group call takes. */
 #define MSQ_GROUP_MAX 8
 
