@@ -56,10 +56,13 @@ __device__ __forceinline__ uint16_t bf16_rn(float v) {
 // Chunks qs .. qe - 1 (whole groups) of row m of one matrix's gather.  The
 // x row is copied into LDS with direct-to-LDS loads (when staged), and the
 // perm_col loads of kBatch passes are issued before any of them is used.
+// sf (optional): the group sums again as fp32, [group][Mpad] (the decode
+// kernel's layout: one 16-byte load gives a lane its four rows).
 __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64_t K, int64_t M,
                                            const int32_t* __restrict__ perm_col,
                                            uint16_t* __restrict__ xr, uint16_t* __restrict__ sxs,
-                                           int staged, int64_t m, int64_t qs, int64_t qe) {
+                                           float* __restrict__ sf, int64_t Mpad, int staged,
+                                           int64_t m, int64_t qs, int64_t qe) {
   constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63;
   const int64_t chunks = K / 8;
@@ -117,6 +120,7 @@ __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64
         dst[0] = t0;
         dst[plane] = t1;
         dst[2 * plane] = t2;
+        if (sf) sf[(q / 16) * Mpad + m] = part;
       }
     }
   }
@@ -127,11 +131,13 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
                                                              int64_t K, int64_t M,
                                                              const int32_t* __restrict__ perm_col,
                                                              uint16_t* __restrict__ xr,
-                                                             uint16_t* __restrict__ sxs, int staged) {
+                                                             uint16_t* __restrict__ sxs,
+                                                             float* __restrict__ sf, int64_t Mpad,
+                                                             int staged) {
   const int64_t Gp = padded_groups(K / kBlockCols);
   const int64_t per = (Gp + gridDim.y - 1) / gridDim.y * 16;
   const int64_t qs = (int64_t)blockIdx.y * per;
-  gather_row(x, K, M, perm_col, xr, sxs, staged, blockIdx.x, qs, min(qs + per, Gp * 16));
+  gather_row(x, K, M, perm_col, xr, sxs, sf, Mpad, staged, blockIdx.x, qs, min(qs + per, Gp * 16));
 }
 
 // ---- GEMM ------------------------------------------------------------------------------
@@ -614,8 +620,8 @@ __device__ __forceinline__ GemmJob pick_gemm_job(const GemmGroup& g, int b, bool
 
 __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) {
   const GemmJob q = pick_gemm_job(g, blockIdx.x, true);
-  gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, q.staged, blockIdx.x % g.M, 0,
-             padded_groups(q.w.K / kBlockCols) * 16);
+  gather_row(q.x, q.w.K, g.M, q.w.perm_col, q.xr, q.sxs, nullptr, 0, q.staged, blockIdx.x % g.M,
+             0, padded_groups(q.w.K / kBlockCols) * 16);
 }
 
 template <int CH>
@@ -702,10 +708,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K, const Options& opt) {
 
 }  // namespace
 
+// [x_r | three bf16 terms of the group sums | fp32 group sums], each part 256-byte aligned
 size_t gather_workspace_bytes(int64_t M, int64_t K) {
   const size_t xr = (size_t)M * K * 2;
   const size_t xr_al = (xr + 255) & ~(size_t)255;
-  return xr_al + 3 * (size_t)M * (size_t)padded_groups(K / kBlockCols) * 2;
+  const size_t gp = (size_t)padded_groups(K / kBlockCols);
+  const size_t terms = ((3 * (size_t)M * gp * 2) + 255) & ~(size_t)255;
+  return xr_al + terms + gp * (size_t)gather_mpad(M) * 4;
+}
+
+float* gather_sums_f32(void* ws, int64_t M, int64_t K) {
+  const size_t xr_al = (((size_t)M * K * 2) + 255) & ~(size_t)255;
+  const size_t gp = (size_t)padded_groups(K / kBlockCols);
+  const size_t terms = ((3 * (size_t)M * gp * 2) + 255) & ~(size_t)255;
+  return reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(ws) + xr_al + terms);
 }
 
 size_t gemm_group_workspace_bytes(int64_t M, const WeightView* w, int count, const Options& opt) {
@@ -781,7 +797,7 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
 }
 
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool sums_f32) {
   const int64_t K = w.K;
   uint16_t* xr = reinterpret_cast<uint16_t*>(ws);
   const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
@@ -792,8 +808,10 @@ hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, vo
   // (every slice stages the whole row), so that small M still fills the GPU
   const int64_t slices = std::max<int64_t>(
       1, std::min<int64_t>(padded_groups(K / kBlockCols) / 16, 256 / std::max<int64_t>(M, 1)));
+  float* sf = sums_f32 ? gather_sums_f32(ws, M, K) : nullptr;
   hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M, (unsigned)slices), dim3(kGatherThreads),
-                     staged ? row_bytes : 0, stream, x, K, M, w.perm_col, xr, sxs, staged);
+                     staged ? row_bytes : 0, stream, x, K, M, w.perm_col, xr, sxs, sf,
+                     (int64_t)gather_mpad(M), staged);
   return hipGetLastError();
 }
 
@@ -814,7 +832,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
                     ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
                                                ((gather_workspace_bytes(M, K) + 255) & ~(size_t)255))
                     : nullptr;
-  hipError_t e = launch_gather_x(x, M, w, workspace, stream);
+  hipError_t e = launch_gather_x(x, M, w, workspace, stream, false);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + kBR - 1) / kBR),
                   (unsigned)p.split);

@@ -276,16 +276,21 @@ constexpr int ring_depth() {
 // more loads per block).  consume(column, registers) uses a block;
 // after_issue(integral_constant<loads issued>) runs once after the first D
 // blocks are issued.
-template <int B, int D, bool kScaleZero, typename Consume, typename AfterIssue>
-__device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
-                                         Consume&& consume, AfterIssue&& after_issue) {
+// Regs: the register set of one block; issue(address, column, regs) issues
+// its loads (the address of this lane's 16 bytes of the block's first chunk);
+// kIssued: loads per issue.
+template <int B, int D, int kIssued, typename Regs, typename Issue, typename Consume,
+          typename AfterIssue>
+__device__ __forceinline__ void ring_run_t(const uint8_t* codes, const uint8_t* base, uint64_t cols,
+                                           int n, Issue&& issue, Consume&& consume,
+                                           AfterIssue&& after_issue) {
   constexpr int64_t kStride = 1024 * B;
-  BlockRegs<B> rs[D];
+  Regs rs[D];
   int cs[D];
-  const int64_t lane_off = base - cx.codes;  // this lane's offset of the run's first block
+  const int64_t lane_off = base - codes;  // this lane's offset of the run's first block
   // block bi of the run, or (live false) the stand-in address
   auto slot = [&](bool live, int bi) __attribute__((always_inline)) {
-    return cx.codes + ((lane_off + (int64_t)bi * kStride) & -(int64_t)live);
+    return codes + ((lane_off + (int64_t)bi * kStride) & -(int64_t)live);
   };
   // compiler-only barriers after the issues keep the loads where they are
   // written (the compiler would otherwise sink them toward their first use)
@@ -299,11 +304,11 @@ __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uin
     }
     int bi = __builtin_amdgcn_readfirstlane(j);
     asm("" : "+s"(bi));
-    issue_block<B, kScaleZero>(cx, slot(j < n, bi), cs[j], rs[j]);
+    issue(slot(j < n, bi), cs[j], rs[j]);
     asm volatile("" ::: "memory");
   }
   // the first run: the workgroup's start-up, while these loads fly
-  after_issue(std::integral_constant<int, D * (B + (kScaleZero ? 2 : 0))>{});
+  after_issue(std::integral_constant<int, D * kIssued>{});
   int i0 = 0;  // run index of the block in set 0
   do {
 #pragma unroll
@@ -316,11 +321,22 @@ __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uin
       }
       int bi = __builtin_amdgcn_readfirstlane(nx);
       asm("" : "+s"(bi));
-      issue_block<B, kScaleZero>(cx, slot(nx < n, bi), cs[j], rs[j]);
+      issue(slot(nx < n, bi), cs[j], rs[j]);
       asm volatile("" ::: "memory");
     }
     i0 += D;
   } while (i0 < n);
+}
+
+template <int B, int D, bool kScaleZero, typename Consume, typename AfterIssue>
+__device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
+                                         Consume&& consume, AfterIssue&& after_issue) {
+  ring_run_t<B, D, B + (kScaleZero ? 2 : 0), BlockRegs<B>>(
+      cx.codes, base, cols, n,
+      [&](const uint8_t* addr, int cl, BlockRegs<B>& br) __attribute__((always_inline)) {
+        issue_block<B, kScaleZero>(cx, addr, cl, br);
+      },
+      consume, after_issue);
 }
 
 // A run of n blocks of bitwidth B whose columns are the lowest n set bits of
@@ -452,6 +468,164 @@ __global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ x
           }
         }
   }
+}
+
+// ======================================================================================
+// 2 <= M <= 16: A operands straight from the reordered x
+// ======================================================================================
+//
+// The activation gather leaves x_r [M][K] (reordered through perm_col) and
+// the fp32 group sums [group][16] in the workspace, a few hundred KB that
+// stay in L2.  Each block's register set holds, besides its b code chunks,
+// the block column's four A fragments (x_r rows lane & 15, columns
+// 32 kt + 8 (lane >> 4) .. +7; rows past M repeat row M - 1 and their
+// outputs are never stored), the group sums of rows 4 (lane >> 4) .. +3 and
+// the scale and zero point of row `lane`, all issued together one ring
+// stage ahead.  No slice of x is staged in LDS, so a workgroup takes a
+// whole block row (or a range of 64 block columns) like the M == 1 kernel
+// and there is no start-up barrier; LDS only holds the final sum over the
+// wavefronts.
+
+template <int B>
+struct RegsX {
+  uint4 ch[B];
+  uint4 a[4];
+  float4 sx;
+  float s;
+  uint32_t z;
+};
+
+struct CtxX {
+  const uint8_t* codes;
+  const float* scale;
+  const uint8_t* zero;
+  int64_t rowbase;      // block index of the range's first column
+  const uint16_t* xa;   // this lane's A row at the range's first column
+  const float* sxa;     // this lane's four group sums at the range's first column
+};
+
+template <int B>
+__device__ __forceinline__ void issue_x(const CtxX& cx, const uint8_t* base, int cl, RegsX<B>& br) {
+  const int lane = threadIdx.x & 63;
+  cl = __builtin_amdgcn_readfirstlane(cl);
+  asm("" : "+s"(cl));
+  const int64_t blk = cx.rowbase + cl;
+#pragma unroll
+  for (int t = 0; t < B; ++t) br.ch[t] = *reinterpret_cast<const uint4*>(base + 1024 * t);
+  const uint16_t* xa = cx.xa + (int64_t)cl * kBlockCols;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) br.a[kt] = *reinterpret_cast<const uint4*>(xa + 32 * kt);
+  br.sx = *reinterpret_cast<const float4*>(cx.sxa + (int64_t)cl * 16);
+  br.s = cx.scale[blk * kBlockRows + lane];
+  br.z = cx.zero[blk * kBlockRows + lane];
+}
+
+// One block into yacc[rt] (rows 4 (lane >> 4) + i, output 16 rt + (lane & 15)):
+//   yacc += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
+template <int B>
+__device__ __forceinline__ void consume_x(const RegsX<B>& br, f32x4 (&yacc)[4]) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 A[1][4];
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) A[0][kt] = as_bf16x8(br.a[kt]);
+  f32x4 acc[1][4];
+  block_product<B, 1>(br.ch, A, acc);
+  constexpr float bias = (float)unpack_bias(B);
+  const float sx[4] = {br.sx.x, br.sx.y, br.sx.z, br.sx.w};
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int src = 16 * rt + (lane & 15);
+    const float s = __shfl(br.s, src, 64);
+    const float zz = bias + (float)__shfl((int)br.z, src, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yacc[rt][i] += s * (acc[0][rt][i] - zz * sx[i]);
+  }
+}
+
+// Ring depth of this kernel: two blocks, one for 8-bit blocks (the A
+// fragments ride along, so the register sets are larger than at M == 1; two
+// workgroups of 8 wavefronts per CU need them within 128 registers).
+template <int B>
+constexpr int ring_depth_x() { return B >= 8 ? 1 : 2; }
+
+template <int B>
+__device__ __forceinline__ void run_x(const CtxX& cx, const uint8_t* base, uint64_t cols, int n,
+                                      f32x4 (&yacc)[4]) {
+  ring_run_t<B, ring_depth_x<B>(), B + 7, RegsX<B>>(
+      cx.codes, base, cols, n,
+      [&](const uint8_t* addr, int cl, RegsX<B>& br) __attribute__((always_inline)) {
+        issue_x<B>(cx, addr, cl, br);
+      },
+      [&](int, const RegsX<B>& br) __attribute__((always_inline)) { consume_x<B>(br, yacc); },
+      [](auto) __attribute__((always_inline)) {});
+}
+
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
+                                                    const float* __restrict__ sf, int M,
+                                                    WeightView w, int split, int kmax,
+                                                    float* __restrict__ out, int direct) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = blockIdx.x / split, sp = blockIdx.x - (blockIdx.x / split) * split;
+  const int c0 = sp * kmax;
+  const int ncl = min(w.NBc, c0 + kmax) - c0;
+  const int64_t rowbase = (int64_t)r * w.NBc + c0;
+  // this wavefront's share of the range's blocks, in packed order
+  const int lc = min(lane, ncl - 1);
+  const int bl = w.bits[rowbase + lc];
+  const uint32_t ol = w.block_offset[rowbase + lc];
+  const WaveRuns wr = wave_runs<NW>(lane < ncl ? bl : 0, wave, kWeightCostM1);
+  const int ma = min(lane & 15, M - 1);
+  CtxX cx{w.codes, w.scale, w.zero, rowbase,
+          xr + (int64_t)ma * w.K + (int64_t)c0 * kBlockCols + 8 * (lane >> 4),
+          sf + (int64_t)c0 * 16 + 4 * (lane >> 4)};
+  f32x4 yacc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) yacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t off[5];
+#pragma unroll
+  for (int k = 0; k < 5; ++k)
+    off[k] = wr.n[k] > 0 ? __builtin_amdgcn_readlane(ol, __builtin_ctzll(wr.cols[k])) : 0u;
+  auto base = [&](uint32_t o) __attribute__((always_inline)) {
+    return w.codes + (int64_t)o * 1024 + 16 * lane;
+  };
+  if (wr.n[0] > 0) run_x<1>(cx, base(off[0]), wr.cols[0], wr.n[0], yacc);
+  if (wr.n[1] > 0) run_x<2>(cx, base(off[1]), wr.cols[1], wr.n[1], yacc);
+  if (wr.n[2] > 0) run_x<3>(cx, base(off[2]), wr.cols[2], wr.n[2], yacc);
+  if (wr.n[3] > 0) run_x<4>(cx, base(off[3]), wr.cols[3], wr.n[3], yacc);
+  if (wr.n[4] > 0) run_x<8>(cx, base(off[4]), wr.cols[4], wr.n[4], yacc);
+
+  // sum over the wavefronts in a fixed order and write out
+  float* red = reinterpret_cast<float*>(smem);
+  const int plane = M * kBlockRows;
+  if (wave > 0) {
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * (lane >> 4) + i;
+        if (m < M) red[(wave - 1) * plane + m * kBlockRows + 16 * rt + (lane & 15)] = yacc[rt][i];
+      }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * (lane >> 4) + i;
+      if (m >= M) continue;
+      const int n = 16 * rt + (lane & 15);
+      float v = yacc[rt][i];
+#pragma unroll
+      for (int k = 0; k < NW - 1; ++k) v += red[k * plane + m * kBlockRows + n];
+      const int64_t row = (int64_t)r * kBlockRows + n;
+      if (direct)
+        out[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
+      else
+        out[((int64_t)sp * M + m) * w.N + row] = v;
+    }
 }
 
 // ======================================================================================
@@ -659,20 +833,36 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const size_t sums_off = m1_sums_offset(kmax);
   const uint32_t zero_off = (uint32_t)m1_zero_offset(kmax);
 
-  // Gathering: the x row, straight into LDS, ahead of the first round trip
-  // (so the waits for the bit map below cover it too).
+  // Every copy into LDS goes out first, ahead of the bit map: the x row
+  // (gathering) or the reordered x slice and its k-step sums (prep), then
+  // the range's scales (16 uint4 per column) and zero points (4 per
+  // column).  Copies need no registers; loads complete in issue order, so
+  // the wait for the bit map below covers them, and the first run's code
+  // loads issued after it have no staging queued ahead of them (the
+  // start-up barrier then waits for nothing that is still in flight).
   const int nperm = ncl * 32;  // uint4s of perm_col in the range (c0 == 0)
   const size_t xrow_off = m1_xrow_offset(kmax);
-  if constexpr (kGather) {
+  const size_t s_off = m1_scale_offset(kmax);
+  const size_t z_off = s_off + 256 * (size_t)ncl;  // the zero points follow the range's scales
+  auto stage16 = [&](const void* g, size_t lds_off, int n, auto Units) __attribute__((always_inline)) {
+    constexpr int kU = decltype(Units)::value;
 #pragma unroll
-    for (int u = 0; u < kUnits; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int idx = t + u * kThreads;
-      if (idx < ncl * 16)
-        lds_copy16(reinterpret_cast<const uint4*>(x) + idx, (uint32_t)xrow_off + 16 * (idx - lane));
+      if (idx < n)  // lane i of the wavefront lands 16 i bytes past the wavefront's base
+        lds_copy16(reinterpret_cast<const uint4*>(g) + idx, (uint32_t)lds_off + 16 * (idx - lane));
     }
-    asm volatile("" ::: "memory");
+  };
+  if constexpr (kGather) {
+    stage16(x, xrow_off, ncl * 16, std::integral_constant<int, kUnits>{});
+  } else {
+    stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
+    stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
   }
-  // First round trip: bit map and offsets (lane = column).
+  stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
+  stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
+  asm volatile("" ::: "memory");
+  // Then the bit map and offsets (lane = column).
   const int lc = min(lane, ncl - 1);
   const int blr = w.bits[rowbase + lc];
   const uint32_t ol = w.block_offset[rowbase + lc];
@@ -693,25 +883,16 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   for (int k = 0; k < 5; ++k)
     off[k] = wr.n[k] > 0 ? __builtin_amdgcn_readlane(ol, __builtin_ctzll(wr.cols[k])) : 0u;
 
-  // Then, copied straight into LDS (no registers; the start-up barrier waits
-  // for them), the range's slices of the reordered x, corrections, group
-  // sums, scales (16 uint4 per column) and zero points (4 per column),
-  // issued just before the first run's code loads so that they travel with
-  // them.
-  const size_t s_off = m1_scale_offset(kmax);
-  const size_t z_off = s_off + 256 * (size_t)ncl;  // the zero points follow the range's scales
-  // the bit map and offsets have landed (the plan above used them): an
-  // explicit wait here tells the compiler so, and it then has no reason
-  // to wait for the copies below when it reuses those registers (gathering:
-  // all but the perm_col loads and the x row copies issued after them)
+  // Every load so far has landed (an explicit vmcnt(0): the compiler does
+  // not see the copies, and with this wait it has no reason to wait for
+  // anything when it reuses their registers).
   // Gathering: the perm_col entries, clamped into [0, K) and packed to 16
   // bits (K <= 128 kMaxCols <= 65536), are parked in the x slice area, in
   // the 8 bytes that the same thread later fills with the four reordered
   // values, so that they hold no registers while the ring's loads are in
-  // flight.  This waits for their loads, issued with the bit map's (an
-  // explicit vmcnt(0), for the reason above: every load so far has landed).
+  // flight.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   if constexpr (kGather) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
     const int kk = (int)w.K - 1;
     static_assert(kBlockCols * kMaxCols <= 65536, "16-bit column indices");
 #pragma unroll
@@ -721,25 +902,7 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
                      (uint32_t)clampi((int)pc[u].z, kk) | ((uint32_t)clampi((int)pc[u].w, kk) << 16)};
       if (i < nperm) *reinterpret_cast<uint2*>(smem + 8 * (size_t)i) = pk;
     }
-  } else {
-    __builtin_amdgcn_s_waitcnt(0x0F70);
   }
-  auto stage16 = [&](const void* g, size_t lds_off, int n, auto Units) __attribute__((always_inline)) {
-    constexpr int kU = decltype(Units)::value;
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int idx = t + u * kThreads;
-      if (idx < n)  // lane i of the wavefront lands 16 i bytes past the wavefront's base
-        lds_copy16(reinterpret_cast<const uint4*>(g) + idx, (uint32_t)lds_off + 16 * (idx - lane));
-    }
-  };
-  if constexpr (!kGather) {
-    stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
-    stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
-  }
-  stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
-  stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
-  asm volatile("" ::: "memory");
 
   Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
          (uint32_t)sums_off, 0u, 0u};
@@ -1069,7 +1232,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   p.nw = M > 16 ? 4 : 8;
   if (M == 1) p.nw = (opt.gemv_waves == 4 || opt.gemv_waves == 16) ? opt.gemv_waves : 8;
   int kr_max = kMaxCols;
-  if (M > 1) {
+  const bool small = M >= 2 && M <= 16;  // k_gemv16: no x slice in LDS
+  if (small) p.nw = 8;
+  if (M > 1 && !small) {
     // LDS per block column: x slice (2 bytes x 128 per row) + one group sum per row
     const size_t per_col = (size_t)M * (kBlockCols * 2 + 4);
     kr_max = (int)((kLdsBudget - 16 * (size_t)M) / per_col);
@@ -1078,7 +1243,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   }
   int split = opt.gemv_split;
   if (split <= 0) {
-    if (M == 1) {
+    if (M <= 16) {
       // about one workgroup of 8 wavefronts per CU: more K splits add start-ups
       // and partials faster than they add memory parallelism
       split = 256 / rows;
@@ -1105,6 +1270,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   if (M == 1) {
     p.xs_stride = kr * kBlockCols;
     x_bytes = m1_lds_bytes(kr);
+  } else if (small) {
+    p.xs_stride = 0;
+    x_bytes = 0;
   } else {
     p.xs_stride = kr * kBlockCols + 8;  // +16 bytes per row against LDS bank conflicts
     x_bytes = (size_t)M * p.xs_stride * 2 + (size_t)M * kr * 4;
@@ -1203,14 +1371,20 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
     if (p.nw == 16) return launch_m1<16>(g, x, gather, w, y, p, stream);
     return launch_m1<8>(g, x, gather, w, y, p, stream);
   } else {
-    // x reordered once per call, then staged slice by slice
-    e = launch_gather_x(x, M, w, g.gather, stream);
+    // x reordered once per call (M <= 16: with fp32 group sums for k_gemv16,
+    // which reads its A operands from it directly; otherwise staged slice by
+    // slice into LDS)
+    const bool small = M <= 16;
+    e = launch_gather_x(x, M, w, g.gather, stream, small);
     if (e != hipSuccess) return e;
     const uint16_t* xr = reinterpret_cast<const uint16_t*>(g.gather);
     const uint16_t* sxs = reinterpret_cast<const uint16_t*>(
         reinterpret_cast<const uint8_t*>(g.gather) + align256((size_t)M * w.K * 2));
-    if (p.nw == 8) {
-      e = launch_cfg<8, 1>(xr, sxs, (int)M, w, dst, p, direct, stream);
+    if (small) {
+      const float* sf = gather_sums_f32(g.gather, M, w.K);
+      hipLaunchKernelGGL(k_gemv16<8>, dim3((unsigned)(w.NBr * p.split)), dim3(512), p.lds_bytes,
+                         stream, xr, sf, (int)M, w, p.split, p.kr, dst, direct);
+      e = hipGetLastError();
     } else {
       switch (p.mt) {
         case 2: e = launch_cfg<4, 2>(xr, sxs, (int)M, w, dst, p, direct, stream); break;

@@ -83,12 +83,17 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
 // ---- activation gather for M > 1 (msq_gemm.hip): x_r[m][j] = x[m][perm_col[j]]
 // and the group sums of x_r split into three bf16 terms S0 + S1 + S2 (exact
 // fp32), [3][M][Gp] with Gp = the group count rounded up to 32.  It writes
-// gather_workspace_bytes(M, K) bytes at ws: x_r first, the sums 256-byte
-// aligned after it.
+// into gather_workspace_bytes(M, K) bytes at ws: x_r first, the sums 256-byte
+// aligned after it, then (on request) the fp32 sums.
 __host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31) & ~(int64_t)31; }
+// Rows of the fp32 group sums: M rounded up to 16.
+__host__ __device__ constexpr int64_t gather_mpad(int64_t M) { return (M + 15) & ~(int64_t)15; }
 size_t gather_workspace_bytes(int64_t M, int64_t K);
+// sums_f32: also write the group sums in fp32, [padded groups][gather_mpad(M)]
+// (rows past M left as they are), at gather_sums_f32(ws, M, K).
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
-                           hipStream_t stream);
+                           hipStream_t stream, bool sums_f32);
+float* gather_sums_f32(void* ws, int64_t M, int64_t K);
 
 // ---- K-split reduction (msq_gemv.hip): y[m][perm_row[n]] = sum over splits,
 // in split order, of part[sp][m][n].

@@ -219,8 +219,9 @@ def test_group_workspace_sizes(lib):
     prep = sum(2 * w.K + 84 * (w.K // 128) for w in ws_list)
     g1 = lib.msq_gemm_group_workspace_bytes(1, arr, 3)
     assert prep <= g1 <= sum(singles) + 3 * 256
-    # M in 2 .. 64: the matrices run one after the other, so the largest one suffices
-    mid = [lib.msq_gemm_workspace_bytes(16, w.N, w.K) for w in ws_list]
+    # M in 2 .. 16: the matrices run one after the other with the automatic kernel
+    # choice, so the largest of those workspaces suffices
+    mid = [lib.msq_gemm_workspace_bytes_ex(16, w.N, w.K, _opt(0)) for w in ws_list]
     assert lib.msq_gemm_group_workspace_bytes(16, arr, 3) == max(mid)
     # prefill: one launch for all, each matrix with its own gathered activation
     big = [lib.msq_gemm_workspace_bytes(2048, w.N, w.K) for w in ws_list]
