@@ -47,9 +47,10 @@ Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 
 Auxiliary modes for rocprofv3 runs (bench.py reads back the HBM traffic of
 the decode kernel):
-  --only-decode NAME --calls C  : pack one linear of the layer, clone it to
-                                  >= 1 GiB of copies, run C decode calls
-                                  (M = 1) rotating over the copies and exit;
+  --only-decode NAME --calls C [--m M] : pack one linear of the layer, clone
+                                  it to >= 1 GiB of copies, run C decode calls
+                                  (M = 1, or M <= 64) rotating over the copies
+                                  and exit;
   --only-configs                : only the per-matrix config lines (for a
                                   kernel trace of the small-M decodes);
   --only-prefill NAME --calls C : the same with prefill calls (M = 2048);
@@ -517,6 +518,7 @@ def main() -> int:
     ap.add_argument("--only-prefill", default=None, metavar="NAME")
     ap.add_argument("--only-configs", action="store_true")
     ap.add_argument("--calls", type=int, default=20)
+    ap.add_argument("--m", type=int, default=1, help="M of --only-decode (default 1)")
     ap.add_argument("--copy-bytes", type=int, default=0)
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -557,9 +559,9 @@ def main() -> int:
         name = args.only_prefill if args.only_prefill is not None else args.only_decode
         mi = synth.matrix_inputs(WORKLOAD, names.index(name))
         pw = msq.quantize_pack(bf16_dev(torch, np, mi.W, dev), mi.bits, mi.perm_row, mi.perm_col)
-        M = PREFILL_M if args.only_prefill is not None else 1
+        M = PREFILL_M if args.only_prefill is not None else args.m
         # decode: rotate >= 1 GiB of copies, as the roofline leg does
-        R = 1 if M > 1 else max(2, int(np.ceil((1 << 30) / pw.packed_bytes)))
+        R = 1 if M > 64 else max(2, int(np.ceil((1 << 30) / pw.packed_bytes)))
         cps = [pw] + [pw.clone() for _ in range(R - 1)]
         x = bf16_dev(torch, np, mi.x(M), dev)
         y = torch.empty((M, pw.N), dtype=torch.float32, device=dev)
@@ -569,8 +571,8 @@ def main() -> int:
             msq.gemm(x, cps[k % R], out=y, workspace=ws)
         torch.cuda.synchronize()
         log(f"{args.calls} calls (M = {M}) on {name} over {R} copies: "
-            f"{decode_bytes(pw, M) if M == 1 else prefill_flops(pw, M)} algorithmic "
-            f"{'bytes' if M == 1 else 'flops'} per call")
+            f"{decode_bytes(pw, M) if M <= 64 else prefill_flops(pw, M)} algorithmic "
+            f"{'bytes' if M <= 64 else 'flops'} per call")
         return 0
 
     clocks_before = gpu_clocks()

@@ -155,10 +155,10 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
 //     loads its block's next scales;
 //   - row tile by row tile, the wavefront reads the code chunks that tile
 //     needs, unpacks its 4 B fragments to exact bf16 (128 + q; 3-bit: both
-//     planes merged into one operand; 8-bit: low 7 bits and top bit, two
-//     operands, bias 384), issues 16 v_mfma_f32_16x16x32_bf16 (32 for 8
-//     bits) into a group accumulator and folds it, acc += s_n * acc_g, while
-//     the next row tile's products run;
+//     planes merged into one operand; 8-bit: q itself, converted through
+//     fp32), issues 16 v_mfma_f32_16x16x32_bf16 into a group accumulator
+//     and folds it, acc += s_n * acc_g, while the next row tile's products
+//     run;
 //   - wait for its own copies, one barrier.
 // acc_g carries the unpack bias and the zero point: acc_g = sum_k (bias +
 // q_k) x_k = sum_k (q_k - z) x_k + (bias + z) S_c with S_c the group's sum
@@ -179,7 +179,9 @@ constexpr int kWaves = 2 * kBR;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTabG = 512;  // groups whose bit map and offsets are staged in LDS
 
-__host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 384.f : 128.f; }
+// Bias of the unpacked operands: 128 + q for b <= 4 (3 bits: both planes in
+// one operand), q itself for b = 8.
+__host__ __device__ constexpr float gemm_bias(int b) { return b == 8 ? 0.f : 128.f; }
 
 // One stage of the pipeline in LDS.
 struct Stage {
@@ -194,14 +196,16 @@ __host__ __device__ constexpr int lo_chunk() {
 }
 
 // Unpacked B operand of fragment F from its chunk c (3 bits: low plane chunk
-// c and high plane chunk c2, one operand; 8 bits: the low 7 bits).
+// c and high plane chunk c2, one operand; 8 bits: the codes themselves,
+// converted exactly through fp32, since every q <= 255 is a bf16 integer: one
+// matrix instruction per fragment).
 template <int B, int F>
 __device__ __forceinline__ bf16x8 b_lo(const uint4& c, const uint4& c2) {
   if constexpr (B == 1) return unpack_magic<1, F>(c);
   else if constexpr (B == 2) return unpack_magic<2, 2 * (F % 8)>(c);
   else if constexpr (B == 3) return unpack3_magic<F>(c, c2);
   else if constexpr (B == 4) return unpack_magic<4, 4 * (F % 4)>(c);
-  else return exp_lo<8, F>(c);
+  else return unpack_u8<F % 2>(c);
 }
 
 // One group of this wavefront's B-bit block (block row q of the workgroup,
@@ -261,11 +265,6 @@ __device__ __forceinline__ void group_mfma(const Stage& st, int q, const bf16x8 
       const bf16x8 bop = b_lo<B, F>(c, c2);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], bop, kt == 0 ? zero : g[mt]);
-      if constexpr (B == 8) {
-        const bf16x8 hop = exp_hi<8, F>(c);
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) g[mt] = mfma_bf16(A[kt][mt], hop, g[mt]);
-      }
     };
     kstep(std::integral_constant<int, 0>{});
     kstep(std::integral_constant<int, 1>{});
