@@ -53,6 +53,8 @@ the decode kernel):
                                   and exit;
   --only-configs                : only the per-matrix config lines (for a
                                   kernel trace of the small-M decodes);
+  --only-pack NAME --calls C    : quantize-pack one linear of the layer C
+                                  times (W resident) and exit;
   --only-prefill NAME --calls C : the same with prefill calls (M = 2048);
   --copy-bytes B                : copy B bytes device to device a few times
                                   (the calibration of the byte counters).
@@ -517,6 +519,7 @@ def main() -> int:
     ap.add_argument("--only-decode", default=None, metavar="NAME")
     ap.add_argument("--only-prefill", default=None, metavar="NAME")
     ap.add_argument("--only-configs", action="store_true")
+    ap.add_argument("--only-pack", default=None, metavar="NAME")
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, help="M of --only-decode (default 1)")
     ap.add_argument("--copy-bytes", type=int, default=0)
@@ -550,6 +553,16 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.copy_bytes} bytes 5 times")
+        return 0
+    if args.only_pack is not None:
+        mi = synth.matrix_inputs(WORKLOAD, names.index(args.only_pack))
+        Wd = bf16_dev(torch, np, mi.W, dev)
+        pw = msq.allocate_packed(mi.N, mi.K, mi.bits, mi.perm_row, mi.perm_col, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.calls):
+            msq.pack_into(Wd, pw)
+        torch.cuda.synchronize()
+        log(f"{args.calls} packs of {args.only_pack}: {msq.pack_bytes(pw)} bytes moved per pack")
         return 0
     if args.only_configs:
         recs = config_legs(msq, synth, torch, np, dev, log, only_decode=True)

@@ -48,13 +48,43 @@ constexpr int kScanPer = 16;  // consecutive blocks per thread per pass
 constexpr int kSegs = 6;
 __constant__ int kSegBits[kSegs] = {1, 2, 3, 4, 8, 16};
 
+// Number of zero bytes of x (exact: no borrow between bytes).
+__device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
+  uint32_t t = (x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+  t = ~(t | x | 0x7F7F7F7Fu);
+  return (uint32_t)__popc(t);
+}
+
+// Bit map bytes i0 .. i0 + 15 as four little-endian words; bytes past nblk
+// read as 0 (no block).
+__device__ __forceinline__ void load16_bits(const uint8_t* __restrict__ bits, int64_t nblk,
+                                            int64_t i0, uint32_t (&w)[4]) {
+  if (i0 + kScanPer <= nblk && (reinterpret_cast<uintptr_t>(bits + i0) & 15) == 0) {
+    const uint4 v = *reinterpret_cast<const uint4*>(bits + i0);
+    w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    return;
+  }
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t x = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t i = i0 + 4 * d + e;
+      const uint32_t byte = bits[i < nblk ? i : nblk - 1];
+      x |= (i < nblk ? byte : 0u) << (8 * e);
+    }
+    w[d] = x;
+  }
+}
+
 // One workgroup, two sweeps over the bit map in passes of kScanThreads *
 // kScanPer blocks (thread t takes 16 consecutive blocks of a pass, so the
 // loads and stores of a wavefront are contiguous).  Sweep 1 counts the
-// blocks of every bitwidth: segment k starts at the sum of bits over the
-// segments before it.  Sweep 2 scans the per-thread counts of each pass
-// (wavefront prefix sums, then across wavefronts) on top of the counts of
-// the passes before, and assigns offset = segment base + b * rank.
+// blocks of every bitwidth (zero bytes of the bits XOR the bitwidth in every
+// byte): segment k starts at the sum of bits over the segments before it.
+// Sweep 2 scans the per-thread counts of each pass (wavefront prefix sums,
+// then across wavefronts) on top of the counts of the passes before, and
+// assigns offset = segment base + b * rank, branch-free.
 __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* __restrict__ bits,
                                                                 int64_t nblk,
                                                                 uint32_t* __restrict__ off) {
@@ -64,23 +94,24 @@ __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* _
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t pass_blocks = (int64_t)kScanThreads * kScanPer;
+  constexpr uint32_t kB[kSegs] = {1, 2, 3, 4, 8, 16};
 
-  auto load16 = [&](int64_t i0, int (&seg)[kScanPer]) __attribute__((always_inline)) {
-    uint8_t v[kScanPer];
+  auto count16 = [&](const uint32_t (&w)[4], uint32_t (&cnt)[kSegs]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < kScanPer; ++e) v[e] = i0 + e < nblk ? bits[i0 + e] : 0;
-#pragma unroll
-    for (int e = 0; e < kScanPer; ++e) seg[e] = segment_of(v[e]);
+    for (int k = 0; k < kSegs; ++k) {
+      const uint32_t rep = kB[k] * 0x01010101u;
+      cnt[k] = zero_bytes(w[0] ^ rep) + zero_bytes(w[1] ^ rep) + zero_bytes(w[2] ^ rep) +
+               zero_bytes(w[3] ^ rep);
+    }
   };
   // sweep 1: totals per segment
   uint32_t tot[kSegs] = {0, 0, 0, 0, 0, 0};
   for (int64_t p0 = 0; p0 < nblk; p0 += pass_blocks) {
-    int seg[kScanPer];
-    load16(p0 + (int64_t)tid * kScanPer, seg);
+    uint32_t w[4], cnt[kSegs];
+    load16_bits(bits, nblk, p0 + (int64_t)tid * kScanPer, w);
+    count16(w, cnt);
 #pragma unroll
-    for (int e = 0; e < kScanPer; ++e)
-#pragma unroll
-      for (int k = 0; k < kSegs; ++k) tot[k] += seg[e] == k ? 1u : 0u;
+    for (int k = 0; k < kSegs; ++k) tot[k] += cnt[k];
   }
 #pragma unroll
   for (int k = 0; k < kSegs; ++k) {
@@ -97,23 +128,19 @@ __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* _
       for (int w = 0; w < kScanThreads / 64; ++w) total += wave_tot[k][w];
       seg_base[k] = acc;
       seg_run[k] = 0;
-      acc += (uint32_t)kSegBits[k] * total;
+      acc += kB[k] * total;
     }
   }
   __syncthreads();
   // sweep 2: ranks and offsets
   for (int64_t p0 = 0; p0 < nblk; p0 += pass_blocks) {
     const int64_t i0 = p0 + (int64_t)tid * kScanPer;
-    int seg[kScanPer];
-    load16(i0, seg);
-    uint32_t cnt[kSegs], incl[kSegs];
+    uint32_t w[4], cnt[kSegs], incl[kSegs];
+    load16_bits(bits, nblk, i0, w);
+    count16(w, cnt);
 #pragma unroll
     for (int k = 0; k < kSegs; ++k) {
-      uint32_t c = 0;
-#pragma unroll
-      for (int e = 0; e < kScanPer; ++e) c += seg[e] == k ? 1u : 0u;
-      cnt[k] = c;
-      uint32_t v = c;
+      uint32_t v = cnt[k];
 #pragma unroll
       for (int d = 1; d < 64; d <<= 1) {
         const uint32_t u = __shfl_up(v, d, 64);
@@ -125,27 +152,41 @@ __global__ __launch_bounds__(kScanThreads) void k_block_offsets(const uint8_t* _
     __syncthreads();
     if (tid < kSegs) {  // exclusive prefixes over the wavefronts, on top of the earlier passes
       uint32_t run = seg_run[tid];
-      for (int w = 0; w < kScanThreads / 64; ++w) {
-        const uint32_t t = wave_tot[tid][w];
-        wave_tot[tid][w] = run;
+      for (int wv = 0; wv < kScanThreads / 64; ++wv) {
+        const uint32_t t = wave_tot[tid][wv];
+        wave_tot[tid][wv] = run;
         run += t;
       }
       seg_run[tid] = run;
     }
     __syncthreads();
-    uint32_t rank[kSegs];
+    uint32_t rank[kSegs], base[kSegs];
 #pragma unroll
-    for (int k = 0; k < kSegs; ++k) rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
+    for (int k = 0; k < kSegs; ++k) {
+      rank[k] = wave_tot[k][wave] + incl[k] - cnt[k];
+      base[k] = seg_base[k];
+    }
+    uint32_t o[kScanPer];
 #pragma unroll
     for (int e = 0; e < kScanPer; ++e) {
-      uint32_t o = kNoBlock;
+      const uint32_t byte = (w[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+      uint32_t v = kNoBlock;
 #pragma unroll
-      for (int k = 0; k < kSegs; ++k)
-        if (seg[e] == k) {
-          o = seg_base[k] + (uint32_t)kSegBits[k] * rank[k];
-          rank[k]++;
-        }
-      if (i0 + e < nblk) off[i0 + e] = o;
+      for (int k = 0; k < kSegs; ++k) {
+        const bool m = byte == kB[k];
+        v = m ? base[k] + kB[k] * rank[k] : v;
+        rank[k] += m ? 1u : 0u;
+      }
+      o[e] = v;
+    }
+    if (i0 + kScanPer <= nblk && (reinterpret_cast<uintptr_t>(off + i0) & 15) == 0) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        reinterpret_cast<uint4*>(off + i0)[d] = uint4{o[4 * d], o[4 * d + 1], o[4 * d + 2], o[4 * d + 3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < kScanPer; ++e)
+        if (i0 + e < nblk) off[i0 + e] = o[e];
     }
     __syncthreads();  // wave_tot is rewritten by the next pass
   }
