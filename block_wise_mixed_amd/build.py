@@ -11,6 +11,7 @@ import os
 import shutil
 import subprocess
 import sys
+from typing import Optional
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -63,6 +64,42 @@ def _link(cc: str, objs, out: str, extra=()) -> None:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, out)
+
+
+# Host-only build with AddressSanitizer and UndefinedBehaviorSanitizer on the
+# host pass: no device code is generated, so the library serves only the
+# host-side ABI (plan, argument checks, workspace sizes, status strings) on a
+# machine without a GPU.  The sanitizer runtime is not linked in: the process
+# that loads the library preloads clang's shared ASan runtime, which also
+# carries the UBSan handlers.
+SANITIZE_FLAGS = [
+    "-O1", "-g", "-fno-omit-frame-pointer",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+]
+
+
+def asan_runtime() -> Optional[str]:
+    """Path of clang's shared ASan runtime next to hipcc's clang, or None."""
+    import glob
+    hits = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    return hits[-1] if hits else None
+
+
+def build_host_sanitized(out: str, verbose: bool = False) -> str:
+    """Build the host side of libmsq.so with ASan + UBSan into `out`."""
+    from concurrent.futures import ThreadPoolExecutor
+    cc = hipcc()
+    objdir = out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, os.path.splitext(src)[0] + ".o") for src in SOURCES]
+    jobs = max(1, min(len(SOURCES), (os.cpu_count() or 1) // 2))
+    with ThreadPoolExecutor(jobs) as ex:
+        list(ex.map(lambda so: _compile(cc, so[0], so[1], extra=SANITIZE_FLAGS, verbose=verbose),
+                    zip(SOURCES, objs)))
+    _link(cc, objs, out)
+    return out
 
 
 def build(verbose: bool = False) -> str:

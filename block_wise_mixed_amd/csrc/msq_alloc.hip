@@ -166,16 +166,17 @@ constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct AllocLayout {
   size_t key_in, key_out, val_in, val_out, sorted_cost, scan, lev, status, bad, temp, temp_bytes,
       total;
+  bool ok;  // false when hipCUB could not size its temporary storage
 };
 
 AllocLayout alloc_layout(int64_t n) {
   AllocLayout L{};
   size_t sort_temp = 0, scan_temp = 0;
-  hipcub::DeviceRadixSort::SortPairsDescending(nullptr, sort_temp, (const uint32_t*)nullptr,
-                                               (uint32_t*)nullptr, (const int32_t*)nullptr,
-                                               (int32_t*)nullptr, (int)n);
-  hipcub::DeviceScan::InclusiveSum(nullptr, scan_temp, (const int32_t*)nullptr, (int32_t*)nullptr,
-                                   (int)n);
+  L.ok = hipcub::DeviceRadixSort::SortPairsDescending(nullptr, sort_temp, (const uint32_t*)nullptr,
+                                                      (uint32_t*)nullptr, (const int32_t*)nullptr,
+                                                      (int32_t*)nullptr, (int)n) == hipSuccess &&
+         hipcub::DeviceScan::InclusiveSum(nullptr, scan_temp, (const int32_t*)nullptr,
+                                          (int32_t*)nullptr, (int)n) == hipSuccess;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -204,7 +205,8 @@ using namespace msq;
 
 extern "C" size_t msq_alloc_workspace_bytes(int64_t n_blocks) {
   if (n_blocks <= 0 || n_blocks > MSQ_ALLOC_MAX_BLOCKS) return 0;
-  return alloc_layout(n_blocks).total;
+  const AllocLayout L = alloc_layout(n_blocks);
+  return L.ok ? L.total : 0;
 }
 
 extern "C" msq_status msq_allocate_bits(const float* utility, int64_t n_blocks, int64_t budget_bits,
@@ -215,6 +217,7 @@ extern "C" msq_status msq_allocate_bits(const float* utility, int64_t n_blocks, 
     return MSQ_ERR_INVALID_ARG;
   if (n_blocks <= 0 || n_blocks > MSQ_ALLOC_MAX_BLOCKS || budget_bits < 0) return MSQ_ERR_SHAPE;
   const AllocLayout L = alloc_layout(n_blocks);
+  if (!L.ok) return MSQ_ERR_HIP;
   if (workspace_bytes < L.total) return MSQ_ERR_BUFFER_TOO_SMALL;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   auto at = [&](size_t off) { return ws + off; };

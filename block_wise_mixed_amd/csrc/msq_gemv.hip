@@ -775,10 +775,6 @@ __device__ __forceinline__ void lds_copy16(const void* g, uint32_t off) {
   const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(off));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m) : "memory", "m0");
 }
-__device__ __forceinline__ void lds_copy4(const void* g, uint32_t off) {
-  const uint32_t m = __builtin_amdgcn_readfirstlane(lds_addr(off));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(m) : "memory", "m0");
-}
 #pragma clang diagnostic pop
 
 // LDS layout of k_gemv_m1 for ranges of ncl <= kmax block columns (38 KB at

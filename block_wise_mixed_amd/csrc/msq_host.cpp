@@ -338,7 +338,7 @@ msq_status msq_gemm_noalloc(const uint16_t* x_bf16, int64_t M, const msq_weight*
   return gemm_impl(x_bf16, M, w, y, ws, (size_t)MSQ_NOALLOC_SCRATCH_BYTES, o, stream);
 }
 
-const char* msq_status_string(msq_status s) {
+const char* msq_status_string(int s) {
   switch (s) {
     case MSQ_OK: return "success";
     case MSQ_ERR_INVALID_ARG: return "invalid argument (null, misaligned pointer or bad enum)";

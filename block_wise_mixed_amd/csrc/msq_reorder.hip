@@ -118,6 +118,7 @@ struct ReorderPlan {
   int slices;
   int64_t rows_per_slice;
   size_t row_sum, col_sum, col_part, key_in, key_out, idx_in, temp, temp_bytes, total;
+  bool ok;  // false when hipCUB could not size its temporary storage
 };
 
 ReorderPlan reorder_plan(int64_t N, int64_t K) {
@@ -127,9 +128,9 @@ ReorderPlan reorder_plan(int64_t N, int64_t K) {
   p.slices = (int)((N + p.rows_per_slice - 1) / p.rows_per_slice);
   const int64_t n = std::max(N, K);
   size_t sort_temp = 0;
-  hipcub::DeviceRadixSort::SortPairsDescending(nullptr, sort_temp, (const uint32_t*)nullptr,
-                                               (uint32_t*)nullptr, (const int32_t*)nullptr,
-                                               (int32_t*)nullptr, (int)n);
+  p.ok = hipcub::DeviceRadixSort::SortPairsDescending(nullptr, sort_temp, (const uint32_t*)nullptr,
+                                                      (uint32_t*)nullptr, (const int32_t*)nullptr,
+                                                      (int32_t*)nullptr, (int)n) == hipSuccess;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     const size_t at = o;
@@ -160,7 +161,8 @@ using namespace msq;
 
 extern "C" size_t msq_reorder_workspace_bytes(int64_t N, int64_t K) {
   if (!reorder_shape_ok(N, K)) return 0;
-  return reorder_plan(N, K).total;
+  const ReorderPlan p = reorder_plan(N, K);
+  return p.ok ? p.total : 0;
 }
 
 extern "C" msq_status msq_reorder_channels(const float* saliency, int64_t N, int64_t K,
@@ -173,6 +175,7 @@ extern "C" msq_status msq_reorder_channels(const float* saliency, int64_t N, int
     return MSQ_ERR_INVALID_ARG;
   if (!reorder_shape_ok(N, K)) return MSQ_ERR_SHAPE;
   const ReorderPlan p = reorder_plan(N, K);
+  if (!p.ok) return MSQ_ERR_HIP;
   if (workspace_bytes < p.total) return MSQ_ERR_BUFFER_TOO_SMALL;
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
   float* row_sum = reinterpret_cast<float*>(ws + p.row_sum);

@@ -318,6 +318,8 @@ msq_status msq_gemm_group_ex(const uint16_t *const *x_bf16, int64_t M,
  *   utility), MSQ_ERR_SHAPE (n_blocks outside [1, MSQ_ALLOC_MAX_BLOCKS] or a
  *   negative budget), MSQ_ERR_BUFFER_TOO_SMALL, MSQ_ERR_HIP. */
 #define MSQ_ALLOC_MAX_BLOCKS (1 << 28)
+/* Bytes of workspace for n_blocks; 0 for n_blocks outside [1,
+ * MSQ_ALLOC_MAX_BLOCKS] or when hipCUB cannot size its sort and scan storage. */
 size_t msq_alloc_workspace_bytes(int64_t n_blocks);
 msq_status msq_allocate_bits(const float *utility, int64_t n_blocks, int64_t budget_bits,
                              uint8_t *bits, void *workspace, size_t workspace_bytes,
@@ -345,13 +347,17 @@ msq_status msq_allocate_bits(const float *utility, int64_t n_blocks, int64_t bud
  *   MSQ_ERR_BUFFER_TOO_SMALL, MSQ_ERR_HIP. */
 #define MSQ_REORDER_MAX_N (1 << 20)
 #define MSQ_REORDER_MAX_K 32768
+/* Bytes of workspace for an N x K map; 0 for a refused shape or when hipCUB
+ * cannot size its sort storage. */
 size_t msq_reorder_workspace_bytes(int64_t N, int64_t K);
 msq_status msq_reorder_channels(const float *saliency, int64_t N, int64_t K, int reorder_rows,
                                 int32_t *perm_row, int32_t *perm_col, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
-/* Static English text for a status code; never NULL. */
-const char *msq_status_string(msq_status status);
+/* Static English text for a status code; never NULL.  Takes an int so that
+ * any value a caller holds, including one outside the enum, is defined input
+ * ("unknown status"). */
+const char *msq_status_string(int status);
 
 /* MSQ_FORMAT_VERSION of the library that was loaded. */
 int msq_format_version(void);
