@@ -69,6 +69,19 @@ __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64
   const int64_t Gp = padded_groups(K / kBlockCols);
   const uint16_t* xrow = x + m * K;
   uint16_t* srow = reinterpret_cast<uint16_t*>(smem);
+  // perm_col entries of kBatch passes (clamped into the row's chunks)
+  int4 pa[kBatch], pb[kBatch];
+  auto load_perm = [&](int64_t q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t q = min(q0 + u * kGatherThreads + threadIdx.x, chunks - 1);
+      const int4* pc = reinterpret_cast<const int4*>(perm_col + 8 * q);
+      pa[u] = pc[0];
+      pb[u] = pc[1];
+    }
+  };
+  // the first passes' perm_col loads fly together with the row's copies
+  load_perm(qs);
   if (staged) {
     const uint4* src = reinterpret_cast<const uint4*>(xrow);
     for (int64_t i = threadIdx.x; i < chunks; i += kGatherThreads)  // lane l lands at base + 16 l
@@ -80,14 +93,7 @@ __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64
   const int kk = (int)K - 1;
   const int64_t plane = M * Gp;
   for (int64_t q0 = qs; q0 < qe; q0 += kBatch * kGatherThreads) {
-    int4 pa[kBatch], pb[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int64_t q = min(q0 + u * kGatherThreads + threadIdx.x, chunks - 1);
-      const int4* pc = reinterpret_cast<const int4*>(perm_col + 8 * q);
-      pa[u] = pc[0];
-      pb[u] = pc[1];
-    }
+    if (q0 != qs) load_perm(q0);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int64_t q = q0 + u * kGatherThreads + threadIdx.x;
@@ -342,6 +348,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   const int64_t m0 = (int64_t)mtile * kBM;
   const int rb = ntile * kBR;  // first block row of the workgroup
   const int r = rb + wn;            // this wavefront's block row
+  // a wavefront whose 64 rows all lie past M (the upper half of the last row
+  // tile when M mod 128 is in 1 .. 64, e.g. M <= 64) skips its products and
+  // its share of the correction; it still copies and meets every barrier
+  const bool live = m0 + 64 * wm < M;
   const int64_t K = w.K;
   const int G = w.NBc;
   const int tabG = min(g1 - g0, kTabG);
@@ -452,13 +462,13 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   auto group = [&](const Stage& st, const Stage& nx, int c) __attribute__((always_inline)) {
     uint32_t unused_off;
     bf16x8 A[4][4];
-    if (block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
+    if (live && block_at(wn, c, unused_off) != 0) read_a(st, apk, A);
     lds_barrier();
     if (c + 1 < g1) {
       copy_group(nx, c + 1);
       load_scales(w, r, c + 1, nxt);
     }
-    products(st, c, A, cur);
+    if (live) products(st, c, A, cur);
     stage_barrier();
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
@@ -534,6 +544,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     }
     if (j0 + 32 < g1) load_t(j0 + 32);
     lds_barrier();
+    if (!live) continue;  // the barriers above are the loop's only ones
     bf16x8 Tb[3][4];
 #pragma unroll
     for (int t = 0; t < 3; ++t)
