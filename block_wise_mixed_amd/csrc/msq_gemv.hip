@@ -54,10 +54,6 @@ namespace {
 extern __shared__ __align__(16) unsigned char smem[];
 
 constexpr int kMaxCols = 64;  // block columns per workgroup: one wave ballot
-#ifndef MSQ_M1_REG_SZ
-#define MSQ_M1_REG_SZ 0
-#endif
-constexpr bool kM1RegSZ = MSQ_M1_REG_SZ;
 constexpr size_t kLdsBudget = 64 * 1024;
 
 __device__ __forceinline__ float bf16f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
@@ -737,15 +733,8 @@ __device__ __forceinline__ void consume_m1(const Ctx& cx, int cl, const BlockReg
   const float4 S = *reinterpret_cast<const float4*>(smem + cx.sums_off + ((uint32_t)cl << 4));
   const float corr = bias.x * S.x + bias.y * S.y + bias.z * S.z + bias.w * S.w;
   const float xsum = (S.x + S.y) + (S.z + S.w);
-  float sc;
-  uint32_t z;
-  if constexpr (kM1RegSZ) {
-    sc = br.s;
-    z = br.z;
-  } else {
-    sc = *reinterpret_cast<const float*>(smem + cx.s_off + ((uint32_t)cl << 8) + 4 * lane);
-    z = smem[cx.z_off + ((uint32_t)cl << 6) + lane];
-  }
+  const float sc = *reinterpret_cast<const float*>(smem + cx.s_off + ((uint32_t)cl << 8) + 4 * lane);
+  const uint32_t z = smem[cx.z_off + ((uint32_t)cl << 6) + lane];
   y1 += sc * ((v - corr) - (float)z * xsum);
 }
 
@@ -762,7 +751,7 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
   };
   const float4 bias{pick(std::integral_constant<int, 0>{}), pick(std::integral_constant<int, 1>{}),
                     pick(std::integral_constant<int, 2>{}), pick(std::integral_constant<int, 3>{})};
-  ring_run<B, ring_depth<B>(), kM1RegSZ>(
+  ring_run<B, ring_depth<B>(), false>(
       cx, base, cols, n,
       [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
         consume_m1<B>(cx, cl, br, y1, bias);
@@ -866,10 +855,8 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
     stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
     stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
   }
-  if constexpr (!kM1RegSZ) {
-    stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
-    stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
-  }
+  stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
+  stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
   asm volatile("" ::: "memory");
   // Then the bit map and offsets (lane = column).
   const int lc = min(lane, ncl - 1);
