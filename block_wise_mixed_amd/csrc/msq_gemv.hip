@@ -544,14 +544,18 @@ __device__ __forceinline__ void consume_x(const RegsX<B>& br, f32x4 (&yacc)[4]) 
 
 // Ring depth of this kernel: two blocks, one for 8-bit blocks (the A
 // fragments ride along, so the register sets are larger than at M == 1; two
-// workgroups of 8 wavefronts per CU need them within 128 registers).
-template <int B>
-constexpr int ring_depth_x() { return B >= 8 ? 1 : 2; }
+// workgroups of 8 wavefronts per CU need them within 128 registers).  ONE:
+// one block for every bitwidth, for ranges of 64 block columns (eight or more
+// blocks per wavefront), where fewer loads in flight measured faster
+// (Llama-3-70B linears at M = 16: 4-6%); with four blocks per wavefront two
+// measured faster.  Deeper rings were slower at every shape tried.
+template <int B, bool ONE>
+constexpr int ring_depth_x() { return ONE ? 1 : (B >= 8 ? 1 : 2); }
 
-template <int B>
+template <int B, bool ONE>
 __device__ __forceinline__ void run_x(const CtxX& cx, const uint8_t* base, uint64_t cols, int n,
                                       f32x4 (&yacc)[4]) {
-  ring_run_t<B, ring_depth_x<B>(), B + 7, RegsX<B>>(
+  ring_run_t<B, ring_depth_x<B, ONE>(), B + 7, RegsX<B>>(
       cx.codes, base, cols, n,
       [&](const uint8_t* addr, int cl, RegsX<B>& br) __attribute__((always_inline)) {
         issue_x<B>(cx, addr, cl, br);
@@ -560,7 +564,7 @@ __device__ __forceinline__ void run_x(const CtxX& cx, const uint8_t* base, uint6
       [](auto) __attribute__((always_inline)) {});
 }
 
-template <int NW>
+template <int NW, bool ONE>
 __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ sf, int M,
                                                     WeightView w, int split, int kmax,
@@ -590,11 +594,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__
   auto base = [&](uint32_t o) __attribute__((always_inline)) {
     return w.codes + (int64_t)o * 1024 + 16 * lane;
   };
-  if (wr.n[0] > 0) run_x<1>(cx, base(off[0]), wr.cols[0], wr.n[0], yacc);
-  if (wr.n[1] > 0) run_x<2>(cx, base(off[1]), wr.cols[1], wr.n[1], yacc);
-  if (wr.n[2] > 0) run_x<3>(cx, base(off[2]), wr.cols[2], wr.n[2], yacc);
-  if (wr.n[3] > 0) run_x<4>(cx, base(off[3]), wr.cols[3], wr.n[3], yacc);
-  if (wr.n[4] > 0) run_x<8>(cx, base(off[4]), wr.cols[4], wr.n[4], yacc);
+  if (wr.n[0] > 0) run_x<1, ONE>(cx, base(off[0]), wr.cols[0], wr.n[0], yacc);
+  if (wr.n[1] > 0) run_x<2, ONE>(cx, base(off[1]), wr.cols[1], wr.n[1], yacc);
+  if (wr.n[2] > 0) run_x<3, ONE>(cx, base(off[2]), wr.cols[2], wr.n[2], yacc);
+  if (wr.n[3] > 0) run_x<4, ONE>(cx, base(off[3]), wr.cols[3], wr.n[3], yacc);
+  if (wr.n[4] > 0) run_x<8, ONE>(cx, base(off[4]), wr.cols[4], wr.n[4], yacc);
 
   // sum over the wavefronts in a fixed order and write out
   float* red = reinterpret_cast<float*>(smem);
@@ -1378,8 +1382,13 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
         reinterpret_cast<const uint8_t*>(g.gather) + align256((size_t)M * w.K * 2));
     if (small) {
       const float* sf = gather_sums_f32(g.gather, M, w.K);
-      hipLaunchKernelGGL(k_gemv16<8>, dim3((unsigned)(w.NBr * p.split)), dim3(512), p.lds_bytes,
-                         stream, xr, sf, (int)M, w, p.split, p.kr, dst, direct);
+      const dim3 grid((unsigned)(w.NBr * p.split));
+      if (p.kr >= kMaxCols)
+        hipLaunchKernelGGL((k_gemv16<8, true>), grid, dim3(512), p.lds_bytes, stream, xr, sf, (int)M,
+                           w, p.split, p.kr, dst, direct);
+      else
+        hipLaunchKernelGGL((k_gemv16<8, false>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                           (int)M, w, p.split, p.kr, dst, direct);
       e = hipGetLastError();
     } else {
       switch (p.mt) {
