@@ -526,8 +526,8 @@ def main() -> int:
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(block rows would shard across GPUs; see the design notes). Run with --gpus 1.",
+        print("bench.py measures one GPU only: there is no multi-GPU path here (block rows "
+              "would shard across GPUs, x replicated, y gathered). Run with --gpus 1.",
               file=sys.stderr)
         return 2
 
@@ -619,7 +619,7 @@ def main() -> int:
             "gbps_read": round(w_bytes / (pack_ms * 1e-3) / 1e9, 1),
             "gbps_moved": round(p_bytes / (pack_ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(p_bytes / (pack_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-            "note": "msq_quantize_pack of the 7 matrices back to back (k_block_offsets + k_pack each), "
+            "note": "msq_quantize_pack of the 7 matrices back to back (k_block_offsets + k_pack_rows each), "
                     "asynchronous, descriptors planned on the host beforehand; median of 3"}
     log(f"pack: {pack_ms:.3f} ms for 7 matrices, {pack['gbps_moved']} GB/s moved "
         f"({pack['hbm_frac']:.3f} of HBM)")
