@@ -83,7 +83,9 @@
  *   - Pointers are device pointers unless the name ends in _host.
  *   - The caller allocates and owns every buffer; the library allocates no
  *     memory, keeps no device state and never synchronizes.  Device calls
- *     are asynchronous on the given stream.
+ *     are asynchronous on the given stream.  Two stated exceptions:
+ *     msq_allocate_bits reads a status back after each iteration, and
+ *     msq_gemm_noalloc keeps its workspace in a static device array.
  *   - Errors are return codes.  All argument checks run before any launch,
  *     so outputs are untouched when a call returns an error.  A failed
  *     launch returns MSQ_ERR_HIP.
