@@ -11,8 +11,8 @@ A step is one decode pass (M = 1) through all seven packed linears: the
 activation gather, on-the-fly dequantization, matrix-core product and row
 scatter of every linear, issued as a decoder layer issues them (q, k, v on
 one activation in one grouped call, o, gate and up on one activation in one
-grouped call, down), captured once per weight copy in a HIP graph and
-replayed.  The same step as seven separate calls, each on its own
+grouped call, down), captured in one HIP graph that holds one step per
+weight copy (a model's decode graph holds all its layers) and replayed.  The same step as seven separate calls, each on its own
 activation, is reported beside it (decode_separate_calls).  The packed weights of the layer are cloned R times (R * packed >=
 1 GiB) and the copies are rotated step by step so that the 256 MB Infinity
 Cache cannot serve them.  value = effective weight GB/s = packed weight bytes
@@ -666,6 +666,11 @@ def main() -> int:
         return grouped, single
 
     def time_steps(step_fn, steps, warmup):
+        """Time exactly `steps` steps.  One HIP graph holds R steps, one per weight
+        copy in rotation order (a model's decode graph holds all its layers, so a
+        graph launch per layer step would overstate the launch cost); steps % R
+        leftover steps replay one-step graphs.  Events bracket every replay on
+        the current stream; per-step times are replay time / steps in it."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -673,27 +678,34 @@ def main() -> int:
                 step_fn(cp)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graphs = []
-        for cp in copies:
+        g_all = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_all):
+            for cp in copies:
+                step_fn(cp)
+        singles = []
+        for cp in copies[:steps % R]:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 step_fn(cp)
-            graphs.append(g)
+            singles.append(g)
         torch.cuda.synchronize()
-        for s in range(warmup):
-            graphs[s % R].replay()
+        for s in range(max(1, (warmup + R - 1) // R)):
+            g_all.replay()
         torch.cuda.synchronize()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        plan = [(g_all, R)] * (steps // R) + [(g, 1) for g in singles]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(plan) + 1)]
         t0 = time.perf_counter()
         evs[0].record()
-        for s in range(steps):
-            graphs[s % R].replay()
-            evs[s + 1].record()
+        for k, (g, _) in enumerate(plan):
+            g.replay()
+            evs[k + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = evs[0].elapsed_time(evs[steps]) / steps
-        per = [evs[s].elapsed_time(evs[s + 1]) for s in range(steps)]
-        del graphs
+        ms = evs[0].elapsed_time(evs[len(plan)]) / steps
+        per = []
+        for k, (_, n) in enumerate(plan):
+            per += [evs[k].elapsed_time(evs[k + 1]) / n] * n
+        del g_all, singles
         return ms, wall, per
 
     M = 1
@@ -833,7 +845,7 @@ def main() -> int:
                                "gate,up 28672x8192; down 8192x28672",
                    "M": M, "mean_bits": round(mean_bits, 4), "packed_bytes": layer_packed,
                    "decode_bytes": step_decode_bytes, "weight_copies": R,
-                   "timing": "HIP graph per weight copy, events around every timed replay"},
+                   "timing": f"one HIP graph of {R} steps (one per weight copy), events around every timed replay"},
         "hbm_frac": round(hbm_frac, 4),
         "step_spread": step_stats,
         "decode_separate_calls": decode_single,
