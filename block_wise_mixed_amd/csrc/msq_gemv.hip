@@ -763,6 +763,113 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
       after_issue);
 }
 
+// ---- half block rows (M == 1) -------------------------------------------------------------
+// For launches with fewer block rows than CUs and one K range, two workgroups
+// share a block row, each taking 32 of its 64 rows (row tiles 2h, 2h + 1 of
+// half h) over all of K, instead of a K split: no prep launch, no split
+// partials or counters.  A half loads only the chunks its row tiles use
+// (b = 2: chunk h; b = 4: chunks 2h, 2h + 1; b = 8: chunks 4h .. 4h + 3; the
+// 3-bit low plane: chunk h; b = 1 and the 3-bit high plane: their one chunk,
+// whose slots 8h .. 8h + 7 are shifted down to 0 .. 7), so that fragment
+// F' = 4 rt' + kt (rt' = rt - 2h) sits where half 0's fragment F' sits.
+// For b in {2, 4, 8} and the 3-bit low plane the operands are exactly those
+// of the whole-row kernel, and so are the sums; for 1-bit blocks and the
+// 3-bit high plane, half 1 unpacks with half 0's exponents (a different but
+// equally exact bias), so its fp32 sums may round differently.
+template <int B>
+constexpr int half_chunks() { return B == 1 ? 1 : (B == 2 ? 1 : (B == 8 ? 4 : 2)); }
+
+template <int B>
+struct HalfRegs {
+  uint4 ch[half_chunks<B>()];
+};
+
+// Chunk of the block that register J of half h holds.
+template <int B, int J>
+__device__ __forceinline__ int half_chunk(int h) {
+  if constexpr (B == 1) return 0;
+  else if constexpr (B == 2) return h;
+  else if constexpr (B == 3) return J == 0 ? h : 2;
+  else if constexpr (B == 4) return 2 * h + J;
+  else return 4 * h + J;
+}
+
+// One block of half h: 8 fragments, kt outer and rt' inner, each row tile's
+// k-steps accumulated in the whole-row kernel's order.
+template <int B>
+__device__ __forceinline__ void block_product_half(const uint4 (&ch)[half_chunks<B>()],
+                                                   const bf16x8 (&A)[4], f32x4 (&acc)[2]) {
+  auto step = [&](auto Ic) {
+    constexpr int I = decltype(Ic)::value;
+    constexpr int kt = I / 2, rt = I % 2, F = 4 * rt + kt;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const uint4& c = ch[B == 4 ? F / 4 : (B == 8 ? F / 2 : 0)];
+    f32x4 a = mfma_bf16(A[kt], exp_lo<B, F>(c), kt == 0 ? zero : acc[rt]);
+    if constexpr (B == 3) a = mfma_bf16(A[kt], exp_hi<3, F>(ch[1]), a);
+    if constexpr (B == 8) a = mfma_bf16(A[kt], exp_hi<8, F>(c), a);
+    acc[rt] = a;
+  };
+  [&]<int... Is>(std::integer_sequence<int, Is...>) {
+    (step(std::integral_constant<int, Is>{}), ...);
+  }(std::make_integer_sequence<int, 8>{});
+}
+
+// consume_m1 for half h (hsh = 8 h): rows 32 h + lane for lanes 0 .. 31;
+// the scales and zero points of the range are staged as [column][32].
+template <int B>
+__device__ __forceinline__ void consume_half(const Ctx& cx, int cl, const HalfRegs<B>& br,
+                                             uint32_t hsh, float& y1, const float4& bias) {
+  const int lane = threadIdx.x & 63;
+  uint4 ch[half_chunks<B>()];
+#pragma unroll
+  for (int j = 0; j < half_chunks<B>(); ++j) ch[j] = br.ch[j];
+  if constexpr (B == 1 || B == 3) {
+    constexpr int k = B == 1 ? 0 : 1;
+    ch[k] = uint4{ch[k].x >> hsh, ch[k].y >> hsh, ch[k].z >> hsh, ch[k].w >> hsh};
+  }
+  bf16x8 A[4];
+  const uint32_t a = (lane & 15) == 0 ? cx.a_lane + ((uint32_t)cl << 8) : cx.zero_off;
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt)
+    A[kt] = as_bf16x8(*reinterpret_cast<const uint4*>(smem + a + 64 * kt));
+  f32x4 acc[2];
+  block_product_half<B>(ch, A, acc);
+  const float v = rows_to_lanes(acc[0][0], acc[1][0], 0.f, 0.f);
+  const float4 S = *reinterpret_cast<const float4*>(smem + cx.sums_off + ((uint32_t)cl << 4));
+  const float corr = bias.x * S.x + bias.y * S.y + bias.z * S.z + bias.w * S.w;
+  const float xsum = (S.x + S.y) + (S.z + S.w);
+  const uint32_t l32 = (uint32_t)lane & 31u;
+  const float sc = *reinterpret_cast<const float*>(smem + cx.s_off + ((uint32_t)cl << 7) + 4 * l32);
+  const uint32_t z = smem[cx.z_off + ((uint32_t)cl << 5) + l32];
+  y1 += sc * ((v - corr) - (float)z * xsum);
+}
+
+// M == 1 run of half h: the same register ring over the half's chunks.
+template <int B, typename AfterIssue>
+__device__ __forceinline__ void run_ring_half(const Ctx& cx, const uint8_t* base, uint64_t cols,
+                                              int n, int h, float& y1, AfterIssue&& after_issue) {
+  const int rt = (threadIdx.x & 63) >> 4;  // rt' for lanes 0 .. 31
+  auto pick = [rt](auto KTc) __attribute__((always_inline)) {
+    constexpr int kt = decltype(KTc)::value;
+    return rt == 0 ? exp_bias(B, kt)
+                   : (rt == 1 ? exp_bias(B, 4 + kt) : (rt == 2 ? exp_bias(B, 8 + kt) : exp_bias(B, 12 + kt)));
+  };
+  const float4 bias{pick(std::integral_constant<int, 0>{}), pick(std::integral_constant<int, 1>{}),
+                    pick(std::integral_constant<int, 2>{}), pick(std::integral_constant<int, 3>{})};
+  const uint32_t hsh = 8u * (uint32_t)h;
+  ring_run_t<B, ring_depth<B>(), half_chunks<B>(), HalfRegs<B>>(
+      cx.codes, base, cols, n,
+      [&](const uint8_t* addr, int, HalfRegs<B>& br) __attribute__((always_inline)) {
+        [&]<int... Js>(std::integer_sequence<int, Js...>) {
+          ((br.ch[Js] = *reinterpret_cast<const uint4*>(addr + 1024 * half_chunk<B, Js>(h))), ...);
+        }(std::make_integer_sequence<int, half_chunks<B>()>{});
+      },
+      [&](int cl, const HalfRegs<B>& br) __attribute__((always_inline)) {
+        consume_half<B>(cx, cl, br, hsh, y1, bias);
+      },
+      after_issue);
+}
+
 // Direct global-to-LDS copies of 16 (4) bytes per lane: lane i writes at
 // LDS byte `off` (wavefront-uniform, from the dynamic LDS base) + 16 i (4 i).
 // Written as inline assembly because the compiler's builtin for them makes
@@ -807,7 +914,7 @@ __host__ __device__ constexpr size_t m1_lds_bytes_gather(int kmax) {
 // its first code loads are in flight, so that no prep launch is needed.
 // Both give the same bits: the reordered values are copies, and the k-step
 // sums are formed by the same pairwise addition tree.
-template <int NW, bool kGather>
+template <int NW, bool kGather, bool kHalf = false>
 __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
                                         const float4* __restrict__ sums_g,
                                         const uint16_t* __restrict__ x,
@@ -823,10 +930,13 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   // (gathering needs at least 8 wavefronts: fewer would hold too many registers)
   constexpr int kPermUnits = (kMaxCols * 32 + kThreads - 1) / kThreads;
   static_assert(!kGather || kPermUnits <= 4, "gathering workgroups have at least 8 wavefronts");
+  static_assert(!kHalf || kGather, "half block rows reorder x themselves (one K range)");
   const int lane = threadIdx.x & 63;
   const int t = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blk / split, sp = blk - (blk / split) * split;
+  // kHalf: workgroup blk takes rows 32 h .. 32 h + 31 of block row r (split == 1)
+  const int r = kHalf ? blk >> 1 : blk / split, sp = kHalf ? 0 : blk - (blk / split) * split;
+  const int h = kHalf ? blk & 1 : 0;
   const int c0 = sp * kmax;
   const int ncl = min(w.NBc, c0 + kmax) - c0;
   const int64_t rowbase = (int64_t)r * w.NBc + c0;
@@ -843,7 +953,8 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   const int nperm = ncl * 32;  // uint4s of perm_col in the range (c0 == 0)
   const size_t xrow_off = m1_xrow_offset(kmax);
   const size_t s_off = m1_scale_offset(kmax);
-  const size_t z_off = s_off + 256 * (size_t)ncl;  // the zero points follow the range's scales
+  // the zero points follow the range's scales ([ncl][64], halves [ncl][32])
+  const size_t z_off = s_off + (kHalf ? 128 : 256) * (size_t)ncl;
   auto stage16 = [&](const void* g, size_t lds_off, int n, auto Units) __attribute__((always_inline)) {
     constexpr int kU = decltype(Units)::value;
 #pragma unroll
@@ -859,8 +970,27 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
     stage16(xg + (int64_t)c0 * kBlockCols, 0, ncl * 16, std::integral_constant<int, kUnits>{});
     stage16(sums_g + c0, sums_off, ncl, std::integral_constant<int, kSumsUnits>{});
   }
-  stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
-  stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
+  if constexpr (kHalf) {
+    // the half's 32 scales (8 uint4) and zero points (2 uint4) of each column
+    auto stage_half = [&](const void* g, size_t lds_off, int per_col, int n, auto Units)
+                          __attribute__((always_inline)) {
+      constexpr int kU = decltype(Units)::value;
+      const uint4* g4 = reinterpret_cast<const uint4*>(g);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int idx = t + u * kThreads;
+        const int c = idx / per_col, part = idx - c * per_col;
+        if (idx < n)
+          lds_copy16(g4 + (int64_t)c * (2 * per_col) + h * per_col + part,
+                     (uint32_t)lds_off + 16 * (idx - lane));
+      }
+    };
+    stage_half(w.scale + rowbase * kBlockRows, s_off, 8, ncl * 8, std::integral_constant<int, kSUnits>{});
+    stage_half(w.zero + rowbase * kBlockRows, z_off, 2, ncl * 2, std::integral_constant<int, kZUnits>{});
+  } else {
+    stage16(w.scale + rowbase * kBlockRows, s_off, ncl * 16, std::integral_constant<int, kSUnits>{});
+    stage16(w.zero + rowbase * kBlockRows, z_off, ncl * 4, std::integral_constant<int, kZUnits>{});
+  }
   asm volatile("" ::: "memory");
   // Then the bit map and offsets (lane = column).
   const int lc = min(lane, ncl - 1);
@@ -956,18 +1086,31 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   // runs of bitwidths 1, 2, 3, 4, 8 in order; the first non-empty one hosts the start-up
   float y1 = 0.f;
   const int kfirst = wr.n[0] > 0 ? 0 : wr.n[1] > 0 ? 1 : wr.n[2] > 0 ? 2 : wr.n[3] > 0 ? 3 : wr.n[4] > 0 ? 4 : 5;
+  // run k (bitwidth kSegBits[k]) of this wavefront, whole rows or the half's
+  auto run = [&](auto Bc, int k, auto&& after) __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    if constexpr (kHalf)
+      run_ring_half<B>(cx, run_base(cx, off[k]), wr.cols[k], wr.n[k], h, y1, after);
+    else
+      run_ring<B>(cx, run_base(cx, off[k]), wr.cols[k], wr.n[k], y1, after);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
   switch (kfirst) {
-    case 0: run_ring<1>(cx, run_base(cx, off[0]), wr.cols[0], wr.n[0], y1, startup); break;
-    case 1: run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1, startup); break;
-    case 2: run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, startup); break;
-    case 3: run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1, startup); break;
-    case 4: run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1, startup); break;
+    case 0: run(I1{}, 0, startup); break;
+    case 1: run(I2{}, 1, startup); break;
+    case 2: run(I3{}, 2, startup); break;
+    case 3: run(I4{}, 3, startup); break;
+    case 4: run(I8{}, 4, startup); break;
     default: startup(std::integral_constant<int, 0>{}); break;
   }
-  if (kfirst < 1 && wr.n[1] > 0) run_ring<2>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], y1, none);
-  if (kfirst < 2 && wr.n[2] > 0) run_ring<3>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], y1, none);
-  if (kfirst < 3 && wr.n[3] > 0) run_ring<4>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], y1, none);
-  if (kfirst < 4 && wr.n[4] > 0) run_ring<8>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], y1, none);
+  if (kfirst < 1 && wr.n[1] > 0) run(I2{}, 1, none);
+  if (kfirst < 2 && wr.n[2] > 0) run(I3{}, 2, none);
+  if (kfirst < 3 && wr.n[3] > 0) run(I4{}, 3, none);
+  if (kfirst < 4 && wr.n[4] > 0) run(I8{}, 4, none);
 
   // reduce the wavefronts in a fixed order and write out
   __syncthreads();
@@ -978,6 +1121,10 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   float v = y1;
 #pragma unroll
   for (int k = 0; k < NW - 1; ++k) v += red[k * 64 + lane];
+  if constexpr (kHalf) {
+    if (lane < 32) y[orig_row(w.perm_row, (int64_t)r * kBlockRows + 32 * h + lane, w.N)] = v;
+    return;
+  }
   const int64_t row = (int64_t)r * kBlockRows + lane;
   if (split == 1) {
     y[orig_row(w.perm_row, row, w.N)] = v;
@@ -1002,12 +1149,12 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
   y[orig_row(w.perm_row, row, w.N)] = tot;
 }
 
-template <int NW, bool kGather>
+template <int NW, bool kGather, bool kHalf = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) void k_gemv_m1(
     const uint16_t* __restrict__ xg, const float4* __restrict__ sums_g,
     const uint16_t* __restrict__ x, WeightView w, int split, int kmax, float* __restrict__ part,
     float* __restrict__ y, uint32_t* __restrict__ counters) {
-  gemv_m1<NW, kGather>(xg, sums_g, x, w, split, kmax, part, y, counters, blockIdx.x);
+  gemv_m1<NW, kGather, kHalf>(xg, sums_g, x, w, split, kmax, part, y, counters, blockIdx.x);
 }
 
 // ---- grouped M == 1 calls: up to kGroupMax matrices per launch ---------------------------
@@ -1030,6 +1177,7 @@ struct M1Job {
   uint32_t* counters;
   int split, kr, ncounters;
   int gather;  // the decode workgroups reorder x themselves (no prep workgroups)
+  int halves;  // two workgroups per block row, 32 rows each (gather, one K range)
   int prep_begin, wg_begin;
 };
 
@@ -1068,6 +1216,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(4))) vo
     M1Group g) {
   const M1Job q = pick_job(g, group_job(g, blockIdx.x, false));
   // the branch is uniform over the workgroup
+  if constexpr (NW == 8) {
+    if (q.halves) {
+      gemv_m1<NW, true, true>(nullptr, nullptr, q.x, q.w, 1, q.kr, q.part, q.y, q.counters,
+                              blockIdx.x - q.wg_begin);
+      return;
+    }
+  }
   if constexpr (NW >= 8) {
     if (q.gather) {
       gemv_m1<NW, true>(nullptr, nullptr, q.x, q.w, q.split, q.kr, q.part, q.y, q.counters,
@@ -1189,6 +1344,14 @@ template <int NW>
 hipError_t launch_m1(const GemvWorkspace& g, const uint16_t* x, bool gather, const WeightView& w,
                      float* y, const GemvPlan& p, hipStream_t stream) {
   const unsigned grid = (unsigned)(w.NBr * p.split);
+  if constexpr (NW == 8) {
+    if (p.halves) {
+      hipLaunchKernelGGL((k_gemv_m1<8, true, true>), dim3(2 * (unsigned)w.NBr), dim3(512),
+                         m1_launch_lds(p, true), stream, nullptr, nullptr, x, w, 1, p.kr, g.part, y,
+                         g.counters);
+      return hipGetLastError();
+    }
+  }
   if constexpr (NW >= 8) {
     if (gather) {
       hipLaunchKernelGGL((k_gemv_m1<NW, true>), dim3(grid), dim3(NW * 64), m1_launch_lds(p, true),
@@ -1255,6 +1418,16 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
       if (NBr >= 128) split = std::min<int>(split, std::max<int>(1, (int)((M + 3) / 4)));
     }
   }
+  // M == 1, all launch choices automatic, at most 64 block columns, and a K
+  // split wanted (at most 128 block rows in the launch): two workgroups per
+  // block row (32 rows each, all of K) instead, so that no prep launch runs.
+  // (With 129 .. 255 block rows whole rows in one K range measured faster:
+  // halves double the x staging per row for little more parallelism.)
+  p.halves = M == 1 && opt.gemv_split <= 0 && opt.gemv_waves == 0 && !opt.m1_prep && split > 1 &&
+                     NBc <= kMaxCols
+                 ? 1
+                 : 0;
+  if (p.halves) split = 1;
   if (split > NBc) split = NBc;
   if (split < 1) split = 1;
   int kr = (NBc + split - 1) / split;
@@ -1325,11 +1498,12 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
     q.kr = p.kr;
     q.ncounters = p.split > 1 ? (int)w[i].NBr : 0;
     q.gather = p.gather;
+    q.halves = p.halves;
     q.prep_begin = prep_total;
     q.wg_begin = wg_total;
     const int64_t nbc = w[i].K / kBlockCols;
     if (!q.gather) prep_total += (int)std::max<int64_t>((nbc + 3) / 4, (q.ncounters + 255) / 256);
-    wg_total += (int)(w[i].NBr * p.split);
+    wg_total += (int)(w[i].NBr * (p.halves ? 2 : p.split));
     lds = std::max(lds, m1_launch_lds(p, q.gather != 0));
   }
   // prep workgroups only for the jobs that do not gather (a job with an

@@ -51,6 +51,7 @@ struct GemvPlan {
   int nw;           // wavefronts per workgroup
   int xs_stride;    // bf16 elements per LDS row of the activation slice
   int gather;       // M == 1: the workgroups reorder x themselves (no prep launch)
+  int halves;       // M == 1: two workgroups per block row of 32 rows each (gather, split 1)
   size_t lds_bytes; // dynamic LDS per workgroup
   size_t workspace; // bytes: fp32 partials (split > 1), then M == 1 prep or M > 1 gather buffers
 };

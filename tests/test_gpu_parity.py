@@ -189,6 +189,30 @@ def test_decode_gather_matches_prep(msq, N, K, seed, waves):
     check_y(msq, pw, c, ref, 1, options=opt)
 
 
+@pytest.mark.parametrize("N,K,seed", [(128, 8192, 80), (192, 1024, 81), (64, 128, 82),
+                                      (320, 640, 83), (960, 4096, 84)])
+def test_decode_half_rows(msq, N, K, seed):
+    """M = 1 on fewer than 256 block rows with one K range: two workgroups per block
+    row, 32 rows each (automatic choice).  With 2-, 4- and 8-bit blocks only, the
+    halves use the whole-row kernel's operands and summation order: y equals the
+    whole-row result (gemv_split = 1) bit for bit.  With every bitwidth, half 1
+    unpacks 1-bit blocks and the 3-bit high plane with other (exact) biases: both
+    match the oracle within tolerance.  Twice in a row: no state between calls."""
+    for dist, bitwise in (({0: .1, 2: .5, 4: .3, 8: .1}, True), (SMALL_DIST, False)):
+        c = synth.random_case(N, K, seed, dist=dist)
+        pw, ref = check_pack(msq, c)
+        x = _bf16_cuda(c.x(1))
+        y_half = msq.gemm(x, pw)
+        y_again = msq.gemm(x, pw)
+        y_whole = msq.gemm(x, pw, options={"gemv_split": 1})
+        torch.cuda.synchronize()
+        assert torch.equal(y_half, y_again)
+        if bitwise:
+            assert torch.equal(y_half, y_whole)
+        check_y(msq, pw, c, ref, 1)
+        check_y(msq, pw, c, ref, 1, options={"gemv_split": 1})
+
+
 def test_group_decode_gather_mixed(msq, group_cases):
     """A grouped M = 1 call whose jobs split between gathering workgroups (one K range)
     and the prep launch (a 16384-wide matrix needs two K ranges; placed first, in the
@@ -329,6 +353,22 @@ def test_group_matches_single_calls(msq, group_cases, M):
             check_y(msq, pw, c, ref, M, x=x, options=opt)
 
 
+def test_group_half_rows_match_single_calls(msq, group_cases):
+    """Automatic M = 1 launch of a group of 17 block rows: every job runs as half
+    block rows in the one decode launch, and each output equals its single call
+    (also half rows) bit for bit, twice in a row."""
+    pws = [pw for _, pw, _ in group_cases]
+    x_shared = group_cases[0][0].x(1)
+    xs = [x_shared, x_shared, x_shared, group_cases[3][0].x(1)]
+    for rep in range(2):
+        outs = msq.gemm_group(xs, pws)
+        singles = [msq.gemm(x, pw) for x, pw in zip(xs, pws)]
+        torch.cuda.synchronize()
+        for (c, pw, ref), x, y, single in zip(group_cases, xs, outs, singles):
+            assert torch.equal(y, single), c.name
+            check_y(msq, pw, c, ref, 1, x=x)
+
+
 def test_group_prefill_one_launch(msq):
     """Two 4096 x 1024 matrices at M = 1024 have enough tiles for the one grouped GEMM
     launch (smaller groups run as split-K single calls): each output equals its single
@@ -385,8 +425,8 @@ def test_group_sizes(msq, group_cases, M):
 def test_group_graph_replay_matches_eager(msq, group_cases, split):
     """bench.py captures grouped decode calls in HIP graphs: every replay, with eager
     work in between on the same workspace, must equal the eager result bit for bit;
-    with the automatic split (prep launch, split counters) and with one K range (the
-    workgroups reorder x themselves)."""
+    automatic (17 block rows: half block rows) and with one K range forced (whole
+    block rows; the workgroups reorder x themselves)."""
     opt = None if split == "auto" else {"gemv_split": int(split)}
     pws = [pw for _, pw, _ in group_cases]
     x_shared = torch.from_numpy(group_cases[0][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
