@@ -1,7 +1,8 @@
 // Device-side helpers shared by the GEMV and GEMM kernels: operand types, the
-// bf16 matrix instruction, and the in-register unpack of packed format v1.
+// bf16 matrix instruction, and the in-register unpack of the quantized blocks
+// of packed format v2 (16-bit blocks are B operands as they are).
 //
-// Packed format v1 (include/msq.h): a b-bit block is b chunks of 1 KiB; lane
+// Packed format (include/msq.h): a b-bit block is b chunks of 1 KiB; lane
 // l of a wavefront owns 16 bytes (four 32-bit words) of every chunk.  For
 // fragment F = 4*rt + kt and b in {1,2,4}, slot s = F % (16/b) of chunk
 // F / (16/b) holds, in each of the four words, two codes at bits b*s and

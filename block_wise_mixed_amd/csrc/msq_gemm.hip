@@ -1,6 +1,6 @@
-// Prefill GEMM for gfx950: y = x . W^T for any M (used for M > 64), W
-// dequantized on the fly from packed format v1 and multiplied on the bf16
-// matrix cores.
+// Prefill GEMM for gfx950: y = x . W^T for any M (the automatic choice above
+// M = 16), W dequantized on the fly from packed format v2 (include/msq.h) and
+// multiplied on the bf16 matrix cores.
 //
 // Two kernels:
 //   k_gather_x : x_r[m][j] = x[m][perm_col[j]] (bf16) and the per-group sums

@@ -1,6 +1,7 @@
 // Decode GEMV for gfx950: y = x . W^T for M <= 64, W dequantized block by
-// block from packed format v1 in registers.  Memory-bound: every byte of the
-// packed codes is read once, with one 16-byte load per lane per 1 KiB chunk.
+// block from packed format v2 (include/msq.h) in registers.  Memory-bound:
+// every byte of the packed codes is read once, with one 16-byte load per
+// lane per 1 KiB chunk.
 //
 // Work split.  A workgroup of NW wavefronts owns one block row r (64 output
 // rows) and a range of at most 64 block columns [c0, c0 + ncl) (a K split).
@@ -8,18 +9,19 @@
 //     forms, per bitwidth, a 64-bit mask of the columns holding it (wave
 //     ballots).  Walking bitwidths 1, 2, 3, 4, 8 and columns in order gives
 //     the blocks in packed order; the wavefronts cut that list into NW pieces
-//     of equal packed size, so each wavefront gets at most a few runs of
+//     of equal cost, so each wavefront gets at most a few runs of
 //     same-bitwidth blocks.
-//  2. The activations, reordered through perm_col once per call by the
-//     gather kernel (the activation reordering of the "SFMP" abstract), are
-//     staged in LDS slice by slice together with their per-group sums, used
-//     to fold the zero point.
+//  2. The activations reordered through perm_col (the activation reordering
+//     of the "SFMP" abstract) and their per-group sums, used to fold the zero
+//     point, come from the gather kernel (k_gemv: staged in LDS slice by
+//     slice; k_gemv16: read straight from L2 with each block) or, at M == 1,
+//     from the workgroup's own reordering of x in LDS (or the prep kernel).
 //  3. Each wavefront walks its runs.  Inside a run the bitwidth is a
-//     compile-time constant, so the loads of the next blocks (codes, scales,
-//     zero points) are issued while the current block is unpacked and
-//     multiplied, with static wait counts.  Each 16x32 fragment is unpacked
-//     into exact bf16 operands and fed to v_mfma_f32_16x16x32_bf16 (M padded
-//     to 16), then scale and zero point are folded per row:
+//     compile-time constant, so the loads of the next blocks are issued while
+//     the current block is unpacked and multiplied, with static wait counts
+//     (register rings).  Each 16x32 fragment is unpacked into exact bf16
+//     operands and fed to v_mfma_f32_16x16x32_bf16 (M padded to 16), then
+//     scale and zero point are folded per row:
 //         y[row] += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
 //  4. The wavefronts reduce through LDS in a fixed order.  One K split writes
 //     y directly (scattered to original rows through perm_row); several
@@ -27,11 +29,12 @@
 //     the last workgroup of the block row to finish; M > 1: by
 //     k_gemv_reduce), so results are bitwise reproducible.
 //
-// M == 1 has its own kernels (k_gemv_m1, after k_prep_m1 only when K is
-// split into several ranges): the reordered x comes with per-column k-step
-// sums for the bias corrections, the unpack avoids most shifts, the scales
-// and zero points are staged in LDS, and each wavefront keeps 2 to 4 KiB of
-// codes in flight.
+// Kernels: k_gemv_m1 (M == 1: per-column k-step sums for the bias
+// corrections, an unpack that avoids most shifts, scales and zero points
+// staged in LDS, 2 to 4 KiB of codes in flight per wavefront; half block
+// rows of 32 rows for small launches instead of a K split), k_gemv16
+// (2 <= M <= 16), k_gemv (M <= 64 when the GEMV is forced), their group
+// variants, and the split reductions.
 //
 // Per-block precision and block layout: "ScaleBITS" summary page, section
 // Approach; RTN-g128 dequantization s * (q - z): section Limitations.
