@@ -5,9 +5,9 @@
 // products afterwards:
 //     y[m][perm_row[n]] += sum over 16-bit blocks (r, c) of row n of
 //                          sum_k x[m][perm_col[128 c + k]] W[n][k].
-// The packed block is the bf16 weight in the v1 layout with one fragment per
-// chunk, so chunk F = 4 rt + kt at lane l is already the matrix instruction's
-// B operand for row tile rt, k-step kt: no unpacking.
+// The packed block is the bf16 weight in the format's b-bit layout with one
+// fragment per chunk, so chunk F = 4 rt + kt at lane l is already the matrix
+// instruction's B operand for row tile rt, k-step kt: no unpacking.
 //
 // Workgroup (block row r, 16 or 64 rows of M); wavefront rt owns rows
 // 16 rt .. 16 rt + 15 of the block row.  Per 16-bit block: x's slice is
