@@ -693,6 +693,61 @@ __global__ __launch_bounds__(kUnpermuteThreads) void k_unpermute_rows(UnpermuteG
   for (int n = t; n < N; n += kUnpermuteThreads) row[n] = lrow[n];
 }
 
+// The same with 16-byte accesses (every job's y and perm_row 16-byte aligned;
+// N is a multiple of 64): each thread reads four float4 of the row and the
+// four int4 of perm_row that go with them before scattering the sixteen
+// values into LDS, and writes the permuted row back as float4.
+constexpr int kUnpermuteVec = 4;  // float4 loads in flight per thread
+__global__ __launch_bounds__(kUnpermuteThreads) void k_unpermute_rows4(UnpermuteGroup g) {
+  UnpermuteJob q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k == (int)blockIdx.y) q = g.job[k];
+  float* row = q.y + (int64_t)blockIdx.x * q.N;
+  float* lrow = reinterpret_cast<float*>(smem);
+  const int N = (int)q.N, N4 = N / 4, hi = N - 1;
+  const int t = threadIdx.x;
+  const float4* row4 = reinterpret_cast<const float4*>(row);
+  const int4* perm4 = reinterpret_cast<const int4*>(q.perm_row);
+  for (int base = t; base < N4; base += kUnpermuteVec * kUnpermuteThreads) {
+    float4 v[kUnpermuteVec];
+    int4 p[kUnpermuteVec];
+#pragma unroll
+    for (int i = 0; i < kUnpermuteVec; ++i) {
+      const int n4 = min(base + i * kUnpermuteThreads, N4 - 1);
+      v[i] = row4[n4];
+      p[i] = perm4[n4];
+    }
+#pragma unroll
+    for (int i = 0; i < kUnpermuteVec; ++i)
+      if (base + i * kUnpermuteThreads < N4) {
+        lrow[min(max(p[i].x, 0), hi)] = v[i].x;
+        lrow[min(max(p[i].y, 0), hi)] = v[i].y;
+        lrow[min(max(p[i].z, 0), hi)] = v[i].z;
+        lrow[min(max(p[i].w, 0), hi)] = v[i].w;
+      }
+  }
+  __syncthreads();  // the whole row is read (and scattered) before any of it is overwritten
+  float4* out4 = reinterpret_cast<float4*>(row);
+  const float4* l4 = reinterpret_cast<const float4*>(lrow);
+  for (int n4 = t; n4 < N4; n4 += kUnpermuteThreads) out4[n4] = l4[n4];
+}
+
+// Launch the un-permutation of the group's jobs (rows 0 .. M-1 of each).
+hipError_t launch_unpermute(const UnpermuteGroup& u, int64_t M, int64_t maxn, hipStream_t stream) {
+  bool vec = true;
+  for (int i = 0; i < u.count; ++i)
+    vec = vec && ((reinterpret_cast<uintptr_t>(u.job[i].y) |
+                   reinterpret_cast<uintptr_t>(u.job[i].perm_row)) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(k_unpermute_rows4, dim3((unsigned)M, (unsigned)u.count),
+                       dim3(kUnpermuteThreads), (size_t)maxn * 4, stream, u);
+  else
+    hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, (unsigned)u.count),
+                       dim3(kUnpermuteThreads), (size_t)maxn * 4, stream, u);
+  return hipGetLastError();
+}
+
 // Launch shape of one GEMM call.  Fewer tiles than kFillTiles (two per CU)
 // split K into ranges of at least kMinSplitGroups groups (the correction
 // product works on batches of 32 groups, so shorter ranges waste it), the
@@ -801,9 +856,7 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
       maxn = std::max(maxn, w[i].N);
     }
   if (u.count == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, (unsigned)u.count), dim3(kUnpermuteThreads),
-                     (size_t)maxn * 4, stream, u);
-  return hipGetLastError();
+  return launch_unpermute(u, M, maxn, stream);
 }
 
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
@@ -862,9 +915,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
   UnpermuteGroup u{};
   u.job[0] = UnpermuteJob{y, w.perm_row, w.N};
   u.count = 1;
-  hipLaunchKernelGGL(k_unpermute_rows, dim3((unsigned)M, 1u), dim3(kUnpermuteThreads),
-                     (size_t)w.N * 4, stream, u);
-  return hipGetLastError();
+  return launch_unpermute(u, M, w.N, stream);
 }
 
 }  // namespace msq

@@ -459,6 +459,25 @@ def test_group_graph_replay_matches_eager(msq, group_cases, split):
 
 # ---- shipped branches that the full-size workloads do not reach ------------------------
 
+def test_prefill_unaligned_output_rows(msq):
+    """The row un-permutation after the prefill GEMM uses 16-byte accesses when y and
+    perm_row are 16-byte aligned and 4-byte ones otherwise: y at a 4-byte offset
+    gives the same result bit for bit."""
+    c = synth.random_case(256, 1024, 90, dist=SMALL_DIST)
+    pw, ref = check_pack(msq, c)
+    M = 130
+    opt = {"gemm_split": 1}  # one K range: the tiles write y reordered, then the un-permutation
+    x = _bf16_cuda(c.x(M))
+    y_al = msq.gemm(x, pw, kernel="gemm", options=opt)
+    buf = torch.empty(M * pw.N + 1, dtype=torch.float32, device="cuda")
+    y_un = buf[1:].view(M, pw.N)
+    assert y_un.data_ptr() % 16 == 4
+    msq.gemm(x, pw, kernel="gemm", out=y_un, options=opt)
+    torch.cuda.synchronize()
+    assert torch.equal(y_un, y_al)
+    check_y(msq, pw, c, ref, M, kernel="gemm", options=opt)
+
+
 def test_prefill_wide_n_scatters_directly(msq):
     """N > 32768 (a vocabulary-sized output): the prefill GEMM stores y through perm_row
     itself instead of the row un-permutation pass (whose LDS row holds at most 32768
