@@ -634,6 +634,39 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x_group(GemmGroup g) 
              0, padded_groups(q.w.K / kBlockCols) * 16);
 }
 
+// Grouped gather of the decode kernel at small M (fp32 sums too): job j owns
+// the workgroups [begin_j, begin of j + 1), M rows x `slices` slices of
+// whole groups, cut as launch_gather_x cuts one matrix's.
+struct GatherJob {
+  const uint16_t* x;
+  const int32_t* perm_col;
+  int64_t K;
+  uint16_t* xr;
+  uint16_t* sxs;
+  float* sf;
+  int staged, slices, begin;
+};
+
+struct GatherGroup {
+  GatherJob job[kGroupMax];
+  int count;
+  int M;
+};
+
+__global__ __launch_bounds__(kGatherThreads) void k_gather_x_jobs(GatherGroup g) {
+  GatherJob q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.count && (int)blockIdx.x >= g.job[k].begin) q = g.job[k];
+  const int b = blockIdx.x - q.begin;
+  const int m = b / q.slices, sl = b - m * q.slices;
+  const int64_t Gp = padded_groups(q.K / kBlockCols);
+  const int64_t per = (Gp + q.slices - 1) / q.slices * 16;
+  const int64_t qs = (int64_t)sl * per;
+  gather_row(q.x, q.K, g.M, q.perm_col, q.xr, q.sxs, q.sf, gather_mpad(g.M), q.staged, m, qs,
+             min(qs + per, Gp * 16));
+}
+
 template <int CH>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm_group(
     GemmGroup g) {
@@ -859,6 +892,43 @@ hipError_t launch_gemm_group(const uint16_t* const* x, int64_t M, const WeightVi
   return launch_unpermute(u, M, maxn, stream);
 }
 
+// Slices per row of the gather: with few rows each row's groups are cut into
+// slices of their own workgroups (every slice stages the whole row), so that
+// small M still fills the GPU.
+static int64_t gather_slices(int64_t M, int64_t K) {
+  return std::max<int64_t>(
+      1, std::min<int64_t>(padded_groups(K / kBlockCols) / 16, 256 / std::max<int64_t>(M, 1)));
+}
+
+hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const WeightView* w,
+                                 void* const* ws, int count, hipStream_t stream) {
+  if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
+  GatherGroup g{};
+  g.count = count;
+  g.M = (int)M;
+  size_t lds = 0;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    GatherJob& q = g.job[i];
+    const int64_t K = w[i].K;
+    uint8_t* b = reinterpret_cast<uint8_t*>(ws[i]);
+    q.x = x[i];
+    q.perm_col = w[i].perm_col;
+    q.K = K;
+    q.xr = reinterpret_cast<uint16_t*>(b);
+    q.sxs = reinterpret_cast<uint16_t*>(b + ((((size_t)M * K * 2) + 255) & ~(size_t)255));
+    q.sf = gather_sums_f32(ws[i], M, K);
+    q.staged = (size_t)K * 2 <= kGatherMaxLds;
+    if (q.staged) lds = std::max(lds, (size_t)K * 2);
+    q.slices = (int)gather_slices(M, K);
+    q.begin = (int)total;
+    total += M * q.slices;
+  }
+  if (total > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_gather_x_jobs, dim3((unsigned)total), dim3(kGatherThreads), lds, stream, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
                            hipStream_t stream, bool sums_f32) {
   const int64_t K = w.K;
@@ -867,10 +937,7 @@ hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, vo
   uint16_t* sxs = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(ws) + xr_bytes);
   const size_t row_bytes = (size_t)K * 2;
   const int staged = row_bytes <= kGatherMaxLds;
-  // few rows: each row's groups are cut into slices of their own workgroups
-  // (every slice stages the whole row), so that small M still fills the GPU
-  const int64_t slices = std::max<int64_t>(
-      1, std::min<int64_t>(padded_groups(K / kBlockCols) / 16, 256 / std::max<int64_t>(M, 1)));
+  const int64_t slices = gather_slices(M, K);
   float* sf = sums_f32 ? gather_sums_f32(ws, M, K) : nullptr;
   hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M, (unsigned)slices), dim3(kGatherThreads),
                      staged ? row_bytes : 0, stream, x, K, M, w.perm_col, xr, sxs, sf,

@@ -567,14 +567,15 @@ __device__ __forceinline__ void run_x(const CtxX& cx, const uint8_t* base, uint6
       [](auto) __attribute__((always_inline)) {});
 }
 
+// Workgroup `blk` (block row blk / split, K range blk % split) of one matrix.
 template <int NW, bool ONE>
-__global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
-                                                    const float* __restrict__ sf, int M,
-                                                    WeightView w, int split, int kmax,
-                                                    float* __restrict__ out, int direct) {
+__device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
+                                       const float* __restrict__ sf, int M, const WeightView& w,
+                                       int split, int kmax, float* __restrict__ out, int direct,
+                                       int blk) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blockIdx.x / split, sp = blockIdx.x - (blockIdx.x / split) * split;
+  const int r = blk / split, sp = blk - (blk / split) * split;
   const int c0 = sp * kmax;
   const int ncl = min(w.NBc, c0 + kmax) - c0;
   const int64_t rowbase = (int64_t)r * w.NBc + c0;
@@ -633,6 +634,14 @@ __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__
       else
         out[((int64_t)sp * M + m) * w.N + row] = v;
     }
+}
+
+template <int NW, bool ONE>
+__global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
+                                                    const float* __restrict__ sf, int M,
+                                                    WeightView w, int split, int kmax,
+                                                    float* __restrict__ out, int direct) {
+  gemv16<NW, ONE>(xr, sf, M, w, split, kmax, out, direct, blockIdx.x);
 }
 
 // ======================================================================================
@@ -1276,12 +1285,11 @@ __global__ __launch_bounds__(kReduceRowThreads) void k_gemv_reduce_rows(
   }
 }
 
-// y[m][perm_row[n]] = sum over splits (in order) of partial[sp][m][n].
-__global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int split,
-                                                     int M, int64_t N,
-                                                     const int32_t* __restrict__ perm_row,
-                                                     float* __restrict__ y) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// y[m][perm_row[n]] = sum over splits (in order) of partial[sp][m][n], for
+// element idx = m N + n.
+__device__ __forceinline__ void reduce_elem(const float* __restrict__ part, int split, int M,
+                                            int64_t N, const int32_t* __restrict__ perm_row,
+                                            float* __restrict__ y, int64_t idx) {
   if (idx >= (int64_t)M * N) return;
   const int64_t m = idx / N, n = idx - (idx / N) * N;
   const int64_t plane = (int64_t)M * N;
@@ -1298,6 +1306,63 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
   }
   for (; sp < split; ++sp) v += p[sp * plane];
   y[m * N + orig_row(perm_row, n, N)] = v;
+}
+
+__global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int split,
+                                                     int M, int64_t N,
+                                                     const int32_t* __restrict__ perm_row,
+                                                     float* __restrict__ y) {
+  reduce_elem(part, split, M, N, perm_row, y, (int64_t)blockIdx.x * 256 + threadIdx.x);
+}
+
+// ---- grouped calls at 2 <= M <= 16 ---------------------------------------------------
+// One gather launch (every matrix's x reordered, with fp32 group sums), one
+// decode launch whose workgroups run all matrices side by side, and one
+// reduction launch for the matrices with several K ranges.  Job j owns the
+// workgroups [wg_begin, wg_begin of j + 1) of the decode launch and
+// [red_begin, red_begin of j + 1) of the reduction (none with one K range;
+// such a job shares its begin with the next job, which the selection picks).
+struct SmallJob {
+  WeightView w;
+  const uint16_t* xr;  // reordered x [M][K] in the job's workspace
+  const float* sf;     // its fp32 group sums
+  float* part;         // fp32 partials [split][M][N] (split > 1)
+  float* y;
+  int split, kr, one;  // one: ranges of 64 block columns (one-block rings)
+  int wg_begin, red_begin;
+};
+
+struct SmallGroup {
+  SmallJob job[kGroupMax];
+  int count;
+  int M;
+};
+
+// Copy of the job owning workgroup b of the decode (or reduction) launch.
+__device__ __forceinline__ SmallJob pick_small_job(const SmallGroup& g, int b, bool reduce) {
+  SmallJob q = g.job[0];
+#pragma unroll
+  for (int k = 1; k < kGroupMax; ++k)
+    if (k < g.count && b >= (reduce ? g.job[k].red_begin : g.job[k].wg_begin)) q = g.job[k];
+  return q;
+}
+
+__global__ __launch_bounds__(512) void k_gemv16_group(SmallGroup g) {
+  const SmallJob q = pick_small_job(g, blockIdx.x, false);
+  const int direct = q.split == 1;
+  float* dst = direct ? q.y : q.part;
+  const int b = blockIdx.x - q.wg_begin;
+  // the branch is uniform over the workgroup
+  if (q.one)
+    gemv16<8, true>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+  else
+    gemv16<8, false>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+}
+
+__global__ __launch_bounds__(256) void k_gemv_reduce_group(SmallGroup g) {
+  const SmallJob q = pick_small_job(g, blockIdx.x, true);
+  reduce_elem(q.part, q.split, g.M, q.w.N, q.w.perm_row, q.y,
+              (int64_t)(blockIdx.x - q.red_begin) * 256 + threadIdx.x);
 }
 
 // Workspace layout of one call: [partials | xg | sums | counters] (M == 1)
@@ -1523,6 +1588,60 @@ hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, f
   else
     hipLaunchKernelGGL((k_gemv_m1_group<8>), dim3((unsigned)wg_total), dim3(512), lds, stream, g);
   return hipGetLastError();
+}
+
+size_t gemv_group_workspace_small(int64_t M, const WeightView* w, int count, const Options& opt) {
+  size_t total = 0;
+  const int64_t rows = group_rows(w, count);
+  for (int i = 0; i < count; ++i) total += align256(plan_gemv(M, w[i].N, w[i].K, opt, rows).workspace);
+  return total;
+}
+
+hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const WeightView* w,
+                                   float* const* y, int count, void* workspace, const Options& opt,
+                                   hipStream_t stream) {
+  if (count < 1 || count > kGroupMax || M < 2 || M > 16) return hipErrorInvalidValue;
+  SmallGroup g{};
+  g.count = count;
+  g.M = (int)M;
+  void* gather_ws[kGroupMax];
+  uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
+  int wg_total = 0, red_total = 0;
+  size_t lds = 0;
+  const int64_t rows = group_rows(w, count);
+  for (int i = 0; i < count; ++i) {
+    const GemvPlan p = plan_gemv(M, w[i].N, w[i].K, opt, rows);
+    const GemvWorkspace gw = carve(ws, p, M, w[i].N, w[i].K);
+    ws += align256(p.workspace);
+    gather_ws[i] = gw.gather;
+    SmallJob& q = g.job[i];
+    q.w = w[i];
+    q.xr = reinterpret_cast<const uint16_t*>(gw.gather);
+    q.sf = gather_sums_f32(gw.gather, M, w[i].K);
+    q.part = gw.part;
+    q.y = y[i];
+    q.split = p.split;
+    q.kr = p.kr;
+    q.one = p.kr >= kMaxCols ? 1 : 0;
+    q.wg_begin = wg_total;
+    q.red_begin = red_total;
+    wg_total += (int)(w[i].NBr * p.split);
+    if (p.split > 1) red_total += (int)((M * w[i].N + 255) / 256);
+    lds = std::max(lds, p.lds_bytes);
+  }
+  hipError_t e = launch_gather_x_group(x, M, w, gather_ws, count, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_gemv16_group, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+  e = hipGetLastError();
+  if (e == hipSuccess && red_total > 0) {
+    hipLaunchKernelGGL(k_gemv_reduce_group, dim3((unsigned)red_total), dim3(256), 0, stream, g);
+    e = hipGetLastError();
+  }
+  // the decode kernel leaves 16-bit blocks to one more pass per matrix, as
+  // in the single call
+  for (int i = 0; i < count && e == hipSuccess; ++i)
+    if (w[i].has16) e = launch_tile16(x[i], g.job[i].xr, M, w[i], y[i], stream);
+  return e;
 }
 
 hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float* y,

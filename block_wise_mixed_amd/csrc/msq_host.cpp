@@ -156,19 +156,15 @@ msq_status gemm_impl(const uint16_t* x_bf16, int64_t M, const msq_weight* w, flo
 size_t group_workspace_impl(int64_t M, const msq_weight* const* w, int count, const msq::Options& o) {
   if (!w || count < 1 || count > MSQ_GROUP_MAX || M <= 0) return 0;
   msq::WeightView v[MSQ_GROUP_MAX];
-  size_t most = 0;
   for (int i = 0; i < count; ++i) {
     if (!w[i] || check_shape(w[i]->N, w[i]->K) != MSQ_OK) return 0;
     v[i] = view_of(w[i]);
-    const size_t one = workspace_for(M, w[i]->N, w[i]->K, o);
-    most = one > most ? one : most;
   }
-  // M == 1 and M > MSQ_AUTO_GEMV_MAX_M: every matrix keeps its own workspace
-  // (one launch for all, or split-K single calls); 2 .. MSQ_AUTO_GEMV_MAX_M:
-  // the matrices run one after the other
+  // every matrix keeps its own workspace (one launch for all, or split-K
+  // single calls)
   if (M == 1) return msq::gemv_group_workspace_m1(v, count, o);
   if (M > MSQ_AUTO_GEMV_MAX_M) return msq::gemm_group_workspace_bytes(M, v, count, o);
-  return most;
+  return msq::gemv_group_workspace_small(M, v, count, o);
 }
 
 msq_status group_impl(const uint16_t* const* x_bf16, int64_t M, const msq_weight* const* w,
@@ -189,16 +185,12 @@ msq_status group_impl(const uint16_t* const* x_bf16, int64_t M, const msq_weight
   const size_t need = group_workspace_impl(M, w, count, o);
   if (need > 0 && (!workspace || !aligned(workspace, 256))) return MSQ_ERR_INVALID_ARG;
   if (workspace_bytes < need) return MSQ_ERR_BUFFER_TOO_SMALL;
-  if (M != 1 && M <= MSQ_AUTO_GEMV_MAX_M) {
-    // one matrix after the other, sharing the workspace (ordered on stream)
-    for (int i = 0; i < count; ++i) {
-      const msq_status st = gemm_impl(x_bf16[i], M, w[i], y[i], workspace, workspace_bytes, o, stream);
-      if (st != MSQ_OK) return st;
-    }
-    return MSQ_OK;
-  }
   msq::WeightView v[MSQ_GROUP_MAX];
   for (int i = 0; i < count; ++i) v[i] = view_of(w[i]);
+  if (M != 1 && M <= MSQ_AUTO_GEMV_MAX_M)
+    return msq::launch_gemv_group_small(x_bf16, M, v, y, count, workspace, o, stream) == hipSuccess
+               ? MSQ_OK
+               : MSQ_ERR_HIP;
   if (M > 1)  // the prefill GEMM multiplies 16-bit blocks itself
     return msq::launch_gemm_group(x_bf16, M, v, y, count, workspace, o, stream) == hipSuccess
                ? MSQ_OK

@@ -80,6 +80,14 @@ size_t gemv_group_workspace_m1(const WeightView* w, int count, const Options& op
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
                                 int count, void* workspace, const Options& opt,
                                 hipStream_t stream);
+// Grouped decode at 2 <= M <= 16: one gather launch, one decode launch over
+// all matrices (each planned with the group's rows), one reduction launch for
+// the matrices with several K ranges, then the 16-bit pass of each matrix
+// that has 16-bit blocks; the workspace holds each matrix's workspace in turn.
+size_t gemv_group_workspace_small(int64_t M, const WeightView* w, int count, const Options& opt);
+hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const WeightView* w,
+                                   float* const* y, int count, void* workspace, const Options& opt,
+                                   hipStream_t stream);
 
 // ---- activation gather for M > 1 (msq_gemm.hip): x_r[m][j] = x[m][perm_col[j]]
 // and the group sums of x_r split into three bf16 terms S0 + S1 + S2 (exact
@@ -95,6 +103,10 @@ size_t gather_workspace_bytes(int64_t M, int64_t K);
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
                            hipStream_t stream, bool sums_f32);
 float* gather_sums_f32(void* ws, int64_t M, int64_t K);
+// The gather of launch_gather_x (sums_f32 on) for count (1 .. 8) matrices at
+// one M in one launch; ws[i] is matrix i's gather workspace.
+hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const WeightView* w,
+                                 void* const* ws, int count, hipStream_t stream);
 
 // ---- K-split reduction (msq_gemv.hip): y[m][perm_row[n]] = sum over splits,
 // in split order, of part[sp][m][n].

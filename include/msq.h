@@ -255,25 +255,29 @@ msq_status msq_gemm_noalloc(const uint16_t *x_bf16, int64_t M, const msq_weight 
 #define MSQ_GROUP_MAX 8
 
 /* Bytes of device workspace msq_gemm_group needs for these count matrices
- * at M rows: for M == 1 and M > MSQ_AUTO_GEMV_MAX_M about the sum of the
- * single-call workspaces (all matrices are in flight together); for
- * 2 .. MSQ_AUTO_GEMV_MAX_M their maximum (the matrices run one after the
- * other).  Zero for M <= 0, count outside 1 .. MSQ_GROUP_MAX or a bad
- * shape. */
+ * at M rows: about the sum of the single-call workspaces (all matrices are
+ * in flight together).  Zero for M <= 0, count outside 1 .. MSQ_GROUP_MAX
+ * or a bad shape. */
 size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int count);
 
-/* y[i] = x[i] . W_i^T for count matrices (1 .. MSQ_GROUP_MAX), each exactly
- * as msq_gemm computes it.  For the decode step of a layer, whose q, k, v
+/* y[i] = x[i] . W_i^T for count matrices (1 .. MSQ_GROUP_MAX), each as
+ * msq_gemm computes it (at M <= MSQ_AUTO_GEMV_MAX_M the K split that fills
+ * the GPU is chosen for the whole group, so results can differ from single
+ * calls in fp32 summation order; with msq_options.gemv_split set they are
+ * the same bit for bit).  For the decode step of a layer, whose q, k, v
  * projections (and gate, up) read the same activation: at M == 1 one
  * decode launch covers all matrices, their workgroups running side by side
  * (matrices whose K is split into several ranges add one activation-prep
  * launch for all of them; the others reorder x inside their workgroups) ("TileQuant" abstract: local accumulation
  * to reduce memory traffic; the grouping itself is this library's).  At
- * M > 16, when the matrices' tiles fill the GPU (prefill), one
- * activation-gather launch and one GEMM launch cover all matrices, the tiles
- * of the smaller ones filling the compute units the larger ones leave idle;
- * with fewer tiles, and at M in 2 .. 16, the matrices are computed one after
- * the other as by msq_gemm.  x,
+ * M in 2 .. MSQ_AUTO_GEMV_MAX_M: one activation-gather launch, one decode
+ * launch and (for matrices with several K ranges) one reduction launch
+ * cover all matrices.  At M > MSQ_AUTO_GEMV_MAX_M, when the matrices' tiles
+ * fill the GPU (prefill), one activation-gather launch and one GEMM launch
+ * cover all matrices, the tiles of the smaller ones filling the compute
+ * units the larger ones leave idle; with fewer tiles the matrices are
+ * computed one after the other as by msq_gemm.  Matrices with 16-bit
+ * blocks add their 16-bit pass after the decode launches.  x,
  * w and y are host arrays of count device pointers / descriptors; x[i] may
  * repeat the same activation.  workspace must hold
  * msq_gemm_group_workspace_bytes(M, w, count) bytes (256-byte aligned).

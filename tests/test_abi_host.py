@@ -219,10 +219,12 @@ def test_group_workspace_sizes(lib):
     prep = sum(2 * w.K + 84 * (w.K // 128) for w in ws_list)
     g1 = lib.msq_gemm_group_workspace_bytes(1, arr, 3)
     assert prep <= g1 <= sum(singles) + 3 * 256
-    # M in 2 .. 16: the matrices run one after the other with the automatic kernel
-    # choice, so the largest of those workspaces suffices
+    # M in 2 .. 16: one gather, decode and reduction launch for all, each matrix
+    # with its own gathered activation; the group's K splits are no more than a
+    # single call's
     mid = [lib.msq_gemm_workspace_bytes_ex(16, w.N, w.K, _opt(0)) for w in ws_list]
-    assert lib.msq_gemm_group_workspace_bytes(16, arr, 3) == max(mid)
+    g16 = lib.msq_gemm_group_workspace_bytes(16, arr, 3)
+    assert sum(16 * w.K * 2 for w in ws_list) <= g16 <= sum(mid) + 3 * 256
     # prefill: one launch for all, each matrix with its own gathered activation
     big = [lib.msq_gemm_workspace_bytes(2048, w.N, w.K) for w in ws_list]
     g = lib.msq_gemm_group_workspace_bytes(2048, arr, 3)

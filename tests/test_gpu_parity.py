@@ -369,6 +369,50 @@ def test_group_half_rows_match_single_calls(msq, group_cases):
             check_y(msq, pw, c, ref, 1, x=x)
 
 
+def _check_given_y(y, case, ref, x):
+    """y (a device result of x . W^T) against the oracle within tolerance."""
+    y = y.cpu().numpy().astype(np.float64)
+    yref = oracle.reference_gemm(x, ref, case.perm_row, case.perm_col)
+    assert np.isfinite(y).all()
+    scale = np.abs(yref).max()
+    err = float(np.abs(y - yref).max() / scale) if scale > 0 else float(np.abs(y).max())
+    _log(f"   {case.name} rel err {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("M", [2, 16])
+def test_group_small_m_one_launch(msq, M):
+    """At 2 <= M <= 16 a group runs as one gather, one decode and (with several K
+    ranges) one reduction launch.  Two 8192-wide matrices and a 1024-wide one: with
+    one K range forced (ranges of 64 block columns, the one-block ring variant, no
+    reduction) and with three (the two-block variant and the reduction; ragged on
+    the 1024-wide matrix) every output equals its single call bit for bit, twice in
+    a row; with the automatic choice (one K split chosen for the whole group) every
+    output matches the oracle."""
+    cases = []
+    for N, K, seed, dist in ((192, 8192, 67, SMALL_DIST), (128, 8192, 68, {2: .5, 3: .3, 8: .2}),
+                             (64, 1024, 69, {1: .5, 4: .5})):
+        c = synth.random_case(N, K, seed, dist=dist)
+        cases.append((c,) + check_pack(msq, c))
+    pws = [pw for _, pw, _ in cases]
+    x_wide = cases[0][0].x(M)
+    x_narrow = cases[2][0].x(M)
+    xs = [x_wide, x_wide, x_narrow]
+    for opt in ({"gemv_split": 1}, {"gemv_split": 3}):
+        _log(f"small-M group M={M} options={opt}")
+        for rep in range(2):
+            outs = msq.gemm_group(xs, pws, options=opt)
+            singles = [msq.gemm(x, pw, options=opt) for x, pw in zip(xs, pws)]
+            torch.cuda.synchronize()
+            for (c, _, _), y, single in zip(cases, outs, singles):
+                assert torch.equal(y, single), c.name
+    _log(f"small-M group M={M} automatic")
+    outs = msq.gemm_group(xs, pws)
+    torch.cuda.synchronize()
+    for (c, pw, ref), x, y in zip(cases, xs, outs):
+        _check_given_y(y, c, ref, x)
+
+
 def test_group_prefill_one_launch(msq):
     """Two 4096 x 1024 matrices at M = 1024 have enough tiles for the one grouped GEMM
     launch (smaller groups run as split-K single calls): each output equals its single
@@ -421,18 +465,19 @@ def test_group_sizes(msq, group_cases, M):
         msq.gemm_group([x] * (msq.GROUP_MAX + 1), [pw] * (msq.GROUP_MAX + 1))
 
 
-@pytest.mark.parametrize("split", ["auto", "1"])
-def test_group_graph_replay_matches_eager(msq, group_cases, split):
+@pytest.mark.parametrize("M,split", [(1, "auto"), (1, "1"), (16, "auto"), (16, "1")])
+def test_group_graph_replay_matches_eager(msq, group_cases, M, split):
     """bench.py captures grouped decode calls in HIP graphs: every replay, with eager
-    work in between on the same workspace, must equal the eager result bit for bit;
-    automatic (17 block rows: half block rows) and with one K range forced (whole
-    block rows; the workgroups reorder x themselves)."""
+    work in between on the same workspace, must equal the eager result bit for bit.
+    M = 1 automatic (17 block rows: half block rows) and with one K range forced
+    (whole block rows; the workgroups reorder x themselves); M = 16 automatic (K
+    ranges and the reduction launch) and with one K range."""
     opt = None if split == "auto" else {"gemv_split": int(split)}
     pws = [pw for _, pw, _ in group_cases]
-    x_shared = torch.from_numpy(group_cases[0][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
-    x_last = torch.from_numpy(group_cases[3][0].x(1).view(np.int16)).view(torch.bfloat16).cuda()
+    x_shared = _bf16_cuda(group_cases[0][0].x(M))
+    x_last = _bf16_cuda(group_cases[3][0].x(M))
     xs = [x_shared, x_shared, x_shared, x_last]
-    ws = torch.empty(max(msq.group_workspace_bytes(1, pws, options=opt), 256), dtype=torch.uint8,
+    ws = torch.empty(max(msq.group_workspace_bytes(M, pws, options=opt), 256), dtype=torch.uint8,
                      device="cuda")
     eager = [y.clone() for y in msq.gemm_group(xs, pws, options=opt)]
     outs = [torch.empty_like(y) for y in eager]

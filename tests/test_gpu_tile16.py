@@ -55,7 +55,7 @@ def test_integer_lattice_exact(msq):
 def test_group_matches_single(msq):
     cases = [synth.random_case(256, 2048, 85 + i, dist=d) for i, d in enumerate((MIX16, TQ))]
     packed = [check_pack(msq, c)[0] for c in cases]
-    for M in (1, 200):
+    for M in (1, 4, 200):  # M = 4: the grouped decode launches, then each 16-bit pass
         xs = [_bf16_cuda(cases[0].x(M))] * 2
         outs = msq.gemm_group(xs, packed)
         for x, pw, y in zip(xs, packed, outs):
