@@ -1259,25 +1259,47 @@ template <bool kLds>
 __global__ __launch_bounds__(kReduceRowThreads) void k_gemv_reduce_rows(
     const float* __restrict__ part, int split, int M, int64_t N, const int32_t* __restrict__ perm_row,
     float* __restrict__ y) {
+  // kU columns per thread and pass, all their partial loads issued before any
+  // is added (a pass is one memory round trip however few rows there are)
+  constexpr int kU = 4;
   const int64_t m = blockIdx.x;
   const int64_t plane = (int64_t)M * N;
   float* lrow = reinterpret_cast<float*>(smem);
-  for (int64_t n = threadIdx.x; n < N; n += kReduceRowThreads) {
-    const float* p = part + m * N + n;
-    float v = 0.f;
+  const float* prow = part + m * N;
+  for (int64_t n0 = threadIdx.x; n0 < N; n0 += kU * kReduceRowThreads) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = 0.f;
     int sp = 0;
-    for (; sp + 8 <= split; sp += 8) {
-      float t[8];
+    for (; sp + 4 <= split; sp += 4) {
+      float t[kU][4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = p[(sp + k) * plane];
+      for (int u = 0; u < kU; ++u) {
+        const int64_t n = min(n0 + u * kReduceRowThreads, N - 1);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v += t[k];
+        for (int k = 0; k < 4; ++k) t[u][k] = prow[(sp + k) * plane + n];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[u] += t[u][k];
     }
-    for (; sp < split; ++sp) v += p[sp * plane];
-    if constexpr (kLds)
-      lrow[orig_row(perm_row, n, N)] = v;
-    else
-      y[m * N + orig_row(perm_row, n, N)] = v;
+    for (; sp < split; ++sp) {
+      float t[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) t[u] = prow[sp * plane + min(n0 + u * kReduceRowThreads, N - 1)];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) v[u] += t[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t n = n0 + u * kReduceRowThreads;
+      if (n >= N) break;
+      if constexpr (kLds)
+        lrow[orig_row(perm_row, n, N)] = v[u];
+      else
+        y[m * N + orig_row(perm_row, n, N)] = v[u];
+    }
   }
   if constexpr (kLds) {
     __syncthreads();
@@ -1700,11 +1722,12 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
 
 hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t N,
                                const int32_t* perm_row, float* y, hipStream_t stream) {
-  if (M >= 256) {
-    // one workgroup per row (enough rows to fill the GPU): every 64-byte line
-    // of the row is completed by one workgroup while it sits in L2
-    // (workgroups sharing a row would each leave it partly written, and
-    // partial lines reach HBM many times over)
+  if (M >= 128) {
+    // one workgroup per row: every 64-byte line of the row is completed by
+    // one workgroup while it sits in L2 (workgroups sharing a row would each
+    // leave it partly written, and partial lines reach HBM many times over);
+    // below 128 rows too few workgroups for the GPU (measured slower at
+    // M = 17 .. 64, faster at 128 and 200)
     if (N <= kReduceRowMaxLdsN)
       hipLaunchKernelGGL(k_gemv_reduce_rows<true>, dim3((unsigned)M), dim3(kReduceRowThreads),
                          (size_t)N * 4, stream, part, split, (int)M, N, perm_row, y);

@@ -540,6 +540,18 @@ def test_prefill_wide_n_scatters_directly(msq):
         assert torch.equal(y, single)
 
 
+def test_split_reduce_rows(msq):
+    """K-split partials summed by one workgroup per row (M >= 128): N <= 32768 permutes
+    the row through LDS, N > 32768 stores each sum at its original column; splits 2
+    and 3 (the second a ragged batch of the four-split unroll) against the oracle."""
+    for N, splits in ((4096, (2, 3)), (32832, (2,))):
+        c = synth.random_case(N, 2048 if N > 32768 else 4096, 94, dist=SMALL_DIST)
+        pw, ref = check_pack(msq, c)
+        x = c.x(130)
+        for sp in splits:
+            check_y(msq, pw, c, ref, 130, kernel="gemm", x=x, options={"gemm_split": sp})
+
+
 @pytest.mark.parametrize("M,kernel", [(1, "auto"), (2, "auto"), (2, "gemm"), (130, "auto")])
 def test_long_k_unstaged_gather(msq, M, kernel):
     """K = 32896 (> 32768): the activation gather reads x from global memory instead of
