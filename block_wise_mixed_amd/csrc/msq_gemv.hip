@@ -13,14 +13,15 @@
 //     same-bitwidth blocks.
 //  2. The activations reordered through perm_col (the activation reordering
 //     of the "SFMP" abstract) and their per-group sums, used to fold the zero
-//     point, come from the gather kernel (k_gemv: staged in LDS slice by
-//     slice; k_gemv16: read straight from L2 with each block) or, at M == 1,
-//     from the workgroup's own reordering of x in LDS (or the prep kernel).
+//     point, come from the gather kernel (k_gemv16: read straight from L2
+//     with each block) or, at M == 1, from the workgroup's own reordering of
+//     x in LDS (or the prep kernel).
 //  3. Each wavefront walks its runs.  Inside a run the bitwidth is a
 //     compile-time constant, so the loads of the next blocks are issued while
 //     the current block is unpacked and multiplied, with static wait counts
 //     (register rings).  Each 16x32 fragment is unpacked into exact bf16
-//     operands and fed to v_mfma_f32_16x16x32_bf16 (M padded to 16), then
+//     operands and fed to v_mfma_f32_16x16x32_bf16 (M padded to a multiple
+//     of 16, one product per 16-row m tile), then
 //     scale and zero point are folded per row:
 //         y[row] += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
 //  4. The wavefronts reduce through LDS in a fixed order.  One K split writes
@@ -33,8 +34,8 @@
 // corrections, an unpack that avoids most shifts, scales and zero points
 // staged in LDS, 2 to 4 KiB of codes in flight per wavefront; half block
 // rows of 32 rows for small launches instead of a K split), k_gemv16
-// (2 <= M <= 16), k_gemv (M <= 64 when the GEMV is forced), their group
-// variants, and the split reductions.
+// (2 <= M <= 64, one to four m tiles), their group variants, and the split
+// reductions.
 //
 // Per-block precision and block layout: "ScaleBITS" summary page, section
 // Approach; RTN-g128 dequantization s * (q - z): section Limitations.
@@ -57,7 +58,7 @@ namespace {
 extern __shared__ __align__(16) unsigned char smem[];
 
 constexpr int kMaxCols = 64;  // block columns per workgroup: one wave ballot
-constexpr size_t kLdsBudget = 64 * 1024;
+constexpr int kSmallMaxM = 64;  // k_gemv16 (A operands from the reordered x) up to this M
 
 __device__ __forceinline__ float bf16f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
@@ -76,11 +77,6 @@ struct Ctx {
   const float* scale;
   const uint8_t* zero;
   int64_t rowbase;       // r * NBc + c0: block index of the range's first column
-  const uint16_t* xs;    // LDS x slice [M][xs_stride]
-  const float* xsum;     // LDS group sums [M][kmax]
-  int xs_stride;         // bf16 elements per LDS row
-  int kmax;              // block columns per workgroup (row length of xsum)
-  int M;
   uint32_t sums_off;     // M == 1: LDS byte offset of the k-step sums [kmax][4] f32
   uint32_t a_lane;       // M == 1: LDS byte offset of this lane's A operand in column 0
   uint32_t zero_off;     // M == 1: LDS byte offset of the zero area (A operand of dead lanes)
@@ -93,35 +89,25 @@ __device__ __forceinline__ const uint8_t* run_base(const Ctx& cx, uint32_t off_k
   return cx.codes + (int64_t)off_kib * 1024 + 16 * (threadIdx.x & 63);
 }
 
-// Per-block operands that live in registers while the block is in flight.
+// Per-block operands that live in registers while the block is in flight
+// (M == 1: the codes; the workgroup stages the scales and zero points of its
+// range in LDS at start-up).
 template <int B>
 struct BlockRegs {
   uint4 ch[B];
-  float s;     // scale of row `lane`
-  uint32_t z;  // zero point of row `lane`
 };
 
 // Issue the loads of one block: its b chunks at `base` (this lane's 16 bytes
-// of the block's first chunk) and the scale / zero point of row `lane`.
-// The block index passes through an empty asm so that the compiler cannot
-// tell two issues of the same block apart (the register rings repeat a
-// run's last block past its end): merging such loads would tie the ring's
-// register sets together and add waits.
-// With kScaleZero false (M == 1) only the codes are loaded: the workgroup
-// stages the scales and zero points of its range in LDS at start-up.
-template <int B, bool kScaleZero = true>
-__device__ __forceinline__ void issue_block(const Ctx& cx, const uint8_t* base, int cl,
-                                            BlockRegs<B>& br) {
-  const int lane = threadIdx.x & 63;
+// of the block's first chunk).  The block index passes through an empty asm
+// so that the compiler cannot tell two issues of the same block apart (the
+// register rings repeat a run's last block past its end): merging such loads
+// would tie the ring's register sets together and add waits.
+template <int B>
+__device__ __forceinline__ void issue_block(const uint8_t* base, int cl, BlockRegs<B>& br) {
   cl = __builtin_amdgcn_readfirstlane(cl);
   asm("" : "+s"(cl));
-  const int64_t blk = cx.rowbase + cl;
 #pragma unroll
   for (int t = 0; t < B; ++t) br.ch[t] = *reinterpret_cast<const uint4*>(base + 1024 * t);
-  if constexpr (kScaleZero) {
-    br.s = cx.scale[blk * kBlockRows + lane];
-    br.z = cx.zero[blk * kBlockRows + lane];
-  }
 }
 
 // The wavefront's share of the range's blocks: per bitwidth k, the columns
@@ -165,19 +151,13 @@ __device__ __forceinline__ WaveRuns wave_runs(int bl, int wave, const int (&wt)[
   return wr;
 }
 
-// Piece weights: packed size (KiB per block) for the general path; for
-// M == 1, where a block's unpack and matrix instructions take about as long
-// as its loads, the measured per-block cost of a wavefront in units of
-// about 0.1 us (1- and 2-bit blocks alike, 3- and 4-bit alike, 8-bit twice
-// those) so that the wavefronts of a workgroup finish together.
-constexpr int kWeightBytes[5] = {1, 2, 3, 4, 8};
+// Piece weights: where a block's unpack and matrix instructions take about
+// as long as its loads, the measured per-block cost of a wavefront in units
+// of about 0.1 us (1- and 2-bit blocks alike, 3- and 4-bit alike, 8-bit
+// twice those) so that the wavefronts of a workgroup finish together.
 constexpr int kWeightCostM1[5] = {4, 4, 9, 9, 17};
 
-// ======================================================================================
-// General M (2 .. 64)
-// ======================================================================================
-
-// One block: unpack + matrix-core product into acc[mt][rt].
+// One block: unpack + matrix-core product into acc[mt][rt] (M > 1).
 template <int B, int MT>
 __device__ __forceinline__ void block_product(const uint4 (&ch)[B], const bf16x8 (&A)[MT][4],
                                               f32x4 (&acc)[MT][4]) {
@@ -204,62 +184,14 @@ __device__ __forceinline__ void block_product(const uint4 (&ch)[B], const bf16x8
   }(std::make_integer_sequence<int, 16>{});
 }
 
-// A operands of block column cl: x rows 16*mt + (l & 15), columns 32*kt + 8*(l >> 4) .. +7.
-template <int MT>
-__device__ __forceinline__ void load_a(const Ctx& cx, int cl, bf16x8 (&A)[MT][4]) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + (lane & 15);
-    const bool live = m < cx.M;
-    const uint16_t* row = cx.xs + (size_t)m * cx.xs_stride + cl * kBlockCols + 8 * (lane >> 4);
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (live) v = *reinterpret_cast<const uint4*>(row + 32 * kt);
-      A[mt][kt] = as_bf16x8(v);
-    }
-  }
-}
-
-template <int B, int MT>
-__device__ __forceinline__ void consume_block(const Ctx& cx, int cl, const BlockRegs<B>& br,
-                                              f32x4 (&yacc)[MT][4]) {
-  const int lane = threadIdx.x & 63;
-  bf16x8 A[MT][4];
-  load_a<MT>(cx, cl, A);
-  f32x4 acc[MT][4];
-  block_product<B, MT>(br.ch, A, acc);
-  constexpr float bias = (float)unpack_bias(B);
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int src = 16 * rt + (lane & 15);
-    const float s = __shfl(br.s, src, 64);
-    const float zz = bias + (float)__shfl((int)br.z, src, 64);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * (lane >> 4) + i;
-        const float sx = m < cx.M ? cx.xsum[m * cx.kmax + cl] : 0.f;
-        yacc[mt][rt][i] += s * (acc[mt][rt][i] - zz * sx);
-      }
-  }
-}
-
-// Blocks per register ring of a B-bit run: (depth - 1) * B KiB of codes stay
-// in flight while one block is consumed.  Thousands of wavefronts share
-// HBM, so shallow rings already keep more in flight than it needs; deeper
-// ones only lengthen the queues that every workgroup's start-up waits in
-// (M == 1 on a 70B layer: 4/2/2/2/2 blocks for 1/2/3/4/8 bits measured ~6%
-// faster than 8/4/3/3/2).  More rows of M keep more accumulators live, so
-// their rings are shallower still.
-template <int B, int MT = 1>
-constexpr int ring_depth() {
-  if constexpr (MT == 1) return B == 1 ? 4 : 2;
-  else if constexpr (MT == 2) return B <= 4 ? 2 : 1;
-  else return B <= 2 ? 2 : 1;
-}
+// Blocks per register ring of a B-bit run at M == 1: (depth - 1) * B KiB of
+// codes stay in flight while one block is consumed.  Thousands of
+// wavefronts share HBM, so shallow rings already keep more in flight than it
+// needs; deeper ones only lengthen the queues that every workgroup's
+// start-up waits in (M == 1 on a 70B layer: 4/2/2/2/2 blocks for 1/2/3/4/8
+// bits measured ~6% faster than 8/4/3/3/2).
+template <int B>
+constexpr int ring_depth() { return B == 1 ? 4 : 2; }
 
 // A run of n >= 1 blocks of bitwidth B whose columns are the lowest n set
 // bits of `cols`, starting at `base` (this lane's 16 bytes of the run's first
@@ -275,8 +207,7 @@ constexpr int ring_depth() {
 // instead of a KiB; no branch, so the loads keep their form).  (An exit from the middle of the
 // unrolled body leaves structurized control-flow paths on which the
 // compiler cannot bound the outstanding loads, and it then waits for all.)
-// kScaleZero: the ring also loads each block's scales and zero points (two
-// more loads per block).  consume(column, registers) uses a block;
+// consume(column, registers) uses a block;
 // after_issue(integral_constant<loads issued>) runs once after the first D
 // blocks are issued.
 // Regs: the register set of one block; issue(address, column, regs) issues
@@ -331,217 +262,101 @@ __device__ __forceinline__ void ring_run_t(const uint8_t* codes, const uint8_t* 
   } while (i0 < n);
 }
 
-template <int B, int D, bool kScaleZero, typename Consume, typename AfterIssue>
+template <int B, int D, typename Consume, typename AfterIssue>
 __device__ __forceinline__ void ring_run(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
                                          Consume&& consume, AfterIssue&& after_issue) {
-  ring_run_t<B, D, B + (kScaleZero ? 2 : 0), BlockRegs<B>>(
+  ring_run_t<B, D, B, BlockRegs<B>>(
       cx.codes, base, cols, n,
       [&](const uint8_t* addr, int cl, BlockRegs<B>& br) __attribute__((always_inline)) {
-        issue_block<B, kScaleZero>(cx, addr, cl, br);
+        issue_block<B>(addr, cl, br);
       },
       consume, after_issue);
 }
 
-// A run of n blocks of bitwidth B whose columns are the lowest n set bits of
-// `cols`.  Blocks of one bitwidth in one block row are consecutive in packed
-// order, so block i of the run starts b * i KiB after the first, at `base`
-// (this lane's 16 bytes of the run's first chunk).
-template <int B, int MT>
-__device__ __forceinline__ void run_blocks(const Ctx& cx, const uint8_t* base, uint64_t cols, int n,
-                                           f32x4 (&yacc)[MT][4]) {
-  ring_run<B, ring_depth<B, MT>(), true>(
-      cx, base, cols, n,
-      [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
-        consume_block<B, MT>(cx, cl, br, yacc);
-      },
-      [](auto) __attribute__((always_inline)) {});
-}
-
-// The workgroup's activation slice: rows 0 .. M-1 of the reordered x_r
-// (written once per call by the gather kernel) for block columns c0 ..
-// c0 + ncl - 1, copied into LDS with 16-byte loads, and the group sums
-// rebuilt from their three bf16 terms (S0 + S1 + S2 is exact in fp32).
-// The loads of kBatch items are issued before any store, and every thread
-// stores at its clamped item (threads past the end rewrite the last item
-// with the value they loaded from it), so no store is conditional.
-__device__ __forceinline__ void stage_x(const uint16_t* __restrict__ xr,
-                                        const uint16_t* __restrict__ sxs, int M, int64_t K,
-                                        int64_t Gp, int c0, int ncl, uint16_t* xs, int xs_stride,
-                                        float* xsum, int kmax, int nthreads) {
-  constexpr int kBatch = 4;
-  const int chunks = ncl * 16;
-  const int items = M * chunks;
-  for (int base = threadIdx.x; base < items; base += kBatch * nthreads) {
-    uint4 v[kBatch];
-    int dst[kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int it = min(base + u * nthreads, items - 1);
-      const int m = it / chunks, q = it - (it / chunks) * chunks;
-      v[u] = reinterpret_cast<const uint4*>(xr + (int64_t)m * K + (int64_t)c0 * kBlockCols)[q];
-      dst[u] = m * xs_stride + 8 * q;
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) *reinterpret_cast<uint4*>(xs + dst[u]) = v[u];
-  }
-  const int64_t plane = (int64_t)M * Gp;
-  for (int it = threadIdx.x; it < M * ncl; it += nthreads) {
-    const int m = it / ncl, c = it - (it / ncl) * ncl;
-    const uint16_t* s = sxs + (int64_t)m * Gp + c0 + c;
-    xsum[m * kmax + c] = (bf16f(s[0]) + bf16f(s[plane])) + bf16f(s[2 * plane]);
-  }
-}
-
-template <int NW, int MT>
-__global__ __launch_bounds__(NW * 64) void k_gemv(const uint16_t* __restrict__ xr,
-                                                  const uint16_t* __restrict__ sxs, int M,
-                                                  WeightView w, int split, int kmax, int xs_stride,
-                                                  float* __restrict__ out, int direct) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = blockIdx.x / split, sp = blockIdx.x - (blockIdx.x / split) * split;
-  const int c0 = sp * kmax;
-  const int ncl = min(w.NBc, c0 + kmax) - c0;
-  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);
-  float* xsum = reinterpret_cast<float*>(smem + (size_t)M * xs_stride * 2);
-
-  // 1. this wavefront's share of the range's blocks, in packed order
-  const int64_t rowbase = (int64_t)r * w.NBc + c0;
-  const int bl = lane < ncl ? (int)w.bits[rowbase + lane] : 0;
-  const uint32_t ol = lane < ncl ? w.block_offset[rowbase + lane] : 0u;
-  const WaveRuns wr = wave_runs<NW>(bl, wave, kWeightBytes);
-
-  // 2. activation slice
-  Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, xs, xsum, xs_stride, kmax, M, 0u, 0u,
-         0u, 0u};
-  stage_x(xr, sxs, M, w.K, padded_groups(w.NBc), c0, ncl, xs, xs_stride, xsum, kmax, NW * 64);
-  __syncthreads();
-
-  f32x4 yacc[MT][4];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) yacc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // 3. runs
-  uint32_t off[5];
-#pragma unroll
-  for (int k = 0; k < 5; ++k)
-    off[k] = wr.n[k] > 0 ? __builtin_amdgcn_readlane(ol, __builtin_ctzll(wr.cols[k])) : 0u;
-  if (wr.n[0] > 0) run_blocks<1, MT>(cx, run_base(cx, off[0]), wr.cols[0], wr.n[0], yacc);
-  if (wr.n[1] > 0) run_blocks<2, MT>(cx, run_base(cx, off[1]), wr.cols[1], wr.n[1], yacc);
-  if (wr.n[2] > 0) run_blocks<3, MT>(cx, run_base(cx, off[2]), wr.cols[2], wr.n[2], yacc);
-  if (wr.n[3] > 0) run_blocks<4, MT>(cx, run_base(cx, off[3]), wr.cols[3], wr.n[3], yacc);
-  if (wr.n[4] > 0) run_blocks<8, MT>(cx, run_base(cx, off[4]), wr.cols[4], wr.n[4], yacc);
-
-  // 4. reduce the wavefronts in a fixed order and write out
-  __syncthreads();  // LDS is reused below
-  float* red = reinterpret_cast<float*>(smem);
-  const int plane = M * kBlockRows;
-  if (wave > 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * mt + 4 * (lane >> 4) + i;
-          if (m < M) red[(wave - 1) * plane + m * kBlockRows + 16 * rt + (lane & 15)] = yacc[mt][rt][i];
-        }
-  }
-  __syncthreads();
-  if (wave == 0) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int m = 16 * mt + 4 * (lane >> 4) + i;
-          if (m >= M) continue;
-          const int n = 16 * rt + (lane & 15);
-          float v = yacc[mt][rt][i];
-#pragma unroll
-          for (int k = 0; k < NW - 1; ++k) v += red[k * plane + m * kBlockRows + n];
-          const int64_t row = (int64_t)r * kBlockRows + n;
-          if (direct) {
-            out[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
-          } else {
-            out[((int64_t)sp * M + m) * w.N + row] = v;
-          }
-        }
-  }
-}
-
 // ======================================================================================
-// 2 <= M <= 16: A operands straight from the reordered x
+// 2 <= M <= 64: A operands straight from the reordered x
 // ======================================================================================
 //
 // The activation gather leaves x_r [M][K] (reordered through perm_col) and
-// the fp32 group sums [group][16] in the workspace, a few hundred KB that
-// stay in L2.  Each block's register set holds, besides its b code chunks,
-// the block column's four A fragments (x_r rows lane & 15, columns
+// the fp32 group sums [group][16 MT] in the workspace (MT = M / 16 rounded
+// up: the 16-row m tiles), a few hundred KB that stay in L2.  Each block's
+// register set holds, besides its b code chunks, the block column's four A
+// fragments per m tile (x_r rows 16 mt + (lane & 15), columns
 // 32 kt + 8 (lane >> 4) .. +7; rows past M repeat row M - 1 and their
-// outputs are never stored), the group sums of rows 4 (lane >> 4) .. +3 and
-// the scale and zero point of row `lane`, all issued together one ring
-// stage ahead.  No slice of x is staged in LDS, so a workgroup takes a
-// whole block row (or a range of 64 block columns) like the M == 1 kernel
-// and there is no start-up barrier; LDS only holds the final sum over the
-// wavefronts.
+// outputs are never stored), the group sums of rows 16 mt + 4 (lane >> 4)
+// .. +3 and the scale and zero point of row `lane`, all issued together one
+// ring stage ahead.  Each B fragment is unpacked once for all m tiles.  No
+// slice of x is staged in LDS, so a workgroup takes a whole block row (or a
+// range of 64 block columns) like the M == 1 kernel and there is no start-up
+// barrier; LDS only holds the final sum over the wavefronts, one m tile at a
+// time.
 
-template <int B>
+template <int B, int MT>
 struct RegsX {
   uint4 ch[B];
-  uint4 a[4];
-  float4 sx;
+  uint4 a[MT][4];
+  float4 sx[MT];
   float s;
   uint32_t z;
 };
 
+template <int MT>
 struct CtxX {
   const uint8_t* codes;
   const float* scale;
   const uint8_t* zero;
-  int64_t rowbase;      // block index of the range's first column
-  const uint16_t* xa;   // this lane's A row at the range's first column
-  const float* sxa;     // this lane's four group sums at the range's first column
+  int64_t rowbase;         // block index of the range's first column
+  const uint16_t* xa[MT];  // this lane's A row of each m tile at the range's first column
+  const float* sxa;        // this lane's four group sums (m tile 0) at the range's first column
 };
 
-template <int B>
-__device__ __forceinline__ void issue_x(const CtxX& cx, const uint8_t* base, int cl, RegsX<B>& br) {
+template <int B, int MT>
+__device__ __forceinline__ void issue_x(const CtxX<MT>& cx, const uint8_t* base, int cl,
+                                        RegsX<B, MT>& br) {
   const int lane = threadIdx.x & 63;
   cl = __builtin_amdgcn_readfirstlane(cl);
   asm("" : "+s"(cl));
   const int64_t blk = cx.rowbase + cl;
 #pragma unroll
   for (int t = 0; t < B; ++t) br.ch[t] = *reinterpret_cast<const uint4*>(base + 1024 * t);
-  const uint16_t* xa = cx.xa + (int64_t)cl * kBlockCols;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) br.a[kt] = *reinterpret_cast<const uint4*>(xa + 32 * kt);
-  br.sx = *reinterpret_cast<const float4*>(cx.sxa + (int64_t)cl * 16);
+  for (int mt = 0; mt < MT; ++mt) {
+    const uint16_t* xa = cx.xa[mt] + (int64_t)cl * kBlockCols;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) br.a[mt][kt] = *reinterpret_cast<const uint4*>(xa + 32 * kt);
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+    br.sx[mt] = *reinterpret_cast<const float4*>(cx.sxa + (int64_t)cl * 16 * MT + 16 * mt);
   br.s = cx.scale[blk * kBlockRows + lane];
   br.z = cx.zero[blk * kBlockRows + lane];
 }
 
-// One block into yacc[rt] (rows 4 (lane >> 4) + i, output 16 rt + (lane & 15)):
+// One block into yacc[mt][rt] (rows 16 mt + 4 (lane >> 4) + i, output
+// 16 rt + (lane & 15)):
 //   yacc += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
-template <int B>
-__device__ __forceinline__ void consume_x(const RegsX<B>& br, f32x4 (&yacc)[4]) {
+template <int B, int MT>
+__device__ __forceinline__ void consume_x(const RegsX<B, MT>& br, f32x4 (&yacc)[MT][4]) {
   const int lane = threadIdx.x & 63;
-  bf16x8 A[1][4];
+  bf16x8 A[MT][4];
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) A[0][kt] = as_bf16x8(br.a[kt]);
-  f32x4 acc[1][4];
-  block_product<B, 1>(br.ch, A, acc);
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) A[mt][kt] = as_bf16x8(br.a[mt][kt]);
+  f32x4 acc[MT][4];
+  block_product<B, MT>(br.ch, A, acc);
   constexpr float bias = (float)unpack_bias(B);
-  const float sx[4] = {br.sx.x, br.sx.y, br.sx.z, br.sx.w};
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
     const int src = 16 * rt + (lane & 15);
     const float s = __shfl(br.s, src, 64);
     const float zz = bias + (float)__shfl((int)br.z, src, 64);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) yacc[rt][i] += s * (acc[0][rt][i] - zz * sx[i]);
+    for (int mt = 0; mt < MT; ++mt) {
+      const float sx[4] = {br.sx[mt].x, br.sx[mt].y, br.sx[mt].z, br.sx[mt].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) yacc[mt][rt][i] += s * (acc[mt][rt][i] - zz * sx[i]);
+    }
   }
 }
 
@@ -551,24 +366,29 @@ __device__ __forceinline__ void consume_x(const RegsX<B>& br, f32x4 (&yacc)[4]) 
 // one block for every bitwidth, for ranges of 64 block columns (eight or more
 // blocks per wavefront), where fewer loads in flight measured faster
 // (Llama-3-70B linears at M = 16: 4-6%); with four blocks per wavefront two
-// measured faster.  Deeper rings were slower at every shape tried.
-template <int B, bool ONE>
-constexpr int ring_depth_x() { return ONE ? 1 : (B >= 8 ? 1 : 2); }
+// measured faster.  Deeper rings were slower at every shape tried.  Several
+// m tiles (M > 16): one block (their A fragments and accumulators fill the
+// registers).
+template <int B, bool ONE, int MT>
+constexpr int ring_depth_x() { return (ONE || MT > 1) ? 1 : (B >= 8 ? 1 : 2); }
 
-template <int B, bool ONE>
-__device__ __forceinline__ void run_x(const CtxX& cx, const uint8_t* base, uint64_t cols, int n,
-                                      f32x4 (&yacc)[4]) {
-  ring_run_t<B, ring_depth_x<B, ONE>(), B + 7, RegsX<B>>(
+template <int B, bool ONE, int MT>
+__device__ __forceinline__ void run_x(const CtxX<MT>& cx, const uint8_t* base, uint64_t cols,
+                                      int n, f32x4 (&yacc)[MT][4]) {
+  ring_run_t<B, ring_depth_x<B, ONE, MT>(), B + 5 * MT + 2, RegsX<B, MT>>(
       cx.codes, base, cols, n,
-      [&](const uint8_t* addr, int cl, RegsX<B>& br) __attribute__((always_inline)) {
-        issue_x<B>(cx, addr, cl, br);
+      [&](const uint8_t* addr, int cl, RegsX<B, MT>& br) __attribute__((always_inline)) {
+        issue_x<B, MT>(cx, addr, cl, br);
       },
-      [&](int, const RegsX<B>& br) __attribute__((always_inline)) { consume_x<B>(br, yacc); },
+      [&](int, const RegsX<B, MT>& br) __attribute__((always_inline)) {
+        consume_x<B, MT>(br, yacc);
+      },
       [](auto) __attribute__((always_inline)) {});
 }
 
-// Workgroup `blk` (block row blk / split, K range blk % split) of one matrix.
-template <int NW, bool ONE>
+// Workgroup `blk` (block row blk / split, K range blk % split) of one matrix,
+// M in 16 (MT - 1) + 1 .. 16 MT.
+template <int NW, bool ONE, int MT>
 __device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
                                        const float* __restrict__ sf, int M, const WeightView& w,
                                        int split, int kmax, float* __restrict__ out, int direct,
@@ -584,13 +404,22 @@ __device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
   const int bl = w.bits[rowbase + lc];
   const uint32_t ol = w.block_offset[rowbase + lc];
   const WaveRuns wr = wave_runs<NW>(lane < ncl ? bl : 0, wave, kWeightCostM1);
-  const int ma = min(lane & 15, M - 1);
-  CtxX cx{w.codes, w.scale, w.zero, rowbase,
-          xr + (int64_t)ma * w.K + (int64_t)c0 * kBlockCols + 8 * (lane >> 4),
-          sf + (int64_t)c0 * 16 + 4 * (lane >> 4)};
-  f32x4 yacc[4];
+  CtxX<MT> cx;
+  cx.codes = w.codes;
+  cx.scale = w.scale;
+  cx.zero = w.zero;
+  cx.rowbase = rowbase;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) yacc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) {
+    const int ma = min(16 * mt + (lane & 15), M - 1);
+    cx.xa[mt] = xr + (int64_t)ma * w.K + (int64_t)c0 * kBlockCols + 8 * (lane >> 4);
+  }
+  cx.sxa = sf + (int64_t)c0 * 16 * MT + 4 * (lane >> 4);
+  f32x4 yacc[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) yacc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint32_t off[5];
 #pragma unroll
   for (int k = 0; k < 5; ++k)
@@ -598,50 +427,58 @@ __device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
   auto base = [&](uint32_t o) __attribute__((always_inline)) {
     return w.codes + (int64_t)o * 1024 + 16 * lane;
   };
-  if (wr.n[0] > 0) run_x<1, ONE>(cx, base(off[0]), wr.cols[0], wr.n[0], yacc);
-  if (wr.n[1] > 0) run_x<2, ONE>(cx, base(off[1]), wr.cols[1], wr.n[1], yacc);
-  if (wr.n[2] > 0) run_x<3, ONE>(cx, base(off[2]), wr.cols[2], wr.n[2], yacc);
-  if (wr.n[3] > 0) run_x<4, ONE>(cx, base(off[3]), wr.cols[3], wr.n[3], yacc);
-  if (wr.n[4] > 0) run_x<8, ONE>(cx, base(off[4]), wr.cols[4], wr.n[4], yacc);
+  if (wr.n[0] > 0) run_x<1, ONE, MT>(cx, base(off[0]), wr.cols[0], wr.n[0], yacc);
+  if (wr.n[1] > 0) run_x<2, ONE, MT>(cx, base(off[1]), wr.cols[1], wr.n[1], yacc);
+  if (wr.n[2] > 0) run_x<3, ONE, MT>(cx, base(off[2]), wr.cols[2], wr.n[2], yacc);
+  if (wr.n[3] > 0) run_x<4, ONE, MT>(cx, base(off[3]), wr.cols[3], wr.n[3], yacc);
+  if (wr.n[4] > 0) run_x<8, ONE, MT>(cx, base(off[4]), wr.cols[4], wr.n[4], yacc);
 
-  // sum over the wavefronts in a fixed order and write out
+  // sum over the wavefronts in a fixed order and write out, one m tile at a
+  // time through the same LDS (NW - 1 planes of min(M, 16) x 64 floats)
   float* red = reinterpret_cast<float*>(smem);
-  const int plane = M * kBlockRows;
-  if (wave > 0) {
+  const int plane = min(M, 16) * kBlockRows;
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt > 0) __syncthreads();  // the previous tile's sums are read
+    if (wave > 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 4 * (lane >> 4) + i;
-        if (m < M) red[(wave - 1) * plane + m * kBlockRows + 16 * rt + (lane & 15)] = yacc[rt][i];
-      }
-  }
-  __syncthreads();
-  if (wave != 0) return;
+      for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * (lane >> 4) + i;
-      if (m >= M) continue;
-      const int n = 16 * rt + (lane & 15);
-      float v = yacc[rt][i];
-#pragma unroll
-      for (int k = 0; k < NW - 1; ++k) v += red[k * plane + m * kBlockRows + n];
-      const int64_t row = (int64_t)r * kBlockRows + n;
-      if (direct)
-        out[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
-      else
-        out[((int64_t)sp * M + m) * w.N + row] = v;
+        for (int i = 0; i < 4; ++i) {
+          const int mr = 4 * (lane >> 4) + i;
+          if (16 * mt + mr < M)
+            red[(wave - 1) * plane + mr * kBlockRows + 16 * rt + (lane & 15)] = yacc[mt][rt][i];
+        }
     }
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mr = 4 * (lane >> 4) + i;
+          const int m = 16 * mt + mr;
+          if (m >= M) continue;
+          const int n = 16 * rt + (lane & 15);
+          float v = yacc[mt][rt][i];
+#pragma unroll
+          for (int k = 0; k < NW - 1; ++k) v += red[k * plane + mr * kBlockRows + n];
+          const int64_t row = (int64_t)r * kBlockRows + n;
+          if (direct)
+            out[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
+          else
+            out[((int64_t)sp * M + m) * w.N + row] = v;
+        }
+    }
+  }
 }
 
-template <int NW, bool ONE>
+template <int NW, bool ONE, int MT>
 __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ sf, int M,
                                                     WeightView w, int split, int kmax,
                                                     float* __restrict__ out, int direct) {
-  gemv16<NW, ONE>(xr, sf, M, w, split, kmax, out, direct, blockIdx.x);
+  gemv16<NW, ONE, MT>(xr, sf, M, w, split, kmax, out, direct, blockIdx.x);
 }
 
 // ======================================================================================
@@ -767,7 +604,7 @@ __device__ __forceinline__ void run_ring(const Ctx& cx, const uint8_t* base, uin
   };
   const float4 bias{pick(std::integral_constant<int, 0>{}), pick(std::integral_constant<int, 1>{}),
                     pick(std::integral_constant<int, 2>{}), pick(std::integral_constant<int, 3>{})};
-  ring_run<B, ring_depth<B>(), false>(
+  ring_run<B, ring_depth<B>()>(
       cx, base, cols, n,
       [&](int cl, const BlockRegs<B>& br) __attribute__((always_inline)) {
         consume_m1<B>(cx, cl, br, y1, bias);
@@ -1046,8 +883,7 @@ __device__ __forceinline__ void gemv_m1(const uint16_t* __restrict__ xg,
     }
   }
 
-  Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, nullptr, nullptr, 0, kmax, 1,
-         (uint32_t)sums_off, 0u, 0u};
+  Ctx cx{w.codes, w.block_offset, w.scale, w.zero, rowbase, (uint32_t)sums_off, 0u, 0u};
   cx.a_lane = (uint32_t)(16 * (lane >> 4));
   cx.zero_off = zero_off;
   cx.s_off = (uint32_t)s_off;
@@ -1337,7 +1173,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
   reduce_elem(part, split, M, N, perm_row, y, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
-// ---- grouped calls at 2 <= M <= 16 ---------------------------------------------------
+// ---- grouped calls at 2 <= M <= 64 ---------------------------------------------------
 // One gather launch (every matrix's x reordered, with fp32 group sums), one
 // decode launch whose workgroups run all matrices side by side, and one
 // reduction launch for the matrices with several K ranges.  Job j owns the
@@ -1369,16 +1205,21 @@ __device__ __forceinline__ SmallJob pick_small_job(const SmallGroup& g, int b, b
   return q;
 }
 
+template <int MT>
 __global__ __launch_bounds__(512) void k_gemv16_group(SmallGroup g) {
   const SmallJob q = pick_small_job(g, blockIdx.x, false);
   const int direct = q.split == 1;
   float* dst = direct ? q.y : q.part;
   const int b = blockIdx.x - q.wg_begin;
-  // the branch is uniform over the workgroup
-  if (q.one)
-    gemv16<8, true>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
-  else
-    gemv16<8, false>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+  if constexpr (MT == 1) {
+    // the branch is uniform over the workgroup
+    if (q.one)
+      gemv16<8, true, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+    else
+      gemv16<8, false, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+  } else {
+    gemv16<8, true, MT>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_gemv_reduce_group(SmallGroup g) {
@@ -1454,15 +1295,6 @@ hipError_t launch_m1(const GemvWorkspace& g, const uint16_t* x, bool gather, con
   return hipGetLastError();
 }
 
-template <int NW, int MT>
-hipError_t launch_cfg(const uint16_t* xr, const uint16_t* sxs, int M, const WeightView& w,
-                      float* dst, const GemvPlan& p, int direct, hipStream_t stream) {
-  const unsigned grid = (unsigned)(w.NBr * p.split);
-  hipLaunchKernelGGL((k_gemv<NW, MT>), dim3(grid), dim3(NW * 64), p.lds_bytes, stream, xr, sxs, M,
-                     w, p.split, p.kr, p.xs_stride, dst, direct);
-  return hipGetLastError();
-}
-
 }  // namespace
 
 // Launch shape.  The block columns of a block row are split into `split`
@@ -1481,32 +1313,14 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   const int NBr = (int)(N / kBlockRows), NBc = (int)(K / kBlockCols);
   // the split heuristic counts the block rows of every matrix in the launch
   const int rows = group_rows > 0 ? (int)(group_rows / kBlockRows) : NBr;
-  p.mt = (int)((M + 15) / 16);
-  p.nw = M > 16 ? 4 : 8;
-  if (M == 1) p.nw = (opt.gemv_waves == 4 || opt.gemv_waves == 16) ? opt.gemv_waves : 8;
-  int kr_max = kMaxCols;
-  const bool small = M >= 2 && M <= 16;  // k_gemv16: no x slice in LDS
-  if (small) p.nw = 8;
-  if (M > 1 && !small) {
-    // LDS per block column: x slice (2 bytes x 128 per row) + one group sum per row
-    const size_t per_col = (size_t)M * (kBlockCols * 2 + 4);
-    kr_max = (int)((kLdsBudget - 16 * (size_t)M) / per_col);
-    if (kr_max > kMaxCols) kr_max = kMaxCols;
-    if (kr_max < 1) kr_max = 1;
-  }
+  p.nw = 8;
+  if (M == 1 && (opt.gemv_waves == 4 || opt.gemv_waves == 16)) p.nw = opt.gemv_waves;
   int split = opt.gemv_split;
   if (split <= 0) {
-    if (M <= 16) {
-      // about one workgroup of 8 wavefronts per CU: more K splits add start-ups
-      // and partials faster than they add memory parallelism
-      split = 256 / rows;
-      if (split > 8) split = 8;
-    } else {
-      split = (512 + NBr - 1) / NBr;
-      // with enough block rows, small M prefers fewer splits (less staging
-      // per workgroup and fewer partials): about one split per 4 rows of M
-      if (NBr >= 128) split = std::min<int>(split, std::max<int>(1, (int)((M + 3) / 4)));
-    }
+    // about one workgroup of 8 wavefronts per CU: more K splits add start-ups
+    // and partials faster than they add memory parallelism
+    split = 256 / rows;
+    if (split > 8) split = 8;
   }
   // M == 1, all launch choices automatic, at most 64 block columns, and a K
   // split wanted (at most 128 block rows in the launch): two workgroups per
@@ -1521,7 +1335,7 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   if (split > NBc) split = NBc;
   if (split < 1) split = 1;
   int kr = (NBc + split - 1) / split;
-  if (kr > kr_max) kr = kr_max;
+  if (kr > kMaxCols) kr = kMaxCols;
   split = (NBc + kr - 1) / kr;
   p.split = split;
   p.kr = kr;
@@ -1529,18 +1343,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   // launch) when the wavefront count allows it; the boundary has checked
   // that x and perm_col are 16-byte aligned, as those workgroups read them.
   p.gather = M == 1 && split == 1 && p.nw >= 8 && !opt.m1_prep ? 1 : 0;
-  size_t x_bytes;
-  if (M == 1) {
-    p.xs_stride = kr * kBlockCols;
-    x_bytes = m1_lds_bytes(kr);
-  } else if (small) {
-    p.xs_stride = 0;
-    x_bytes = 0;
-  } else {
-    p.xs_stride = kr * kBlockCols + 8;  // +16 bytes per row against LDS bank conflicts
-    x_bytes = (size_t)M * p.xs_stride * 2 + (size_t)M * kr * 4;
-  }
-  const size_t red_bytes = (size_t)(p.nw - 1) * (size_t)M * kBlockRows * 4;
+  // M == 1: the range's staging; the sum over the wavefronts (k_gemv16: one
+  // m tile of at most 16 rows at a time)
+  const size_t x_bytes = M == 1 ? m1_lds_bytes(kr) : 0;
+  const size_t red_bytes = (size_t)(p.nw - 1) * (size_t)std::min<int64_t>(M, 16) * kBlockRows * 4;
   p.lds_bytes = x_bytes > red_bytes ? x_bytes : red_bytes;
   p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : gather_workspace_bytes(M, K));
   return p;
@@ -1622,7 +1428,7 @@ size_t gemv_group_workspace_small(int64_t M, const WeightView* w, int count, con
 hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const WeightView* w,
                                    float* const* y, int count, void* workspace, const Options& opt,
                                    hipStream_t stream) {
-  if (count < 1 || count > kGroupMax || M < 2 || M > 16) return hipErrorInvalidValue;
+  if (count < 1 || count > kGroupMax || M < 2 || M > kSmallMaxM) return hipErrorInvalidValue;
   SmallGroup g{};
   g.count = count;
   g.M = (int)M;
@@ -1653,7 +1459,20 @@ hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const We
   }
   hipError_t e = launch_gather_x_group(x, M, w, gather_ws, count, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_gemv16_group, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+  switch ((M + 15) / 16) {
+    case 1:
+      hipLaunchKernelGGL(k_gemv16_group<1>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_gemv16_group<2>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+      break;
+    case 3:
+      hipLaunchKernelGGL(k_gemv16_group<3>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+      break;
+    default:
+      hipLaunchKernelGGL(k_gemv16_group<4>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+      break;
+  }
   e = hipGetLastError();
   if (e == hipSuccess && red_total > 0) {
     hipLaunchKernelGGL(k_gemv_reduce_group, dim3((unsigned)red_total), dim3(256), 0, stream, g);
@@ -1689,32 +1508,29 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
     if (p.nw == 16) return launch_m1<16>(g, x, gather, w, y, p, stream);
     return launch_m1<8>(g, x, gather, w, y, p, stream);
   } else {
-    // x reordered once per call (M <= 16: with fp32 group sums for k_gemv16,
-    // which reads its A operands from it directly; otherwise staged slice by
-    // slice into LDS)
-    const bool small = M <= 16;
-    e = launch_gather_x(x, M, w, g.gather, stream, small);
+    // x reordered once per call with fp32 group sums; k_gemv16 reads its A
+    // operands from it directly
+    e = launch_gather_x(x, M, w, g.gather, stream, true);
     if (e != hipSuccess) return e;
     const uint16_t* xr = reinterpret_cast<const uint16_t*>(g.gather);
-    const uint16_t* sxs = reinterpret_cast<const uint16_t*>(
-        reinterpret_cast<const uint8_t*>(g.gather) + align256((size_t)M * w.K * 2));
-    if (small) {
-      const float* sf = gather_sums_f32(g.gather, M, w.K);
-      const dim3 grid((unsigned)(w.NBr * p.split));
-      if (p.kr >= kMaxCols)
-        hipLaunchKernelGGL((k_gemv16<8, true>), grid, dim3(512), p.lds_bytes, stream, xr, sf, (int)M,
-                           w, p.split, p.kr, dst, direct);
-      else
-        hipLaunchKernelGGL((k_gemv16<8, false>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                           (int)M, w, p.split, p.kr, dst, direct);
-      e = hipGetLastError();
-    } else {
-      switch (p.mt) {
-        case 2: e = launch_cfg<4, 2>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
-        case 3: e = launch_cfg<4, 3>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
-        default: e = launch_cfg<4, 4>(xr, sxs, (int)M, w, dst, p, direct, stream); break;
-      }
-    }
+    const float* sf = gather_sums_f32(g.gather, M, w.K);
+    const dim3 grid((unsigned)(w.NBr * p.split));
+    if (M > 48)
+      hipLaunchKernelGGL((k_gemv16<8, true, 4>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                         (int)M, w, p.split, p.kr, dst, direct);
+    else if (M > 32)
+      hipLaunchKernelGGL((k_gemv16<8, true, 3>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                         (int)M, w, p.split, p.kr, dst, direct);
+    else if (M > 16)
+      hipLaunchKernelGGL((k_gemv16<8, true, 2>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                         (int)M, w, p.split, p.kr, dst, direct);
+    else if (p.kr >= kMaxCols)
+      hipLaunchKernelGGL((k_gemv16<8, true, 1>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                         (int)M, w, p.split, p.kr, dst, direct);
+    else
+      hipLaunchKernelGGL((k_gemv16<8, false, 1>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
+                         (int)M, w, p.split, p.kr, dst, direct);
+    e = hipGetLastError();
   }
   if (e != hipSuccess || direct) return e;
   return launch_split_reduce(g.part, p.split, M, w.N, w.perm_row, y, stream);

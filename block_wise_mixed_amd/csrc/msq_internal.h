@@ -47,9 +47,7 @@ hipError_t launch_pack(const uint16_t* W, int64_t N, int64_t K, const uint8_t* b
 struct GemvPlan {
   int split;        // K-splits across workgroups
   int kr;           // block columns per split (<= 64)
-  int mt;           // 16-row tiles of M
   int nw;           // wavefronts per workgroup
-  int xs_stride;    // bf16 elements per LDS row of the activation slice
   int gather;       // M == 1: the workgroups reorder x themselves (no prep launch)
   int halves;       // M == 1: two workgroups per block row of 32 rows each (gather, split 1)
   size_t lds_bytes; // dynamic LDS per workgroup
@@ -80,7 +78,7 @@ size_t gemv_group_workspace_m1(const WeightView* w, int count, const Options& op
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
                                 int count, void* workspace, const Options& opt,
                                 hipStream_t stream);
-// Grouped decode at 2 <= M <= 16: one gather launch, one decode launch over
+// Grouped decode at 2 <= M <= 64: one gather launch, one decode launch over
 // all matrices (each planned with the group's rows), one reduction launch for
 // the matrices with several K ranges, then the 16-bit pass of each matrix
 // that has 16-bit blocks; the workspace holds each matrix's workspace in turn.

@@ -112,7 +112,7 @@ extern "C" {
 #define MSQ_GEMV_MAX_M 64
 /* Largest M for which MSQ_KERNEL_AUTO picks the GEMV kernel; above it the
  * GEMM (which splits K when its tiles cannot fill the GPU) is faster. */
-#define MSQ_AUTO_GEMV_MAX_M 16
+#define MSQ_AUTO_GEMV_MAX_M 32
 
 typedef enum {
   MSQ_OK = 0,

@@ -131,7 +131,7 @@ def test_smoke_workload_256x512(msq, kernel):
 def test_m_boundary_sweep(msq, N, K, seed):
     c = synth.random_case(N, K, seed, dist=SMALL_DIST)
     pw, ref = check_pack(msq, c)
-    for M in (1, 2, 15, 16, 17, 63, 64, 65, 511, 512, 513):
+    for M in (1, 2, 15, 16, 17, 33, 48, 63, 64, 65, 511, 512, 513):
         check_y(msq, pw, c, ref, M, kernel="auto")
         if M <= 64:
             check_y(msq, pw, c, ref, M, kernel="gemm")
@@ -242,7 +242,8 @@ def test_integer_lattice_is_exact(msq, N, K, seed):
     c, xgen = synth.lattice_case(N, K, seed, dist={0: .1, 1: .2, 2: .2, 3: .2, 4: .2, 8: .1})
     pw, ref = check_pack(msq, c)
     assert (ref["s"][np.repeat(c.bits, 64, axis=0) > 0] == 1).all()
-    for M, kernel in ((1, "auto"), (5, "auto"), (64, "auto"), (1, "gemm"), (130, "gemm")):
+    for M, kernel in ((1, "auto"), (5, "auto"), (64, "auto"), (40, "gemv"), (1, "gemm"),
+                      (130, "gemm")):
         check_y(msq, pw, c, ref, M, kernel=kernel, exact=True, x=xgen(M))
 
 
@@ -380,9 +381,9 @@ def _check_given_y(y, case, ref, x):
     assert err <= TOL
 
 
-@pytest.mark.parametrize("M", [2, 16])
+@pytest.mark.parametrize("M", [2, 16, 24])
 def test_group_small_m_one_launch(msq, M):
-    """At 2 <= M <= 16 a group runs as one gather, one decode and (with several K
+    """At 2 <= M <= 32 a group runs as one gather, one decode and (with several K
     ranges) one reduction launch.  Two 8192-wide matrices and a 1024-wide one: with
     one K range forced (ranges of 64 block columns, the one-block ring variant, no
     reduction) and with three (the two-block variant and the reduction; ragged on
