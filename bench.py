@@ -57,7 +57,10 @@ the decode kernel):
                                   times (W resident) and exit;
   --only-prefill NAME --calls C : the same with prefill calls (M = 2048);
   --copy-bytes B                : copy B bytes device to device a few times
-                                  (the calibration of the byte counters).
+                                  (the calibration of the byte counters);
+  --rows-sweep                  : the M = 1 decode kernel of the roofline leg
+                                  on the first 1 .. 448 block rows of gate_proj
+                                  (fixed cost per call against streaming rate).
 """
 from __future__ import annotations
 
@@ -162,18 +165,19 @@ def bf16_dev(torch, np, a, dev):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-def decode_record(msq, torch, np, pw, x, M, rec, reps=10):
+def decode_record(msq, torch, np, pw, x, M, rec, reps=10, options=None):
     """M <= 64 decode of one matrix in a HIP graph over >= 1 GiB of rotating copies."""
     dev = x.device
     y = torch.empty((M, pw.N), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(msq.workspace_bytes(M, pw.N, pw.K), 256), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(msq.workspace_bytes(M, pw.N, pw.K, options=options), 256),
+                     dtype=torch.uint8, device=dev)
     R = max(2, min(256, int(np.ceil((1 << 30) / pw.packed_bytes))))
     cps = [pw] + [pw.clone() for _ in range(R - 1)]
-    msq.gemm(x, pw, out=y, workspace=ws)
+    msq.gemm(x, pw, out=y, workspace=ws, options=options)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for c in cps:
-            msq.gemm(x, c, out=y, workspace=ws)
+            msq.gemm(x, c, out=y, workspace=ws, options=options)
     g.replay()
     ts = replay_times_us(torch, [g], reps, R)
     us = pct(ts, 50)
@@ -185,6 +189,31 @@ def decode_record(msq, torch, np, pw, x, M, rec, reps=10):
                 "hbm_frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)})
     del g, cps
     return rec
+
+
+def rows_sweep(msq, synth, torch, np, dev, log):
+    """The roofline leg's kernel (M = 1, whole block rows, one K range: the
+    workgroups reorder x themselves) on the first k block rows of gate_proj
+    (W rows 0 .. 64k - 1, their bit-map rows and the restriction of perm_row),
+    k = 1 .. 448: how the call time grows from one workgroup to the full
+    matrix separates the per-call fixed cost (launch, start-up, drain) from
+    the streaming rate."""
+    mi = synth.matrix_inputs(WORKLOAD, "gate_proj")
+    x = bf16_dev(torch, np, mi.x(1), dev)
+    opt = {"gemv_split": 1}
+    out = []
+    for k in (1, 2, 4, 8, 16, 32, 64, 128, 192, 256, 320, 384, 448):
+        N = 64 * k
+        prow = mi.perm_row[mi.perm_row < N].astype(np.int32)
+        pw = msq.quantize_pack(bf16_dev(torch, np, mi.W[:N], dev), np.ascontiguousarray(mi.bits[:k]),
+                               prow, mi.perm_col)
+        rec = {"block_rows": k, "N": N, "K": mi.K, "workgroups": k}
+        decode_record(msq, torch, np, pw, x, 1, rec, options=opt)
+        log(f"rows sweep k={k}: {rec['us_per_call']} us, {rec['gbps_effective']} GB/s")
+        out.append(rec)
+        del pw
+        torch.cuda.empty_cache()
+    return out
 
 
 def config_legs(msq, synth, torch, np, dev, log, only_decode=False):
@@ -523,6 +552,8 @@ def main() -> int:
     ap.add_argument("--calls", type=int, default=20)
     ap.add_argument("--m", type=int, default=1, help="M of --only-decode (default 1)")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--rows-sweep", action="store_true",
+                    help="only the M = 1 decode on the first 1 .. 448 block rows of gate_proj")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -563,6 +594,9 @@ def main() -> int:
             msq.pack_into(Wd, pw)
         torch.cuda.synchronize()
         log(f"{args.calls} packs of {args.only_pack}: {msq.pack_bytes(pw)} bytes moved per pack")
+        return 0
+    if args.rows_sweep:
+        print(json.dumps({"rows_sweep": rows_sweep(msq, synth, torch, np, dev, log)}), flush=True)
         return 0
     if args.only_configs:
         recs = config_legs(msq, synth, torch, np, dev, log, only_decode=True)
