@@ -376,8 +376,7 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
                                                                0xF, 0xF, false));
-}
-__device__ __forceinline__ float row_min16(float v) {
+}__device__ __forceinline__ float row_min16(float v) {
   v = fminf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
   v = fminf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
   v = fminf(v, dpp_f<0x141>(v));  // row_half_mirror
@@ -393,14 +392,17 @@ __device__ __forceinline__ float row_max16(float v) {
 }
 
 // clamp(rint(fl(x / s)) + z, 0, qmax) for s > 0 (see above); rs = rcp(s),
-// fast = s is a normal number <= 2^125.
+// fast = s is a normal number <= 2^125.  t lies within 2^-13 of a
+// half-integer exactly when its distance to the nearest integer exceeds
+// 1/2 - 2^-13 (t - rint(t) is exact for |t| < 2^23); the clamp is one
+// median of three.
 __device__ __forceinline__ uint32_t code_of(float x, float s, float rs, bool fast, float z,
                                             float qmax) {
   const float t = x * rs;
   float r = __builtin_rintf(t);
-  const bool near = fabsf((t - floorf(t)) - 0.5f) < 0x1p-13f;
+  const bool near = fabsf(t - r) > 0.5f - 0x1p-13f;
   if (!fast || near) r = __builtin_rintf(x / s);
-  return (uint32_t)fminf(fmaxf(r + z, 0.0f), qmax);
+  return (uint32_t)__builtin_amdgcn_fmed3f(r + z, 0.0f, qmax);
 }
 
 // kThreads threads (4 groups of 16 lanes per wavefront), at most kRounds
@@ -563,14 +565,15 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
       hi = row_max16(hi);
       const float qmax = (float)((1 << b) - 1);
       const float s = (hi - lo) / qmax;
-      float z = 0.0f;
-      if (s > 0.0f) z = fminf(fmaxf(__builtin_rintf((-lo) / s), 0.0f), qmax);
+      // z = clamp(rint(fl(-lo / s)), 0, qmax) by the same rule as the codes
+      // (0 <= -lo / s <= qmax: hi >= 0)
+      const bool fast = s >= 0x1p-126f && s <= 0x1p125f;
+      const float rs = __builtin_amdgcn_rcpf(s);
+      const float z = s > 0.0f ? (float)code_of(-lo, s, rs, fast, 0.0f, qmax) : 0.0f;
       hs[j] = s;
       hz[j] = (uint32_t)z;
       uint32_t p[4];
       if (s > 0.0f) {
-        const bool fast = s >= 0x1p-126f && s <= 0x1p125f;
-        const float rs = __builtin_amdgcn_rcpf(s);
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
           p[kt] = code_of(x[kt][0], s, rs, fast, z, qmax) |
