@@ -371,24 +371,40 @@ constexpr int kRowMaxK = 32768;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 // DPP row (16-lane) reductions: xor 1, xor 2 (quad permutes), then the
-// half-row and row mirrors pair the remaining partners.
+// half-row and row mirrors pair the remaining partners.  Every source lane
+// of these patterns lies in the lane's own row and a row is active as a
+// whole, so no lane keeps its old value (none is supplied).
 template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
-                                                               0xF, 0xF, false));
-}__device__ __forceinline__ float row_min16(float v) {
-  v = fminf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fminf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fminf(v, dpp_f<0x141>(v));  // row_half_mirror
-  v = fminf(v, dpp_f<0x140>(v));  // row_mirror
-  return v;
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}// min / max of finite values as a median of three with -inf / +inf (one
+// instruction; fminf / fmaxf would first quiet a possible signaling NaN of
+// each permuted operand).  The infinity passes through an empty asm so that
+// the compiler does not turn the median back into fminf / fmaxf.
+__device__ __forceinline__ float min_f(float a, float b) {
+  float lo = -__builtin_inff();
+  asm("" : "+s"(lo));
+  return __builtin_amdgcn_fmed3f(a, b, lo);
 }
-__device__ __forceinline__ float row_max16(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));
-  v = fmaxf(v, dpp_f<0x4E>(v));
-  v = fmaxf(v, dpp_f<0x141>(v));
-  v = fmaxf(v, dpp_f<0x140>(v));
-  return v;
+__device__ __forceinline__ float max_f(float a, float b) {
+  float hi = __builtin_inff();
+  asm("" : "+s"(hi));
+  return __builtin_amdgcn_fmed3f(a, b, hi);
+}
+// Both reductions step by step, so that each step's two permutes and two
+// medians interleave.
+template <int kCtrl>
+__device__ __forceinline__ void minmax_step(float& lo, float& hi) {
+  const float a = dpp_f<kCtrl>(lo), b = dpp_f<kCtrl>(hi);
+  lo = min_f(lo, a);
+  hi = max_f(hi, b);
+}
+__device__ __forceinline__ void row_minmax16(float& lo, float& hi) {
+  minmax_step<0xB1>(lo, hi);   // quad_perm [1,0,3,2]
+  minmax_step<0x4E>(lo, hi);   // quad_perm [2,3,0,1]
+  minmax_step<0x141>(lo, hi);  // row_half_mirror
+  minmax_step<0x140>(lo, hi);  // row_mirror
 }
 
 // clamp(rint(fl(x / s)) + z, 0, qmax) for s > 0 (see above); rs = rcp(s),
@@ -561,8 +577,7 @@ __global__ __launch_bounds__(kThreads) void k_pack_rows(
           lo = fminf(lo, x[kt][h]);
           hi = fmaxf(hi, x[kt][h]);
         }
-      lo = row_min16(lo);
-      hi = row_max16(hi);
+      row_minmax16(lo, hi);
       const float qmax = (float)((1 << b) - 1);
       const float s = (hi - lo) / qmax;
       // z = clamp(rint(fl(-lo / s)), 0, qmax) by the same rule as the codes
