@@ -1166,11 +1166,30 @@ __device__ __forceinline__ void reduce_elem(const float* __restrict__ part, int 
   y[m * N + orig_row(perm_row, n, N)] = v;
 }
 
+// Workgroups of the element-wise reduction: 256 columns each, workgroup b
+// taking row m = 8 (j / chunks) + b mod 8 (j = b / 8, chunks = workgroups per
+// row).  Consecutive workgroup ids go to the XCDs in turn, so every
+// workgroup of a row runs on one XCD and the row's scattered stores meet in
+// one L2 (8B gate_proj at M = 64: 41.4 -> 39.2 us per call).
+__host__ __device__ inline int64_t reduce_workgroups(int64_t M, int64_t N) {
+  return 8 * ((M + 7) / 8) * ((N + 255) / 256);
+}
+__device__ __forceinline__ void reduce_wg(const float* __restrict__ part, int split, int M,
+                                          int64_t N, const int32_t* __restrict__ perm_row,
+                                          float* __restrict__ y, int64_t b) {
+  const int64_t chunks = (N + 255) / 256;
+  const int64_t j = b >> 3;
+  const int64_t m = 8 * (j / chunks) + (b & 7);
+  const int64_t n = (j - (j / chunks) * chunks) * 256 + threadIdx.x;
+  if (m >= M || n >= N) return;
+  reduce_elem(part, split, M, N, perm_row, y, m * N + n);
+}
+
 __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ part, int split,
                                                      int M, int64_t N,
                                                      const int32_t* __restrict__ perm_row,
                                                      float* __restrict__ y) {
-  reduce_elem(part, split, M, N, perm_row, y, (int64_t)blockIdx.x * 256 + threadIdx.x);
+  reduce_wg(part, split, M, N, perm_row, y, blockIdx.x);
 }
 
 // ---- grouped calls at 2 <= M <= 64 ---------------------------------------------------
@@ -1224,8 +1243,7 @@ __global__ __launch_bounds__(512) void k_gemv16_group(SmallGroup g) {
 
 __global__ __launch_bounds__(256) void k_gemv_reduce_group(SmallGroup g) {
   const SmallJob q = pick_small_job(g, blockIdx.x, true);
-  reduce_elem(q.part, q.split, g.M, q.w.N, q.w.perm_row, q.y,
-              (int64_t)(blockIdx.x - q.red_begin) * 256 + threadIdx.x);
+  reduce_wg(q.part, q.split, g.M, q.w.N, q.w.perm_row, q.y, blockIdx.x - q.red_begin);
 }
 
 // Workspace layout of one call: [partials | xg | sums | counters] (M == 1)
@@ -1454,7 +1472,7 @@ hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const We
     q.wg_begin = wg_total;
     q.red_begin = red_total;
     wg_total += (int)(w[i].NBr * p.split);
-    if (p.split > 1) red_total += (int)((M * w[i].N + 255) / 256);
+    if (p.split > 1) red_total += (int)reduce_workgroups(M, w[i].N);
     lds = std::max(lds, p.lds_bytes);
   }
   hipError_t e = launch_gather_x_group(x, M, w, gather_ws, count, stream);
@@ -1552,8 +1570,7 @@ hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t 
                          stream, part, split, (int)M, N, perm_row, y);
     return hipGetLastError();
   }
-  const int64_t total = M * N;
-  hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_gemv_reduce, dim3((unsigned)reduce_workgroups(M, N)), dim3(256), 0, stream,
                      part, split, (int)M, N, perm_row, y);
   return hipGetLastError();
 }
