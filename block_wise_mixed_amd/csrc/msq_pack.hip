@@ -358,13 +358,15 @@ __global__ __launch_bounds__(kPackThreads) void k_pack_blocks(
 // exactly the codes of its dword d of the lane slice n + 16 kg, for every
 // bitwidth.  The group's min / max run over its 16 lanes (one DPP row).
 //
-// Codes without a division per weight: q = rint(fl(w / s)) is taken as
-// rint(w * rcp(s)) unless w * rcp(s) lies within 2^-13 of a half-integer.
-// v_rcp_f32 is within 1 ulp, so w * rcp(s) differs from w / s by at most
-// 1.5 * 2^-23 relative, and fl(w / s) from w / s by 2^-24 relative; with
-// |w / s| <= 255 (w lies in [lo, hi], s = (hi - lo) / qmax) both stay within
-// 6.1e-5 < 2^-13 of each other, so outside that band both round to the same
-// integer.  Inside the band, and when s is not a normal number at most
+// Codes without a division per weight: rint(fl(w / s)) + z is taken as
+// rint(T), T = fl(w * rcp(s) + z) (one fused multiply-add), unless T lies
+// within 2^-13 of a half-integer.  v_rcp_f32 is within 1 ulp, so the exact
+// w * rcp(s) differs from w / s by at most 2^-23 relative; with |w / s| <=
+// 255 (w lies in [lo, hi], s = (hi - lo) / qmax) and z <= 255 the sum's
+// rounding adds at most 2^-15 (T < 512), and fl(w / s) differs from w / s
+// by at most 2^-24 relative: T and fl(w / s) + z stay within 7.6e-5 <
+// 2^-13 of each other, so outside that band both round to the same integer
+// (z is one).  Inside the band, and when s is not a normal number at most
 // 2^125, the correctly rounded division decides.  Bit-identical to rint of
 // the correctly rounded quotient for every input.
 constexpr int kRowMaxK = 32768;
@@ -408,17 +410,17 @@ __device__ __forceinline__ void row_minmax16(float& lo, float& hi) {
 }
 
 // clamp(rint(fl(x / s)) + z, 0, qmax) for s > 0 (see above); rs = rcp(s),
-// fast = s is a normal number <= 2^125.  t lies within 2^-13 of a
-// half-integer exactly when its distance to the nearest integer exceeds
-// 1/2 - 2^-13 (t - rint(t) is exact for |t| < 2^23); the clamp is one
-// median of three.
+// fast = s is a normal number <= 2^125, z an integer in [0, 255].  T lies
+// within 2^-13 of a half-integer exactly when its distance to the nearest
+// integer exceeds 1/2 - 2^-13 (T - rint(T) is exact for |T| < 2^23); the
+// clamp is one median of three.
 __device__ __forceinline__ uint32_t code_of(float x, float s, float rs, bool fast, float z,
                                             float qmax) {
-  const float t = x * rs;
+  const float t = __builtin_fmaf(x, rs, z);
   float r = __builtin_rintf(t);
   const bool near = fabsf(t - r) > 0.5f - 0x1p-13f;
-  if (!fast || near) r = __builtin_rintf(x / s);
-  return (uint32_t)__builtin_amdgcn_fmed3f(r + z, 0.0f, qmax);
+  if (!fast || near) r = __builtin_rintf(x / s) + z;
+  return (uint32_t)__builtin_amdgcn_fmed3f(r, 0.0f, qmax);
 }
 
 // kThreads threads (4 groups of 16 lanes per wavefront), at most kRounds
