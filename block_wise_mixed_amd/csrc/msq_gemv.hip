@@ -1192,7 +1192,7 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
   reduce_wg(part, split, M, N, perm_row, y, blockIdx.x);
 }
 
-// ---- grouped calls at 2 <= M <= 64 ---------------------------------------------------
+// ---- grouped calls at 2 <= M <= 32 ---------------------------------------------------
 // One gather launch (every matrix's x reordered, with fp32 group sums), one
 // decode launch whose workgroups run all matrices side by side, and one
 // reduction launch for the matrices with several K ranges.  Job j owns the
@@ -1446,7 +1446,7 @@ size_t gemv_group_workspace_small(int64_t M, const WeightView* w, int count, con
 hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const WeightView* w,
                                    float* const* y, int count, void* workspace, const Options& opt,
                                    hipStream_t stream) {
-  if (count < 1 || count > kGroupMax || M < 2 || M > kSmallMaxM) return hipErrorInvalidValue;
+  if (count < 1 || count > kGroupMax || M < 2 || M > kGemvGroupMaxSmallM) return hipErrorInvalidValue;
   SmallGroup g{};
   g.count = count;
   g.M = (int)M;
@@ -1477,20 +1477,10 @@ hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const We
   }
   hipError_t e = launch_gather_x_group(x, M, w, gather_ws, count, stream);
   if (e != hipSuccess) return e;
-  switch ((M + 15) / 16) {
-    case 1:
-      hipLaunchKernelGGL(k_gemv16_group<1>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
-      break;
-    case 2:
-      hipLaunchKernelGGL(k_gemv16_group<2>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
-      break;
-    case 3:
-      hipLaunchKernelGGL(k_gemv16_group<3>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
-      break;
-    default:
-      hipLaunchKernelGGL(k_gemv16_group<4>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
-      break;
-  }
+  if (M <= 16)
+    hipLaunchKernelGGL(k_gemv16_group<1>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
+  else
+    hipLaunchKernelGGL(k_gemv16_group<2>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
   e = hipGetLastError();
   if (e == hipSuccess && red_total > 0) {
     hipLaunchKernelGGL(k_gemv_reduce_group, dim3((unsigned)red_total), dim3(256), 0, stream, g);

@@ -171,6 +171,8 @@ msq_status group_impl(const uint16_t* const* x_bf16, int64_t M, const msq_weight
                       float* const* y, int count, void* workspace, size_t workspace_bytes,
                       const msq::Options& o, hipStream_t stream) {
   static_assert(MSQ_GROUP_MAX == msq::kGemvGroupMax, "group size of the header and the kernels");
+  static_assert(MSQ_AUTO_GEMV_MAX_M == msq::kGemvGroupMaxSmallM,
+                "grouped decode covers every M the automatic choice sends to the decode kernel");
   if (!x_bf16 || !w || !y || count < 1 || count > MSQ_GROUP_MAX) return MSQ_ERR_INVALID_ARG;
   if (o.kernel != MSQ_KERNEL_AUTO) return MSQ_ERR_INVALID_ARG;
   for (int i = 0; i < count; ++i) {

@@ -78,10 +78,12 @@ size_t gemv_group_workspace_m1(const WeightView* w, int count, const Options& op
 hipError_t launch_gemv_group_m1(const uint16_t* const* x, const WeightView* w, float* const* y,
                                 int count, void* workspace, const Options& opt,
                                 hipStream_t stream);
-// Grouped decode at 2 <= M <= 64: one gather launch, one decode launch over
+// Grouped decode at 2 <= M <= kGemvGroupMaxSmallM (the automatic choice's
+// limit; one or two m tiles): one gather launch, one decode launch over
 // all matrices (each planned with the group's rows), one reduction launch for
 // the matrices with several K ranges, then the 16-bit pass of each matrix
 // that has 16-bit blocks; the workspace holds each matrix's workspace in turn.
+constexpr int kGemvGroupMaxSmallM = 32;
 size_t gemv_group_workspace_small(int64_t M, const WeightView* w, int count, const Options& opt);
 hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const WeightView* w,
                                    float* const* y, int count, void* workspace, const Options& opt,
