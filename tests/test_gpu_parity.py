@@ -563,6 +563,27 @@ def test_long_k_unstaged_gather(msq, M, kernel):
     check_y(msq, pw, c, ref, M, kernel=kernel)
 
 
+def test_long_k_group_gather(msq):
+    """The grouped small-M gather with K = 32896 (x read from global memory, the row
+    no longer fits the LDS copy) beside a matrix whose row is staged: each output of
+    the group equals its single call bit for bit (the same K ranges in both:
+    gemv_split = 1, ranges of at most 64 block columns; five on the long row) and the
+    oracle within tolerance."""
+    cases = []
+    for N, K, seed in ((128, 32896, 95), (192, 1024, 96)):
+        c = synth.random_case(N, K, seed, dist=SMALL_DIST)
+        cases.append((c,) + check_pack(msq, c))
+    M = 4
+    xs = [c.x(M) for c, _, _ in cases]
+    opt = {"gemv_split": 1}
+    outs = msq.gemm_group(xs, [pw for _, pw, _ in cases], options=opt)
+    singles = [msq.gemm(x, pw, options=opt) for x, (_, pw, _) in zip(xs, cases)]
+    torch.cuda.synchronize()
+    for (c, pw, ref), x, y, single in zip(cases, xs, outs, singles):
+        assert torch.equal(y, single), c.name
+        _check_given_y(y, c, ref, x)
+
+
 @pytest.mark.parametrize("M", [1, 4])
 def test_long_k_tile16_pass(msq, M):
     """16-bit blocks with K = 32896 after the decode kernel: at M = 1 the 16-bit pass
