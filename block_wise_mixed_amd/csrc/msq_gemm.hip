@@ -235,24 +235,25 @@ __device__ __forceinline__ void read_a(const Stage& st, const uint32_t (&apk)[4]
 
 // 16-bit block: chunk F is the B operand of fragment F as it is (bf16
 // weights, no unpack, no scale), so the products go straight into acc.
-template <int CH>
+// Row tiles RT0 .. RT0 + NRT - 1 of the block (acc[mt][rt - RT0]).
+template <int CH, int RT0, int NRT>
 __device__ __forceinline__ void group_mfma16(const Stage& st, int q, const bf16x8 (&A)[4][4],
-                                             f32x4 (&acc)[4][4]) {
+                                             f32x4 (&acc)[4][NRT]) {
   static_assert(CH == 16, "16-bit blocks need 16 chunks per block in LDS");
   const uint4* cb = st.codes + q * CH * 64 + (threadIdx.x & 63);
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+  for (int j = 0; j < NRT; ++j)
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
-      const bf16x8 bop = as_bf16x8(cb[64 * (4 * rt + kt)]);
+      const bf16x8 bop = as_bf16x8(cb[64 * (4 * (RT0 + j) + kt)]);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[mt][rt] = mfma_bf16(A[kt][mt], bop, acc[mt][rt]);
+      for (int mt = 0; mt < 4; ++mt) acc[mt][j] = mfma_bf16(A[kt][mt], bop, acc[mt][j]);
     }
 }
 
-template <int B, int CH>
+template <int B, int CH, int RT0, int NRT>
 __device__ __forceinline__ void group_mfma(const Stage& st, int q, const bf16x8 (&A)[4][4],
-                                           const float (&sc)[4], f32x4 (&acc)[4][4]) {
+                                           const float (&sc)[NRT], f32x4 (&acc)[4][NRT]) {
   const int lane = threadIdx.x & 63;
   const uint4* cb = st.codes + q * CH * 64 + lane;
   auto rstep = [&](auto RTc) __attribute__((always_inline)) {
@@ -279,20 +280,22 @@ __device__ __forceinline__ void group_mfma(const Stage& st, int q, const bf16x8 
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[mt][rt][i] = fmaf(sc[rt], g[mt][i], acc[mt][rt][i]);
+      for (int i = 0; i < 4; ++i)
+        acc[mt][rt - RT0][i] = fmaf(sc[rt - RT0], g[mt][i], acc[mt][rt - RT0][i]);
   };
-  rstep(std::integral_constant<int, 0>{});
-  rstep(std::integral_constant<int, 1>{});
-  rstep(std::integral_constant<int, 2>{});
-  rstep(std::integral_constant<int, 3>{});
+  [&]<int... Js>(std::integer_sequence<int, Js...>) {
+    (rstep(std::integral_constant<int, RT0 + Js>{}), ...);
+  }(std::make_integer_sequence<int, NRT>{});
 }
 
-// Scales of rows 16 rt + (lane & 15) of block (r, c).
-__device__ __forceinline__ void load_scales(const WeightView& w, int r, int c, float (&s)[4]) {
+// Scales of rows 16 (rt0 + j) + (lane & 15) of block (r, c).
+template <int NRT>
+__device__ __forceinline__ void load_scales(const WeightView& w, int r, int c, int rt0,
+                                            float (&s)[NRT]) {
   const int lane = threadIdx.x & 63;
   const int64_t blk = r < w.NBr ? (int64_t)r * w.NBc + c : 0;  // in range for absent rows
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) s[rt] = w.scale[blk * kBlockRows + 16 * rt + (lane & 15)];
+  for (int j = 0; j < NRT; ++j) s[j] = w.scale[blk * kBlockRows + 16 * (rt0 + j) + (lane & 15)];
 }
 
 // Correction product.  With T[n][c] = -s[n][c] (bias_c + z[n][c]) (0 for
@@ -331,11 +334,20 @@ __device__ __forceinline__ void lds_barrier() {
 // and y is written (scattered through perm_row); otherwise the tile's share
 // of a K split goes to part[m][reordered row] (summed over the splits, in
 // split order, by the split-reduce kernel).
-template <int CH>
+//
+// BM = kBM: wavefront (wm, wn) = (wave & 1, wave >> 1) takes rows 64 wm ..
+// 64 wm + 63 of the tile and all four row tiles of block row rb + wn.  BM =
+// 64 (M <= 64, where a 128-row tile would leave half its wavefronts idle):
+// wavefront (wr, wn) = (wave & 1, wave >> 1) takes all 64 rows and row tiles
+// 2 wr, 2 wr + 1 of block row rb + wn; the products and their order per
+// output are the same.
+template <int CH, int BM = kBM>
 __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
                                           const uint16_t* __restrict__ sxs, int M,
                                           const WeightView& w, float* __restrict__ y, int mtile,
                                           int ntile, int g0, int g1, float* __restrict__ part) {
+  static_assert(BM == kBM || BM == 64, "tile heights");
+  constexpr int kRT = BM == kBM ? 4 : 2;  // row tiles per wavefront
   static_assert(kTUnits * kThreads == kBR * 32 * 16, "T units per thread");
   __shared__ __align__(16) uint4 a0[kBM * 16];
   __shared__ __align__(16) uint4 c0s[kBR * CH * 64], c1s[kBR * CH * 64];
@@ -343,9 +355,11 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   __shared__ uint8_t tbits[kBR][kTabG];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // wavefront (wm, wn): rows 64 wm .. 64 wm + 63 of the tile, block row rb + wn
-  const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)mtile * kBM;
+  // wavefront (wm, wn): rows 64 wm .. 64 wm + 63 of the tile, block row rb +
+  // wn, row tiles rt0 .. rt0 + kRT - 1
+  const int wm = BM == kBM ? (wave & 1) : 0, wn = wave >> 1;
+  const int rt0 = BM == kBM ? 0 : 2 * (wave & 1);
+  const int64_t m0 = (int64_t)mtile * BM;
   const int rb = ntile * kBR;  // first block row of the workgroup
   const int r = rb + wn;            // this wavefront's block row
   // a wavefront whose 64 rows all lie past M (the upper half of the last row
@@ -378,7 +392,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
   // M - 1; their products are never stored), and wavefronts 2q, 2q + 1
   // alternate the code chunks of block q.
   auto copy_group = [&](const Stage& st, int c) __attribute__((always_inline)) {
-    constexpr int kRows = kBM / kWaves;
+    constexpr int kRows = BM / kWaves;
     const int g = lane >> 4, p = lane & 15;
 #pragma unroll
     for (int i = 0; i < kRows / 4; ++i) {
@@ -418,28 +432,45 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
       apk[kt] = (uint32_t)((64 * wm + n) * 256 + (((4 * kt + g) ^ n) << 4));
   }
 
-  // acc[mt][rt]: rows 64 wm + 16 mt + 4 (lane >> 4) + i, output row 16 rt + (lane & 15)
-  f32x4 acc[4][4];
+  // acc[mt][j]: rows 64 wm + 16 mt + 4 (lane >> 4) + i, output row
+  // 16 (rt0 + j) + (lane & 15)
+  f32x4 acc[4][kRT];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) acc[mt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kRT; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // one group from stage st (A fragments A) with the block's scales sc
-  auto products = [&](const Stage& st, int c, const bf16x8 (&A)[4][4], const float (&sc)[4])
+  // the wavefront's row tiles of one B-bit block (BM = 64: which pair is
+  // uniform over the wavefront)
+  auto mma = [&](const Stage& st, const bf16x8 (&A)[4][4], const float (&sc)[kRT], auto Bc)
+                 __attribute__((always_inline)) {
+    constexpr int B = decltype(Bc)::value;
+    if constexpr (BM == kBM) {
+      if constexpr (B == 16) group_mfma16<CH, 0, 4>(st, wn, A, acc);
+      else group_mfma<B, CH, 0, 4>(st, wn, A, sc, acc);
+    } else if (rt0 == 0) {
+      if constexpr (B == 16) group_mfma16<CH, 0, 2>(st, wn, A, acc);
+      else group_mfma<B, CH, 0, 2>(st, wn, A, sc, acc);
+    } else {
+      if constexpr (B == 16) group_mfma16<CH, 2, 2>(st, wn, A, acc);
+      else group_mfma<B, CH, 2, 2>(st, wn, A, sc, acc);
+    }
+  };
+  auto products = [&](const Stage& st, int c, const bf16x8 (&A)[4][4], const float (&sc)[kRT])
                       __attribute__((always_inline)) {
     uint32_t unused_off;
     const int b = block_at(wn, c, unused_off);
     switch (b) {
       case 0: break;
-      case 1: group_mfma<1, CH>(st, wn, A, sc, acc); break;
-      case 2: group_mfma<2, CH>(st, wn, A, sc, acc); break;
-      case 3: group_mfma<3, CH>(st, wn, A, sc, acc); break;
-      case 4: group_mfma<4, CH>(st, wn, A, sc, acc); break;
+      case 1: mma(st, A, sc, std::integral_constant<int, 1>{}); break;
+      case 2: mma(st, A, sc, std::integral_constant<int, 2>{}); break;
+      case 3: mma(st, A, sc, std::integral_constant<int, 3>{}); break;
+      case 4: mma(st, A, sc, std::integral_constant<int, 4>{}); break;
       case 16:
-        if constexpr (CH == 16) group_mfma16<CH>(st, wn, A, acc);
+        if constexpr (CH == 16) mma(st, A, sc, std::integral_constant<int, 16>{});
         break;
-      default: group_mfma<8, CH>(st, wn, A, sc, acc); break;
+      default: mma(st, A, sc, std::integral_constant<int, 8>{}); break;
     }
   };
   // own copies done, then the workgroup barrier (no memory fence: the copies
@@ -451,9 +482,9 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     asm volatile("" ::: "memory");
   };
 
-  float cur[4], nxt[4];
+  float cur[kRT], nxt[kRT];
   copy_group(st0, g0);
-  load_scales(w, r, g0, cur);
+  load_scales(w, r, g0, rt0, cur);
   stage_barrier();
 
   // group c: A fragments from the one x_r buffer into registers, barrier,
@@ -466,12 +497,12 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     lds_barrier();
     if (c + 1 < g1) {
       copy_group(nx, c + 1);
-      load_scales(w, r, c + 1, nxt);
+      load_scales(w, r, c + 1, rt0, nxt);
     }
     if (live) products(st, c, A, cur);
     stage_barrier();
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) cur[rt] = nxt[rt];
+    for (int j = 0; j < kRT; ++j) cur[j] = nxt[j];
   };
   for (int c = g0; c < g1; c += 2) {
     group(st0, st1, c);
@@ -545,32 +576,32 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
     if (j0 + 32 < g1) load_t(j0 + 32);
     lds_barrier();
     if (!live) continue;  // the barriers above are the loop's only ones
-    bf16x8 Tb[3][4];
+    bf16x8 Tb[3][kRT];
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt)
-        Tb[t][rt] = as_bf16x8(
-            *reinterpret_cast<const uint4*>(tq(wn) + t * kTermBytes + (rt * 64 + lane) * 16));
+      for (int j = 0; j < kRT; ++j)
+        Tb[t][j] = as_bf16x8(*reinterpret_cast<const uint4*>(
+            tq(wn) + t * kTermBytes + ((rt0 + j) * 64 + lane) * 16));
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        f32x4 v = acc[mt][rt];
-        v = mfma_bf16(Sa[2][mt], Tb[0][rt], v);
-        v = mfma_bf16(Sa[1][mt], Tb[1][rt], v);
-        v = mfma_bf16(Sa[0][mt], Tb[2][rt], v);
-        v = mfma_bf16(Sa[1][mt], Tb[0][rt], v);
-        v = mfma_bf16(Sa[0][mt], Tb[1][rt], v);
-        acc[mt][rt] = mfma_bf16(Sa[0][mt], Tb[0][rt], v);
+      for (int j = 0; j < kRT; ++j) {
+        f32x4 v = acc[mt][j];
+        v = mfma_bf16(Sa[2][mt], Tb[0][j], v);
+        v = mfma_bf16(Sa[1][mt], Tb[1][j], v);
+        v = mfma_bf16(Sa[0][mt], Tb[2][j], v);
+        v = mfma_bf16(Sa[1][mt], Tb[0][j], v);
+        v = mfma_bf16(Sa[0][mt], Tb[1][j], v);
+        acc[mt][j] = mfma_bf16(Sa[0][mt], Tb[0][j], v);
       }
   }
 
   // epilogue: y[m][perm_row[n]], or the split's partial part[m][n]
   if (r >= w.NBr) return;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const int64_t row = (int64_t)r * kBlockRows + 16 * rt + (lane & 15);
+  for (int j = 0; j < kRT; ++j) {
+    const int64_t row = (int64_t)r * kBlockRows + 16 * (rt0 + j) + (lane & 15);
     int col = part ? (int)row : w.perm_row[row];
     col = min(max(col, 0), (int)w.N - 1);
     float* out = part ? part : y;
@@ -579,19 +610,19 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ xr,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 64 * wm + 16 * mt + 4 * (lane >> 4) + i;
-        if (m < M) out[m * w.N + col] = acc[mt][rt][i];
+        if (m < M) out[m * w.N + col] = acc[mt][j][i];
       }
   }
 }
 
-template <int CH>
+template <int CH, int BM>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void k_gemm(
     const uint16_t* __restrict__ xr, const uint16_t* __restrict__ sxs, int M, WeightView w,
     float* __restrict__ y, float* __restrict__ part, int gper) {
   // K split blockIdx.z: groups gper z .. ; partials plane z of part
   const int g0 = blockIdx.z * gper, g1 = min(w.NBc, g0 + gper);
-  gemm_tile<CH>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
-                part ? part + (int64_t)blockIdx.z * M * w.N : nullptr);
+  gemm_tile<CH, BM>(xr, sxs, M, w, y, blockIdx.x, blockIdx.y, g0, g1,
+                    part ? part + (int64_t)blockIdx.z * M * w.N : nullptr);
 }
 
 // ---- grouped calls: up to kGroupMax matrices at the same M -------------------------------
@@ -964,17 +995,24 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
                     : nullptr;
   hipError_t e = launch_gather_x(x, M, w, workspace, stream, false);
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((M + kBM - 1) / kBM), (unsigned)((w.NBr + kBR - 1) / kBR),
+  // M <= 64: 64-row tiles (every wavefront holds rows below M)
+  const bool short_m = M <= 64;
+  const int64_t bm = short_m ? 64 : kBM;
+  const dim3 grid((unsigned)((M + bm - 1) / bm), (unsigned)((w.NBr + kBR - 1) / kBR),
                   (unsigned)p.split);
   // one K range: the tiles write y in reordered order (into y), un-permuted after
   const bool unpermute = p.split == 1 && w.N <= kUnpermuteMaxN;
   float* out = p.split > 1 ? part : (unpermute ? y : nullptr);
-  if (w.has16)
-    hipLaunchKernelGGL((k_gemm<16>), grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y, out,
-                       p.gper);
-  else
-    hipLaunchKernelGGL((k_gemm<8>), grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y, out,
-                       p.gper);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, stream, xr, sxs, (int)M, w, y, out, p.gper);
+  };
+  if (w.has16) {
+    if (short_m) go(k_gemm<16, 64>);
+    else go(k_gemm<16, kBM>);
+  } else {
+    if (short_m) go(k_gemm<8, 64>);
+    else go(k_gemm<8, kBM>);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.split > 1) return launch_split_reduce(part, p.split, M, w.N, w.perm_row, y, stream);
