@@ -332,8 +332,7 @@ def group_workspace_bytes(M: int, pws, options: Optional[dict] = None) -> int:
 def gemm_group(xs, pws, outs=None, workspace=None, stream=None, options: Optional[dict] = None):
     """[x_i . W_i^T] for up to GROUP_MAX packed weights in one call (M == 1: one decode
     launch for all of them, plus one prep launch if some have several K ranges; M = 2..32:
-    one gather, one decode and at most one reduction launch; large M: one gather and one
-    GEMM launch).  xs: one activation per weight (the same tensor may repeat); returns
+    one gather and one decode launch; large M: one gather and one GEMM launch).  xs: one activation per weight (the same tensor may repeat); returns
     the list of fp32 [M][N_i] outputs."""
     torch = _torch()
     lib = load_library()

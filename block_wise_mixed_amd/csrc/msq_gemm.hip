@@ -132,6 +132,15 @@ __device__ __forceinline__ void gather_row(const uint16_t* __restrict__ x, int64
   }
 }
 
+// The decode's K-split counters of the call (ncounters of them, zero when
+// the decode kernel has one K range) cleared by the workgroups of the gather
+// that runs before it, b-th of nb workgroups.
+__device__ __forceinline__ void clear_counters(uint32_t* __restrict__ counters, int ncounters,
+                                               int64_t b, int64_t nb) {
+  for (int64_t i = b * kGatherThreads + threadIdx.x; i < ncounters; i += nb * kGatherThreads)
+    counters[i] = 0u;
+}
+
 // Row blockIdx.x, chunk slice blockIdx.y of gridDim.y (whole groups).
 __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __restrict__ x,
                                                              int64_t K, int64_t M,
@@ -139,7 +148,11 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x(const uint16_t* __r
                                                              uint16_t* __restrict__ xr,
                                                              uint16_t* __restrict__ sxs,
                                                              float* __restrict__ sf, int64_t Mpad,
-                                                             int staged) {
+                                                             int staged,
+                                                             uint32_t* __restrict__ counters,
+                                                             int ncounters) {
+  clear_counters(counters, ncounters, (int64_t)blockIdx.y * gridDim.x + blockIdx.x,
+                 (int64_t)gridDim.x * gridDim.y);
   const int64_t Gp = padded_groups(K / kBlockCols);
   const int64_t per = (Gp + gridDim.y - 1) / gridDim.y * 16;
   const int64_t qs = (int64_t)blockIdx.y * per;
@@ -675,6 +688,8 @@ struct GatherJob {
   uint16_t* xr;
   uint16_t* sxs;
   float* sf;
+  uint32_t* counters;  // the decode's K-split counters, cleared here
+  int ncounters;
   int staged, slices, begin;
 };
 
@@ -690,6 +705,7 @@ __global__ __launch_bounds__(kGatherThreads) void k_gather_x_jobs(GatherGroup g)
   for (int k = 1; k < kGroupMax; ++k)
     if (k < g.count && (int)blockIdx.x >= g.job[k].begin) q = g.job[k];
   const int b = blockIdx.x - q.begin;
+  clear_counters(q.counters, q.ncounters, b, (int64_t)g.M * q.slices);
   const int m = b / q.slices, sl = b - m * q.slices;
   const int64_t Gp = padded_groups(q.K / kBlockCols);
   const int64_t per = (Gp + q.slices - 1) / q.slices * 16;
@@ -932,7 +948,8 @@ static int64_t gather_slices(int64_t M, int64_t K) {
 }
 
 hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const WeightView* w,
-                                 void* const* ws, int count, hipStream_t stream) {
+                                 void* const* ws, uint32_t* const* counters,
+                                 const int* ncounters, int count, hipStream_t stream) {
   if (count < 1 || count > kGroupMax) return hipErrorInvalidValue;
   GatherGroup g{};
   g.count = count;
@@ -952,6 +969,8 @@ hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const Weig
     q.staged = (size_t)K * 2 <= kGatherMaxLds;
     if (q.staged) lds = std::max(lds, (size_t)K * 2);
     q.slices = (int)gather_slices(M, K);
+    q.counters = counters[i];
+    q.ncounters = ncounters[i];
     q.begin = (int)total;
     total += M * q.slices;
   }
@@ -961,7 +980,8 @@ hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const Weig
 }
 
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
-                           hipStream_t stream, bool sums_f32) {
+                           hipStream_t stream, bool sums_f32, uint32_t* counters,
+                           int ncounters) {
   const int64_t K = w.K;
   uint16_t* xr = reinterpret_cast<uint16_t*>(ws);
   const size_t xr_bytes = (((size_t)M * K * 2) + 255) & ~(size_t)255;
@@ -972,7 +992,7 @@ hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, vo
   float* sf = sums_f32 ? gather_sums_f32(ws, M, K) : nullptr;
   hipLaunchKernelGGL(k_gather_x, dim3((unsigned)M, (unsigned)slices), dim3(kGatherThreads),
                      staged ? row_bytes : 0, stream, x, K, M, w.perm_col, xr, sxs, sf,
-                     (int64_t)gather_mpad(M), staged);
+                     (int64_t)gather_mpad(M), staged, counters, ncounters);
   return hipGetLastError();
 }
 
@@ -993,7 +1013,7 @@ hipError_t launch_gemm(const uint16_t* x, int64_t M, const WeightView& w, float*
                     ? reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(workspace) +
                                                ((gather_workspace_bytes(M, K) + 255) & ~(size_t)255))
                     : nullptr;
-  hipError_t e = launch_gather_x(x, M, w, workspace, stream, false);
+  hipError_t e = launch_gather_x(x, M, w, workspace, stream, false, nullptr, 0);
   if (e != hipSuccess) return e;
   // M <= 64: 64-row tiles (every wavefront holds rows below M)
   const bool short_m = M <= 64;

@@ -387,12 +387,17 @@ __device__ __forceinline__ void run_x(const CtxX<MT>& cx, const uint8_t* base, u
 }
 
 // Workgroup `blk` (block row blk / split, K range blk % split) of one matrix,
-// M in 16 (MT - 1) + 1 .. 16 MT.
+// M in 16 (MT - 1) + 1 .. 16 MT.  One K range: y is written directly.
+// Several: the range's partial goes to part[sp][m][n] and the last workgroup
+// of the block row to arrive (counters[r], cleared by the gather before this
+// launch) adds the partials in split order into y.
 template <int NW, bool ONE, int MT>
 __device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
                                        const float* __restrict__ sf, int M, const WeightView& w,
-                                       int split, int kmax, float* __restrict__ out, int direct,
+                                       int split, int kmax, float* __restrict__ part,
+                                       float* __restrict__ y, uint32_t* __restrict__ counters,
                                        int blk) {
+  const bool direct = split == 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = blk / split, sp = blk - (blk / split) * split;
@@ -465,11 +470,50 @@ __device__ __forceinline__ void gemv16(const uint16_t* __restrict__ xr,
           for (int k = 0; k < NW - 1; ++k) v += red[k * plane + mr * kBlockRows + n];
           const int64_t row = (int64_t)r * kBlockRows + n;
           if (direct)
-            out[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
+            y[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
           else
-            out[((int64_t)sp * M + m) * w.N + row] = v;
+            __hip_atomic_store(&part[((int64_t)sp * M + m) * w.N + row], v, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+  }
+  if (direct) return;
+  // Several K ranges: the partials are stored and read back with device-scope
+  // (relaxed atomic) accesses, which go to the level shared by all XCDs, and
+  // wavefront 0's stores (the only ones) are complete before it increments
+  // the row's counter; the last workgroup of the row adds the partials in
+  // split order (the order of the separate reduction kernel), so y is
+  // reproducible.  Wavefront 0 has read the LDS sums above, so it may reuse
+  // their first word for the verdict.
+  int* verdict = reinterpret_cast<int*>(smem);
+  if (wave == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    unsigned prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(&counters[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __shfl(prev, 0, 64);
+    if (lane == 0) *verdict = prev == (unsigned)(split - 1);
+  }
+  __syncthreads();
+  if (*verdict == 0) return;
+  const int64_t pstride = (int64_t)M * w.N;  // one split's partials
+  for (int e = threadIdx.x; e < M * kBlockRows; e += NW * 64) {
+    const int m = e / kBlockRows, n = e - (e / kBlockRows) * kBlockRows;
+    const int64_t row = (int64_t)r * kBlockRows + n;
+    const float* p = part + (int64_t)m * w.N + row;
+    float v = 0.f;
+    int k = 0;
+    for (; k + 8 <= split; k += 8) {
+      float t[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        t[j] = __hip_atomic_load(p + (k + j) * pstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v += t[j];
+    }
+    for (; k < split; ++k)
+      v += __hip_atomic_load(p + k * pstride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    y[(int64_t)m * w.N + orig_row(w.perm_row, row, w.N)] = v;
   }
 }
 
@@ -477,8 +521,9 @@ template <int NW, bool ONE, int MT>
 __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__ xr,
                                                     const float* __restrict__ sf, int M,
                                                     WeightView w, int split, int kmax,
-                                                    float* __restrict__ out, int direct) {
-  gemv16<NW, ONE, MT>(xr, sf, M, w, split, kmax, out, direct, blockIdx.x);
+                                                    float* __restrict__ part, float* __restrict__ y,
+                                                    uint32_t* __restrict__ counters) {
+  gemv16<NW, ONE, MT>(xr, sf, M, w, split, kmax, part, y, counters, blockIdx.x);
 }
 
 // ======================================================================================
@@ -497,7 +542,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemv16(const uint16_t* __restrict__
 // x, the others read a zero area, and the 64 row results of a block come out
 // in lanes 0..15 of the four row-tile accumulators (rows_to_lanes moves row
 // 16*rt + n to lane 16*rt + n).
-
 
 // One wavefront per block column; lane l handles columns 2l, 2l + 1.
 // Workgroup `blk` of the prep of one matrix.
@@ -1193,20 +1237,20 @@ __global__ __launch_bounds__(256) void k_gemv_reduce(const float* __restrict__ p
 }
 
 // ---- grouped calls at 2 <= M <= 32 ---------------------------------------------------
-// One gather launch (every matrix's x reordered, with fp32 group sums), one
-// decode launch whose workgroups run all matrices side by side, and one
-// reduction launch for the matrices with several K ranges.  Job j owns the
-// workgroups [wg_begin, wg_begin of j + 1) of the decode launch and
-// [red_begin, red_begin of j + 1) of the reduction (none with one K range;
-// such a job shares its begin with the next job, which the selection picks).
+// One gather launch (every matrix's x reordered, with fp32 group sums; the
+// split counters cleared) and one decode launch whose workgroups run all
+// matrices side by side (matrices with several K ranges reduce them in the
+// decode's last arriving workgroups).  Job j owns the workgroups [wg_begin,
+// wg_begin of j + 1) of the decode launch.
 struct SmallJob {
   WeightView w;
   const uint16_t* xr;  // reordered x [M][K] in the job's workspace
   const float* sf;     // its fp32 group sums
   float* part;         // fp32 partials [split][M][N] (split > 1)
   float* y;
+  uint32_t* counters;  // split counters, one per block row (split > 1)
   int split, kr, one;  // one: ranges of 64 block columns (one-block rings)
-  int wg_begin, red_begin;
+  int wg_begin;
 };
 
 struct SmallGroup {
@@ -1215,40 +1259,34 @@ struct SmallGroup {
   int M;
 };
 
-// Copy of the job owning workgroup b of the decode (or reduction) launch.
-__device__ __forceinline__ SmallJob pick_small_job(const SmallGroup& g, int b, bool reduce) {
+// Copy of the job owning workgroup b of the decode launch.
+__device__ __forceinline__ SmallJob pick_small_job(const SmallGroup& g, int b) {
   SmallJob q = g.job[0];
 #pragma unroll
   for (int k = 1; k < kGroupMax; ++k)
-    if (k < g.count && b >= (reduce ? g.job[k].red_begin : g.job[k].wg_begin)) q = g.job[k];
+    if (k < g.count && b >= g.job[k].wg_begin) q = g.job[k];
   return q;
 }
 
 template <int MT>
 __global__ __launch_bounds__(512) void k_gemv16_group(SmallGroup g) {
-  const SmallJob q = pick_small_job(g, blockIdx.x, false);
-  const int direct = q.split == 1;
-  float* dst = direct ? q.y : q.part;
+  const SmallJob q = pick_small_job(g, blockIdx.x);
   const int b = blockIdx.x - q.wg_begin;
   if constexpr (MT == 1) {
     // the branch is uniform over the workgroup
     if (q.one)
-      gemv16<8, true, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+      gemv16<8, true, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, q.part, q.y, q.counters, b);
     else
-      gemv16<8, false, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+      gemv16<8, false, 1>(q.xr, q.sf, g.M, q.w, q.split, q.kr, q.part, q.y, q.counters, b);
   } else {
-    gemv16<8, true, MT>(q.xr, q.sf, g.M, q.w, q.split, q.kr, dst, direct, b);
+    gemv16<8, true, MT>(q.xr, q.sf, g.M, q.w, q.split, q.kr, q.part, q.y, q.counters, b);
   }
 }
 
-__global__ __launch_bounds__(256) void k_gemv_reduce_group(SmallGroup g) {
-  const SmallJob q = pick_small_job(g, blockIdx.x, true);
-  reduce_wg(q.part, q.split, g.M, q.w.N, q.w.perm_row, q.y, blockIdx.x - q.red_begin);
-}
-
 // Workspace layout of one call: [partials | xg | sums | counters] (M == 1)
-// or [partials | gather buffers] (M > 1), each part 256-byte aligned; the
-// partials only with several splits.
+// or [partials | gather buffers | counters] (M > 1), each part 256-byte
+// aligned; the partials (and, at M > 1, the counters) only with several
+// splits.
 struct GemvWorkspace {
   float* part;
   void* gather;  // M > 1: the gather kernel's x_r and split group sums
@@ -1273,7 +1311,11 @@ GemvWorkspace carve(void* ws, const GemvPlan& p, int64_t M, int64_t N, int64_t K
   GemvWorkspace g{};
   g.part = reinterpret_cast<float*>(b);
   b += part_bytes(p, M, N);
-  if (M > 1) g.gather = b;
+  if (M > 1) {
+    g.gather = b;
+    b += align256(gather_workspace_bytes(M, K));
+    if (p.split > 1) g.counters = reinterpret_cast<uint32_t*>(b);
+  }
   if (M == 1) {
     const size_t nbc = (size_t)(K / kBlockCols);
     g.xg = reinterpret_cast<uint16_t*>(b);
@@ -1366,7 +1408,10 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   const size_t x_bytes = M == 1 ? m1_lds_bytes(kr) : 0;
   const size_t red_bytes = (size_t)(p.nw - 1) * (size_t)std::min<int64_t>(M, 16) * kBlockRows * 4;
   p.lds_bytes = x_bytes > red_bytes ? x_bytes : red_bytes;
-  p.workspace = part_bytes(p, M, N) + (M == 1 ? m1_prep_bytes(N, K) : gather_workspace_bytes(M, K));
+  p.workspace = part_bytes(p, M, N) +
+                (M == 1 ? m1_prep_bytes(N, K)
+                        : align256(gather_workspace_bytes(M, K)) +
+                              (split > 1 ? align256((size_t)(N / kBlockRows) * 4) : 0));
   return p;
 }
 
@@ -1451,8 +1496,10 @@ hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const We
   g.count = count;
   g.M = (int)M;
   void* gather_ws[kGroupMax];
+  uint32_t* counters[kGroupMax];
+  int ncounters[kGroupMax];
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);
-  int wg_total = 0, red_total = 0;
+  int wg_total = 0;
   size_t lds = 0;
   const int64_t rows = group_rows(w, count);
   for (int i = 0; i < count; ++i) {
@@ -1460,32 +1507,29 @@ hipError_t launch_gemv_group_small(const uint16_t* const* x, int64_t M, const We
     const GemvWorkspace gw = carve(ws, p, M, w[i].N, w[i].K);
     ws += align256(p.workspace);
     gather_ws[i] = gw.gather;
+    counters[i] = gw.counters;
+    ncounters[i] = p.split > 1 ? (int)w[i].NBr : 0;
     SmallJob& q = g.job[i];
     q.w = w[i];
     q.xr = reinterpret_cast<const uint16_t*>(gw.gather);
     q.sf = gather_sums_f32(gw.gather, M, w[i].K);
     q.part = gw.part;
     q.y = y[i];
+    q.counters = gw.counters;
     q.split = p.split;
     q.kr = p.kr;
     q.one = p.kr >= kMaxCols ? 1 : 0;
     q.wg_begin = wg_total;
-    q.red_begin = red_total;
     wg_total += (int)(w[i].NBr * p.split);
-    if (p.split > 1) red_total += (int)reduce_workgroups(M, w[i].N);
     lds = std::max(lds, p.lds_bytes);
   }
-  hipError_t e = launch_gather_x_group(x, M, w, gather_ws, count, stream);
+  hipError_t e = launch_gather_x_group(x, M, w, gather_ws, counters, ncounters, count, stream);
   if (e != hipSuccess) return e;
   if (M <= 16)
     hipLaunchKernelGGL(k_gemv16_group<1>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
   else
     hipLaunchKernelGGL(k_gemv16_group<2>, dim3((unsigned)wg_total), dim3(512), lds, stream, g);
   e = hipGetLastError();
-  if (e == hipSuccess && red_total > 0) {
-    hipLaunchKernelGGL(k_gemv_reduce_group, dim3((unsigned)red_total), dim3(256), 0, stream, g);
-    e = hipGetLastError();
-  }
   // the decode kernel leaves 16-bit blocks to one more pass per matrix, as
   // in the single call
   for (int i = 0; i < count && e == hipSuccess; ++i)
@@ -1497,7 +1541,6 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
                        void* workspace, const GemvPlan& p, hipStream_t stream) {
   const int direct = p.split == 1;
   const GemvWorkspace g = carve(workspace, p, M, w.N, w.K);
-  float* dst = direct ? y : g.part;
   hipError_t e;
   if (M == 1) {
     const bool gather = p.gather != 0;
@@ -1515,33 +1558,25 @@ hipError_t launch_gemv(const uint16_t* x, int64_t M, const WeightView& w, float*
     if (p.nw == 4) return launch_m1<4>(g, x, gather, w, y, p, stream);
     if (p.nw == 16) return launch_m1<16>(g, x, gather, w, y, p, stream);
     return launch_m1<8>(g, x, gather, w, y, p, stream);
-  } else {
-    // x reordered once per call with fp32 group sums; k_gemv16 reads its A
-    // operands from it directly
-    e = launch_gather_x(x, M, w, g.gather, stream, true);
-    if (e != hipSuccess) return e;
-    const uint16_t* xr = reinterpret_cast<const uint16_t*>(g.gather);
-    const float* sf = gather_sums_f32(g.gather, M, w.K);
-    const dim3 grid((unsigned)(w.NBr * p.split));
-    if (M > 48)
-      hipLaunchKernelGGL((k_gemv16<8, true, 4>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                         (int)M, w, p.split, p.kr, dst, direct);
-    else if (M > 32)
-      hipLaunchKernelGGL((k_gemv16<8, true, 3>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                         (int)M, w, p.split, p.kr, dst, direct);
-    else if (M > 16)
-      hipLaunchKernelGGL((k_gemv16<8, true, 2>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                         (int)M, w, p.split, p.kr, dst, direct);
-    else if (p.kr >= kMaxCols)
-      hipLaunchKernelGGL((k_gemv16<8, true, 1>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                         (int)M, w, p.split, p.kr, dst, direct);
-    else
-      hipLaunchKernelGGL((k_gemv16<8, false, 1>), grid, dim3(512), p.lds_bytes, stream, xr, sf,
-                         (int)M, w, p.split, p.kr, dst, direct);
-    e = hipGetLastError();
   }
-  if (e != hipSuccess || direct) return e;
-  return launch_split_reduce(g.part, p.split, M, w.N, w.perm_row, y, stream);
+  // x reordered once per call with fp32 group sums (and the split counters
+  // cleared); k_gemv16 reads its A operands from it directly and, with
+  // several K ranges, reduces them in its last arriving workgroups
+  e = launch_gather_x(x, M, w, g.gather, stream, true, g.counters, direct ? 0 : (int)w.NBr);
+  if (e != hipSuccess) return e;
+  const uint16_t* xr = reinterpret_cast<const uint16_t*>(g.gather);
+  const float* sf = gather_sums_f32(g.gather, M, w.K);
+  const dim3 grid((unsigned)(w.NBr * p.split));
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(512), p.lds_bytes, stream, xr, sf, (int)M, w, p.split,
+                       p.kr, g.part, y, g.counters);
+  };
+  if (M > 48) go(k_gemv16<8, true, 4>);
+  else if (M > 32) go(k_gemv16<8, true, 3>);
+  else if (M > 16) go(k_gemv16<8, true, 2>);
+  else if (p.kr >= kMaxCols) go(k_gemv16<8, true, 1>);
+  else go(k_gemv16<8, false, 1>);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_reduce(const float* part, int split, int64_t M, int64_t N,

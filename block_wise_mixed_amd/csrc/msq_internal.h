@@ -99,14 +99,19 @@ __host__ __device__ constexpr int64_t padded_groups(int64_t G) { return (G + 31)
 __host__ __device__ constexpr int64_t gather_mpad(int64_t M) { return (M + 15) & ~(int64_t)15; }
 size_t gather_workspace_bytes(int64_t M, int64_t K);
 // sums_f32: also write the group sums in fp32, [padded groups][gather_mpad(M)]
-// (rows past M left as they are), at gather_sums_f32(ws, M, K).
+// (rows past M left as they are), at gather_sums_f32(ws, M, K).  The
+// gather's workgroups also zero counters[0 .. ncounters - 1] (the K-split
+// counters of the decode launch that follows it; nullptr and 0 for none).
 hipError_t launch_gather_x(const uint16_t* x, int64_t M, const WeightView& w, void* ws,
-                           hipStream_t stream, bool sums_f32);
+                           hipStream_t stream, bool sums_f32, uint32_t* counters,
+                           int ncounters);
 float* gather_sums_f32(void* ws, int64_t M, int64_t K);
 // The gather of launch_gather_x (sums_f32 on) for count (1 .. 8) matrices at
-// one M in one launch; ws[i] is matrix i's gather workspace.
+// one M in one launch; ws[i] is matrix i's gather workspace, counters[i] and
+// ncounters[i] its decode's K-split counters.
 hipError_t launch_gather_x_group(const uint16_t* const* x, int64_t M, const WeightView* w,
-                                 void* const* ws, int count, hipStream_t stream);
+                                 void* const* ws, uint32_t* const* counters,
+                                 const int* ncounters, int count, hipStream_t stream);
 
 // ---- K-split reduction (msq_gemv.hip): y[m][perm_row[n]] = sum over splits,
 // in split order, of part[sp][m][n].

@@ -270,9 +270,9 @@ size_t msq_gemm_group_workspace_bytes(int64_t M, const msq_weight *const *w, int
  * (matrices whose K is split into several ranges add one activation-prep
  * launch for all of them; the others reorder x inside their workgroups) ("TileQuant" abstract: local accumulation
  * to reduce memory traffic; the grouping itself is this library's).  At
- * M in 2 .. MSQ_AUTO_GEMV_MAX_M: one activation-gather launch, one decode
- * launch and (for matrices with several K ranges) one reduction launch
- * cover all matrices.  At M > MSQ_AUTO_GEMV_MAX_M, when the matrices' tiles
+ * M in 2 .. MSQ_AUTO_GEMV_MAX_M: one activation-gather launch and one
+ * decode launch cover all matrices (matrices with several K ranges add
+ * them up in the decode launch's last arriving workgroups).  At M > MSQ_AUTO_GEMV_MAX_M, when the matrices' tiles
  * fill the GPU (prefill), one activation-gather launch and one GEMM launch
  * cover all matrices, the tiles of the smaller ones filling the compute
  * units the larger ones leave idle; with fewer tiles the matrices are

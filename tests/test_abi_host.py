@@ -219,7 +219,7 @@ def test_group_workspace_sizes(lib):
     prep = sum(2 * w.K + 84 * (w.K // 128) for w in ws_list)
     g1 = lib.msq_gemm_group_workspace_bytes(1, arr, 3)
     assert prep <= g1 <= sum(singles) + 3 * 256
-    # M in 2 .. 32: one gather, decode and reduction launch for all, each matrix
+    # M in 2 .. 32: one gather and one decode launch for all, each matrix
     # with its own gathered activation; the group's K splits are no more than a
     # single call's
     mid = [lib.msq_gemm_workspace_bytes_ex(16, w.N, w.K, _opt(0)) for w in ws_list]

@@ -383,11 +383,11 @@ def _check_given_y(y, case, ref, x):
 
 @pytest.mark.parametrize("M", [2, 16, 24])
 def test_group_small_m_one_launch(msq, M):
-    """At 2 <= M <= 32 a group runs as one gather, one decode and (with several K
-    ranges) one reduction launch.  Two 8192-wide matrices and a 1024-wide one: with
-    one K range forced (ranges of 64 block columns, the one-block ring variant, no
-    reduction) and with three (the two-block variant and the reduction; ragged on
-    the 1024-wide matrix) every output equals its single call bit for bit, twice in
+    """At 2 <= M <= 32 a group runs as one gather and one decode launch (with several
+    K ranges the decode's last arriving workgroups add them up).  Two 8192-wide
+    matrices and a 1024-wide one: with one K range forced (ranges of 64 block
+    columns, the one-block ring variant, no reduction) and with three (the two-block
+    variant and the reduction; ragged on the 1024-wide matrix) every output equals its single call bit for bit, twice in
     a row; with the automatic choice (one K split chosen for the whole group) every
     output matches the oracle."""
     cases = []
@@ -472,7 +472,8 @@ def test_group_graph_replay_matches_eager(msq, group_cases, M, split):
     work in between on the same workspace, must equal the eager result bit for bit.
     M = 1 automatic (17 block rows: half block rows) and with one K range forced
     (whole block rows; the workgroups reorder x themselves); M = 16 automatic (K
-    ranges and the reduction launch) and with one K range."""
+    ranges, added up by the last arriving workgroups after the gather has cleared
+    their counters) and with one K range."""
     opt = None if split == "auto" else {"gemv_split": int(split)}
     pws = [pw for _, pw, _ in group_cases]
     x_shared = _bf16_cuda(group_cases[0][0].x(M))
