@@ -58,7 +58,6 @@ namespace {
 extern __shared__ __align__(16) unsigned char smem[];
 
 constexpr int kMaxCols = 64;  // block columns per workgroup: one wave ballot
-constexpr int kSmallMaxM = 64;  // k_gemv16 (A operands from the reordered x) up to this M
 
 __device__ __forceinline__ float bf16f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
