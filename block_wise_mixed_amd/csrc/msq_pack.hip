@@ -46,7 +46,6 @@ __device__ __forceinline__ int segment_of(int b) {
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 16;  // consecutive blocks per thread per pass
 constexpr int kSegs = 6;
-__constant__ int kSegBits[kSegs] = {1, 2, 3, 4, 8, 16};
 
 // Number of zero bytes of x (exact: no borrow between bytes).
 __device__ __forceinline__ uint32_t zero_bytes(uint32_t x) {
