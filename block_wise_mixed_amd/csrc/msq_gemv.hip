@@ -26,16 +26,15 @@
 //         y[row] += s * (sum_k (bias + q_k) x_k - (bias + z) * sum_k x_k).
 //  4. The wavefronts reduce through LDS in a fixed order.  One K split writes
 //     y directly (scattered to original rows through perm_row); several
-//     splits write fp32 partials that are summed in split order (M == 1: by
-//     the last workgroup of the block row to finish; M > 1: by
-//     k_gemv_reduce), so results are bitwise reproducible.
+//     splits write fp32 partials that the last workgroup of the block row to
+//     finish sums in split order, so results are bitwise reproducible.
 //
 // Kernels: k_gemv_m1 (M == 1: per-column k-step sums for the bias
 // corrections, an unpack that avoids most shifts, scales and zero points
 // staged in LDS, 2 to 4 KiB of codes in flight per wavefront; half block
 // rows of 32 rows for small launches instead of a K split), k_gemv16
 // (2 <= M <= 64, one to four m tiles), their group variants, and the split
-// reductions.
+// reductions of the prefill GEMM's K ranges (k_gemv_reduce, k_gemv_reduce_rows).
 //
 // Per-block precision and block layout: "ScaleBITS" summary page, section
 // Approach; RTN-g128 dequantization s * (q - z): section Limitations.
