@@ -27,7 +27,7 @@ def _bf16_cuda(a):
 # (N, K, M), each pair run big then small
 CASES = [((4096, 8192, 1), (512, 1024, 1)),        # decode, one K range, then a small one
          ((2048, 14336, 1), (256, 4096, 1)),       # decode with K split (counters), then small
-         ((4096, 4096, 16), (1024, 2048, 16)),     # decode M = 16 (gather + reduce)
+         ((4096, 4096, 16), (1024, 2048, 16)),     # decode M = 16, K split (arrival counters)
          ((4096, 8192, 200), (1024, 1024, 130))]   # prefill, split K, then smaller
 
 
