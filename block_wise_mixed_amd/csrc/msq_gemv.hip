@@ -149,11 +149,13 @@ __device__ __forceinline__ WaveRuns wave_runs(int bl, int wave, const int (&wt)[
   return wr;
 }
 
-// Piece weights: where a block's unpack and matrix instructions take about
-// as long as its loads, the measured per-block cost of a wavefront in units
-// of about 0.1 us (1- and 2-bit blocks alike, 3- and 4-bit alike, 8-bit
-// twice those) so that the wavefronts of a workgroup finish together.
-constexpr int kWeightCostM1[5] = {4, 4, 9, 9, 17};
+// Piece weights: the relative cost of a block in a wavefront's walk, so
+// that the wavefronts of a workgroup finish together.  Each block is one
+// dependent round trip of its loads plus its unpack and products, so the
+// weights grow more slowly than the bytes: 1- and 2-bit blocks alike, 3-
+// and 4-bit 1.5 times those, 8-bit 2.75 times (measured 2-4% faster per
+// call than weights proportional to the unpack work, 4 / 4 / 9 / 9 / 17).
+constexpr int kWeightCostM1[5] = {4, 4, 6, 6, 11};
 
 // One block: unpack + matrix-core product into acc[mt][rt] (M > 1).
 template <int B, int MT>
