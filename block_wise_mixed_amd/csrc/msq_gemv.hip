@@ -1397,6 +1397,9 @@ GemvPlan plan_gemv(int64_t M, int64_t N, int64_t K, const Options& opt, int64_t 
   int kr = (NBc + split - 1) / split;
   if (kr > kMaxCols) kr = kMaxCols;
   split = (NBc + kr - 1) / kr;
+  // ranges of equal width (224 block columns in 4 ranges: 56 each, not
+  // 64, 64, 64, 32, whose short range leaves its workgroups idle early)
+  kr = (NBc + split - 1) / split;
   p.split = split;
   p.kr = kr;
   // M == 1 with one K range reorders x inside the decode workgroups (no prep
